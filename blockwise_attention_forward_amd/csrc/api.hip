@@ -1,0 +1,321 @@
+// C ABI entry points: argument validation on the host, then one or more
+// asynchronous launches on the caller's stream.  Nothing here allocates
+// device memory, synchronises or keeps state between calls (the last-error
+// string is thread-local).
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <algorithm>
+
+#include "internal.h"
+
+using bwa::i64;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int32_t ok() {
+    g_last_error[0] = '\0';
+    return BWA_OK;
+}
+
+int32_t hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(BWA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+constexpr i64 kMaxLen = (i64)1 << 30;  // positions are kept in int32 inside the kernels
+
+int elem_size(int32_t dt) { return dt == BWA_BF16 ? 2 : 4; }
+
+int32_t check_tensor(const bwa_tensor* t, const char* name) {
+    if (!t) return fail(BWA_ERR_NULL_ARG, "%s: tensor descriptor is NULL", name);
+    if (t->dtype != BWA_F32 && t->dtype != BWA_BF16)
+        return fail(BWA_ERR_BAD_DTYPE, "%s: unknown dtype code %d", name, t->dtype);
+    if (t->B < 0 || t->L < 0 || t->H < 0 || t->D < 0)
+        return fail(BWA_ERR_BAD_SHAPE, "%s: negative size", name);
+    if (t->L > kMaxLen) return fail(BWA_ERR_UNSUPPORTED, "%s: L=%lld exceeds 2^30", name, (long long)t->L);
+    if (t->D != 64 && t->D != 128)
+        return fail(BWA_ERR_UNSUPPORTED, "%s: head dim %lld (supported: 64, 128)", name, (long long)t->D);
+    const i64 n = t->B * t->L * t->H;
+    if (n == 0) return BWA_OK;
+    if (!t->ptr) return fail(BWA_ERR_NULL_ARG, "%s: data pointer is NULL", name);
+    const i64 es = elem_size(t->dtype);
+    if (((uintptr_t)t->ptr) % 16) return fail(BWA_ERR_BAD_STRIDE, "%s: pointer not 16-byte aligned", name);
+    if ((t->sB * es) % 16 || (t->sL * es) % 16 || (t->sH * es) % 16)
+        return fail(BWA_ERR_BAD_STRIDE, "%s: strides must be multiples of 16 bytes", name);
+    if (t->sB < 0 || t->sL < 0 || t->sH < 0) return fail(BWA_ERR_BAD_STRIDE, "%s: negative stride", name);
+    return BWA_OK;
+}
+
+// Resolve and validate a mask for a [B, lq] x [B, lk] problem.
+int32_t resolve_mask(const bwa_mask* m, i64 B, i64 lq, i64 lk, bwa::MaskDev& out) {
+    if (!m) return fail(BWA_ERR_NULL_ARG, "mask is NULL");
+    if (m->causal != 0 && m->causal != 1) return fail(BWA_ERR_BAD_MASK, "causal must be 0 or 1");
+    if (m->window < 0) return fail(BWA_ERR_BAD_MASK, "window must be >= 0");
+    if (m->window > 0 && !m->causal)
+        return fail(BWA_ERR_BAD_MASK, "a sliding window needs causal = 1");
+    if (m->q_valid > lq) return fail(BWA_ERR_BAD_MASK, "q_valid %lld > Lq %lld", (long long)m->q_valid, (long long)lq);
+    if (m->kv_valid > lk) return fail(BWA_ERR_BAD_MASK, "kv_valid %lld > Lk %lld", (long long)m->kv_valid, (long long)lk);
+    if (m->kv_offset > kMaxLen || m->kv_offset < -kMaxLen)
+        return fail(BWA_ERR_BAD_MASK, "kv_offset out of range");
+    const bool cu = m->cu_seqlens_q != nullptr;
+    const bool ids = m->segment_ids_q != nullptr;
+    if (cu && ids) return fail(BWA_ERR_BAD_MASK, "give cu_seqlens or segment ids, not both");
+    if (!cu && m->cu_seqlens_kv) return fail(BWA_ERR_BAD_MASK, "cu_seqlens_kv given without cu_seqlens_q");
+    if (!ids && m->segment_ids_kv) return fail(BWA_ERR_BAD_MASK, "segment_ids_kv given without segment_ids_q");
+    if (cu && m->num_segments <= 0) return fail(BWA_ERR_BAD_MASK, "cu_seqlens needs num_segments >= 1");
+    if (!cu && m->num_segments != 0) return fail(BWA_ERR_BAD_MASK, "num_segments without cu_seqlens");
+    if (ids && !m->segment_ids_kv && lq != lk)
+        return fail(BWA_ERR_BAD_MASK, "segment_ids_kv may be omitted only when Lq == Lk");
+    out.lq = lq;
+    out.lk = lk;
+    out.kv_offset = m->kv_offset;
+    out.q_valid = m->q_valid < 0 ? lq : m->q_valid;
+    out.kv_valid = m->kv_valid < 0 ? lk : m->kv_valid;
+    out.causal = m->causal;
+    out.window = m->window;
+    out.seg_mode = cu ? 1 : (ids ? 2 : 0);
+    out.num_segments = cu ? m->num_segments : 0;
+    out.cu_q = m->cu_seqlens_q;
+    out.cu_kv = m->cu_seqlens_kv ? m->cu_seqlens_kv : m->cu_seqlens_q;
+    out.ids_q = m->segment_ids_q;
+    out.ids_kv = m->segment_ids_kv ? m->segment_ids_kv : m->segment_ids_q;
+    (void)B;
+    return BWA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bwa_status_string(int32_t s) {
+    switch (s) {
+        case BWA_OK: return "ok";
+        case BWA_ERR_NULL_ARG: return "null argument";
+        case BWA_ERR_BAD_SHAPE: return "bad shape";
+        case BWA_ERR_BAD_STRIDE: return "bad stride or alignment";
+        case BWA_ERR_BAD_DTYPE: return "bad dtype";
+        case BWA_ERR_BAD_MASK: return "bad mask";
+        case BWA_ERR_UNSUPPORTED: return "unsupported";
+        case BWA_ERR_CAPACITY: return "list capacity too small";
+        case BWA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* bwa_last_error(void) { return g_last_error; }
+
+int32_t bwa_version(void) { return BWATTN_VERSION; }
+
+int32_t bwa_attn_tile(int32_t dtype, int64_t D, int32_t* bq, int32_t* bkv) {
+    if (!bq || !bkv) return fail(BWA_ERR_NULL_ARG, "bq/bkv output is NULL");
+    if (dtype != BWA_F32 && dtype != BWA_BF16) return fail(BWA_ERR_BAD_DTYPE, "unknown dtype %d", dtype);
+    if (D != 64 && D != 128) return fail(BWA_ERR_UNSUPPORTED, "head dim %lld", (long long)D);
+    *bq = 128;
+    *bkv = 64;
+    return ok();
+}
+
+int32_t bwa_block_mask_size(const bwa_mask* mask, int64_t B, int64_t lq, int64_t lk, int32_t bq,
+                            int32_t bkv, int64_t* n_qblocks, int64_t* capacity, int64_t* list_batch) {
+    if (!n_qblocks || !capacity || !list_batch) return fail(BWA_ERR_NULL_ARG, "size outputs are NULL");
+    if (B < 0 || lq < 0 || lk < 0) return fail(BWA_ERR_BAD_SHAPE, "negative size");
+    if (lq > kMaxLen || lk > kMaxLen) return fail(BWA_ERR_UNSUPPORTED, "length exceeds 2^30");
+    if (bq <= 0 || bkv <= 0 || bq % 64 || bkv % 64)
+        return fail(BWA_ERR_BAD_SHAPE, "bq and bkv must be positive multiples of 64");
+    bwa::MaskDev md;
+    int32_t st = resolve_mask(mask, B, lq, lk, md);
+    if (st) return st;
+    const i64 nqb = (lq + bq - 1) / bq, nkb = (lk + bkv - 1) / bkv;
+    const i64 per = md.seg_mode ? std::min<i64>(nkb, (i64)bq + 2) : std::min<i64>(nkb, 3);
+    *n_qblocks = nqb;
+    *capacity = std::max<i64>(nqb * per, 1);
+    *list_batch = md.seg_mode == 2 ? B : 1;
+    return ok();
+}
+
+int32_t bwa_block_mask_build(const bwa_mask* mask, int64_t B, int64_t lq, int64_t lk, bwa_blocks* out,
+                             void* stream) {
+    if (!out) return fail(BWA_ERR_NULL_ARG, "blocks output is NULL");
+    i64 nqb, cap, lb;
+    int32_t st = bwa_block_mask_size(mask, B, lq, lk, out->bq, out->bkv, &nqb, &cap, &lb);
+    if (st) return st;
+    if (out->lq != lq || out->lk != lk || out->n_qblocks != nqb || out->batch != lb)
+        return fail(BWA_ERR_BAD_SHAPE, "blocks descriptor does not match (lq, lk, n_qblocks, batch)");
+    if (out->capacity < cap)
+        return fail(BWA_ERR_CAPACITY, "capacity %lld < required %lld", (long long)out->capacity, (long long)cap);
+    if (!out->row_ptr || !out->run_begin || !out->run_end || !out->run_kind || (lq > 0 && (!out->row_lo || !out->row_hi)))
+        return fail(BWA_ERR_NULL_ARG, "blocks arrays must be non-NULL");
+    bwa::BlocksLaunch a;
+    resolve_mask(mask, B, lq, lk, a.mask);
+    a.copies = lb;
+    a.bq = out->bq;
+    a.bkv = out->bkv;
+    a.n_qblocks = nqb;
+    a.capacity = out->capacity;
+    a.row_ptr = out->row_ptr;
+    a.run_begin = out->run_begin;
+    a.run_end = out->run_end;
+    a.run_kind = out->run_kind;
+    a.row_lo = out->row_lo;
+    a.row_hi = out->row_hi;
+    return hip_status(bwa::launch_block_mask_build(a, (hipStream_t)stream), "block_mask_build launch");
+}
+
+int32_t bwa_fixed_m_bound(const bwa_tensor* q, const bwa_tensor* k_chunks, int32_t n_chunks,
+                          const float* kmax_in, const int64_t* kv_valid, int64_t q_valid, float scale,
+                          float tau, float* kmax_out, float* mmax_out, float* m_out, uint8_t* gate_out,
+                          void* stream) {
+    int32_t st = check_tensor(q, "q");
+    if (st) return st;
+    if (n_chunks < 0 || n_chunks > bwa::kMaxChunks)
+        return fail(BWA_ERR_BAD_SHAPE, "n_chunks must be in [0, %d]", bwa::kMaxChunks);
+    if (n_chunks > 0 && !k_chunks) return fail(BWA_ERR_NULL_ARG, "k_chunks is NULL");
+    if (q_valid > q->L) return fail(BWA_ERR_BAD_SHAPE, "q_valid > Lq");
+    const i64 BH = q->B * q->H;
+    if (BH > 0 && (!kmax_out || !mmax_out || !gate_out || (q->L > 0 && !m_out)))
+        return fail(BWA_ERR_NULL_ARG, "bound outputs must be non-NULL");
+    bwa::BoundLaunch a;
+    a.q = {q->ptr, q->L, q->sB, q->sL, q->sH, q_valid < 0 ? q->L : q_valid};
+    for (int c = 0; c < n_chunks; ++c) {
+        const bwa_tensor* k = &k_chunks[c];
+        char name[32];
+        snprintf(name, sizeof(name), "k_chunks[%d]", c);
+        st = check_tensor(k, name);
+        if (st) return st;
+        if (k->dtype != q->dtype || k->B != q->B || k->H != q->H || k->D != q->D)
+            return fail(BWA_ERR_BAD_SHAPE, "%s: dtype/B/H/D differ from q", name);
+        i64 valid = k->L;
+        if (kv_valid && kv_valid[c] >= 0) {
+            if (kv_valid[c] > k->L) return fail(BWA_ERR_BAD_SHAPE, "%s: kv_valid > L", name);
+            valid = kv_valid[c];
+        }
+        a.k[c] = {k->ptr, k->L, k->sB, k->sL, k->sH, valid};
+    }
+    a.n_chunks = n_chunks;
+    a.B = (int)q->B;
+    a.H = (int)q->H;
+    a.D = (int)q->D;
+    a.dtype = q->dtype;
+    a.kmax_in = kmax_in;
+    a.scale = scale;
+    a.tau = tau;
+    a.kmax_out = kmax_out;
+    a.mmax_out = mmax_out;
+    a.m_out = m_out;
+    a.gate_out = gate_out;
+    return hip_status(bwa::launch_fixed_m_bound(a, (hipStream_t)stream), "fixed_m_bound launch");
+}
+
+int32_t bwa_attn_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v, const bwa_mask* mask,
+                     const bwa_blocks* blocks, float scale, int32_t mode, const float* m,
+                     const uint8_t* gate, bwa_tensor* o, float* lse, void* stream) {
+    int32_t st;
+    if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
+        (st = check_tensor(o, "o")))
+        return st;
+    if (k->dtype != q->dtype || v->dtype != q->dtype)
+        return fail(BWA_ERR_BAD_DTYPE, "q, k and v must share a dtype");
+    if (o->dtype != BWA_F32 && o->dtype != q->dtype)
+        return fail(BWA_ERR_BAD_DTYPE, "o must be fp32 or q's dtype");
+    if (k->B != q->B || v->B != q->B || k->H != q->H || v->H != q->H || k->D != q->D || v->D != q->D)
+        return fail(BWA_ERR_BAD_SHAPE, "q, k, v disagree on B, H or D");
+    if (k->L != v->L) return fail(BWA_ERR_BAD_SHAPE, "k and v lengths differ");
+    if (o->B != q->B || o->L != q->L || o->H != q->H || o->D != q->D)
+        return fail(BWA_ERR_BAD_SHAPE, "o must have q's shape");
+    if (mode != BWA_MODE_ONLINE && mode != BWA_MODE_FIXED_M) return fail(BWA_ERR_BAD_SHAPE, "unknown mode %d", mode);
+    const i64 B = q->B, H = q->H, Lq = q->L, Lk = k->L;
+    const i64 rows = B * H * Lq;
+    if (rows > 0 && !lse) return fail(BWA_ERR_NULL_ARG, "lse is NULL");
+    if (mode == BWA_MODE_FIXED_M && rows > 0 && !m) return fail(BWA_ERR_NULL_ARG, "fixed-m mode needs m");
+    bwa::AttnLaunch a;
+    memset(&a, 0, sizeof(a));
+    if ((st = resolve_mask(mask, B, Lq, Lk, a.mask))) return st;
+    int32_t bq, bkv;
+    bwa_attn_tile(q->dtype, q->D, &bq, &bkv);
+    if (blocks) {
+        if (blocks->bq != bq || blocks->bkv <= 0 || blocks->bkv % bkv)
+            return fail(BWA_ERR_BAD_SHAPE, "blocks built with bq=%d bkv=%d; need bq=%d, bkv a multiple of %d",
+                        blocks->bq, blocks->bkv, bq, bkv);
+        if (blocks->lq != Lq || blocks->lk != Lk || blocks->n_qblocks != (Lq + bq - 1) / bq)
+            return fail(BWA_ERR_BAD_SHAPE, "blocks describe a different problem size");
+        if (blocks->batch != 1 && blocks->batch != B) return fail(BWA_ERR_BAD_SHAPE, "blocks batch must be 1 or B");
+        if (a.mask.seg_mode == 2 && blocks->batch != B)
+            return fail(BWA_ERR_BAD_SHAPE, "per-token segment ids need one list copy per batch element");
+        if (!blocks->row_ptr || !blocks->run_begin || !blocks->run_end || !blocks->run_kind ||
+            (Lq > 0 && (!blocks->row_lo || !blocks->row_hi)))
+            return fail(BWA_ERR_NULL_ARG, "blocks arrays must be non-NULL");
+        a.have_blocks = 1;
+        a.row_ptr = blocks->row_ptr;
+        a.run_begin = blocks->run_begin;
+        a.run_end = blocks->run_end;
+        a.run_kind = blocks->run_kind;
+        a.row_lo = blocks->row_lo;
+        a.row_hi = blocks->row_hi;
+        a.list_batch = blocks->batch;
+        a.capacity = blocks->capacity;
+        a.bkv_list = blocks->bkv;
+    }
+    if (B * H * ((Lq + bq - 1) / bq) >= ((i64)1 << 31)) return fail(BWA_ERR_UNSUPPORTED, "grid too large");
+    a.q = q->ptr; a.k = k->ptr; a.v = v->ptr;
+    a.q_sB = q->sB; a.q_sL = q->sL; a.q_sH = q->sH;
+    a.k_sB = k->sB; a.k_sL = k->sL; a.k_sH = k->sH;
+    a.v_sB = v->sB; a.v_sL = v->sL; a.v_sH = v->sH;
+    a.o = o->ptr; a.o_sB = o->sB; a.o_sL = o->sL; a.o_sH = o->sH;
+    a.lse = lse;
+    a.B = (int)B; a.H = (int)H; a.D = (int)q->D;
+    a.Lq = Lq; a.Lk = Lk;
+    a.in_dtype = q->dtype;
+    a.out_dtype = o->dtype;
+    a.scale = scale;
+    a.mode = mode;
+    a.m = m;
+    a.gate = gate;
+    a.n_qblocks = (Lq + bq - 1) / bq;
+    return hip_status(bwa::launch_attn_fwd(a, (hipStream_t)stream), "attn_fwd launch");
+}
+
+int32_t bwa_lse_merge(int32_t n_parts, const bwa_tensor* o_parts, const float* const* lse_parts,
+                      bwa_tensor* o_out, float* lse_out, void* stream) {
+    if (n_parts < 1 || n_parts > bwa::kMaxParts)
+        return fail(BWA_ERR_BAD_SHAPE, "n_parts must be in [1, %d]", bwa::kMaxParts);
+    if (!o_parts || !lse_parts) return fail(BWA_ERR_NULL_ARG, "o_parts/lse_parts is NULL");
+    int32_t st = check_tensor(o_out, "o_out");
+    if (st) return st;
+    bwa::MergeLaunch a;
+    memset(&a, 0, sizeof(a));
+    const i64 rows = o_out->B * o_out->L * o_out->H;
+    for (int t = 0; t < n_parts; ++t) {
+        char name[32];
+        snprintf(name, sizeof(name), "o_parts[%d]", t);
+        if ((st = check_tensor(&o_parts[t], name))) return st;
+        const bwa_tensor& p = o_parts[t];
+        if (p.dtype != BWA_F32) return fail(BWA_ERR_BAD_DTYPE, "%s must be fp32", name);
+        if (p.B != o_out->B || p.L != o_out->L || p.H != o_out->H || p.D != o_out->D)
+            return fail(BWA_ERR_BAD_SHAPE, "%s shape differs from o_out", name);
+        if (rows > 0 && !lse_parts[t]) return fail(BWA_ERR_NULL_ARG, "lse_parts[%d] is NULL", t);
+        a.o[t] = (const float*)p.ptr;
+        a.lse[t] = lse_parts[t];
+        a.sB[t] = p.sB; a.sL[t] = p.sL; a.sH[t] = p.sH;
+    }
+    a.n_parts = n_parts;
+    a.B = (int)o_out->B; a.H = (int)o_out->H; a.D = (int)o_out->D;
+    a.L = o_out->L;
+    a.out = o_out->ptr; a.out_sB = o_out->sB; a.out_sL = o_out->sL; a.out_sH = o_out->sH;
+    a.out_dtype = o_out->dtype;
+    a.lse_out = lse_out;
+    return hip_status(bwa::launch_lse_merge(a, (hipStream_t)stream), "lse_merge launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+// Tile run lists for blockwise attention (gfx950).
+//
+// "Add more optimal dk order optional arg" (flash-attention pull request
+// 2512), "Sliding window perf issue": a block-sparse kernel walks partial
+// tiles (element mask needed) and full tiles (no mask) and skips the rest;
+// "A simplish fix" merges both kinds into one ordered list.  Here every
+// query block gets its visited key blocks in ascending order as maximal runs
+// of one kind, stored CSR-style in HBM.  The metadata is O(query blocks x
+// runs) plus one key interval per row; nothing per token or per tile pair is
+// held on chip, which is what capped the segmented splash kernel ("Let
+// splash attention exceed 524,288 tokens when packing is off", Effect).
+//
+// Four launches: row intervals; run count per query block; exclusive scan
+// of the counts into row_ptr; run fill.  Integer-only, deterministic.
+
+#include "internal.h"
+
+namespace bwa {
+namespace {
+
+__global__ __launch_bounds__(256) void rows_kernel(const BlocksLaunch a) {
+    const i64 idx = (i64)blockIdx.x * 256 + threadIdx.x;
+    const i64 lq = a.mask.lq;
+    if (idx >= a.copies * lq) return;
+    const i64 copy = idx / lq, i = idx % lq;
+    int lo, hi;
+    row_interval(a.mask, copy, i, lo, hi);
+    a.row_lo[idx] = lo;
+    a.row_hi[idx] = hi;
+}
+
+// One wavefront per (copy, query block).  Each lane holds bq/64 rows.
+template <bool FILL>
+__global__ __launch_bounds__(256) void runs_kernel(const BlocksLaunch a) {
+    const i64 wg = (i64)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const i64 nqb = a.n_qblocks;
+    if (wg >= a.copies * nqb) return;
+    const int lane = threadIdx.x & 63;
+    const i64 copy = wg / nqb, qb = wg % nqb;
+    const i64 lq = a.mask.lq, lk = a.mask.lk;
+    const int* rlo = a.row_lo + copy * lq;
+    const int* rhi = a.row_hi + copy * lq;
+    const int per_lane = a.bq / 64;
+
+    // Range of key blocks any row of this block can meet.
+    int mn_lo = 0x7fffffff, mx_hi = 0;
+    for (int t = 0; t < per_lane; ++t) {
+        const i64 r = qb * a.bq + lane + 64 * t;
+        if (r < lq) {
+            const int lo = rlo[r], hi = rhi[r];
+            if (lo < hi) { mn_lo = min(mn_lo, lo); mx_hi = max(mx_hi, hi); }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        mn_lo = min(mn_lo, __shfl_xor(mn_lo, o));
+        mx_hi = max(mx_hi, __shfl_xor(mx_hi, o));
+    }
+    i64* rp = a.row_ptr + copy * (nqb + 1);
+    i64 out = 0;
+    if (FILL) out = rp[qb];
+    i64 n = 0;
+    if (mx_hi > 0) {
+        const int kb_lo = mn_lo / a.bkv;
+        const int kb_hi = (int)((mx_hi + (i64)a.bkv - 1) / a.bkv);
+        int cur_kind = 0, cur_b = 0, cur_e = 0;
+        auto emit = [&]() {
+            if (FILL && lane == 0) {
+                const i64 slot = out + n;
+                if (slot < a.capacity) {
+                    a.run_begin[copy * a.capacity + slot] = cur_b;
+                    a.run_end[copy * a.capacity + slot] = cur_e;
+                    a.run_kind[copy * a.capacity + slot] = (uint8_t)cur_kind;
+                }
+            }
+            ++n;
+        };
+        for (int kb = kb_lo; kb < kb_hi; ++kb) {
+            const i64 j0 = (i64)kb * a.bkv;
+            const i64 j1 = min(j0 + a.bkv, lk);
+            bool meets = false, covers = true;
+            for (int t = 0; t < per_lane; ++t) {
+                const i64 r = qb * a.bq + lane + 64 * t;
+                if (r < lq) {
+                    const int lo = rlo[r], hi = rhi[r];
+                    const bool ne = lo < hi;
+                    meets |= ne && lo < j1 && hi > j0;
+                    covers &= ne && lo <= j0 && hi >= j1;
+                }
+            }
+            const bool any_meet = __ballot(meets) != 0;
+            const bool all_cover = __ballot(!covers) == 0;
+            const int kind = all_cover ? BWA_TILE_FULL : (any_meet ? BWA_TILE_PARTIAL : BWA_TILE_SKIP);
+            if (kind == BWA_TILE_SKIP) {
+                if (cur_kind) { emit(); cur_kind = 0; }
+            } else if (cur_kind == kind && cur_e == kb) {
+                cur_e = kb + 1;
+            } else {
+                if (cur_kind) emit();
+                cur_kind = kind; cur_b = kb; cur_e = kb + 1;
+            }
+        }
+        if (cur_kind) emit();
+    }
+    if (!FILL && lane == 0) rp[qb + 1] = n;
+}
+
+// In-place inclusive scan of row_ptr[1..nqb] (counts) -> CSR offsets;
+// row_ptr[0] = 0.  One workgroup per list copy.
+__global__ __launch_bounds__(1024) void scan_kernel(const BlocksLaunch a) {
+    __shared__ i64 part[1024];
+    const i64 nqb = a.n_qblocks;
+    i64* v = a.row_ptr + (i64)blockIdx.x * (nqb + 1) + 1;
+    const int t = threadIdx.x;
+    if (t == 0) v[-1] = 0;
+    const i64 chunk = (nqb + 1023) / 1024;
+    const i64 s = t * chunk, e = min(nqb, s + chunk);
+    i64 sum = 0;
+    for (i64 i = s; i < e; ++i) sum += v[i];
+    part[t] = sum;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+        const i64 x = (t >= o) ? part[t - o] : 0;
+        __syncthreads();
+        part[t] += x;
+        __syncthreads();
+    }
+    i64 run = part[t] - sum;  // exclusive prefix of this thread's chunk
+    for (i64 i = s; i < e; ++i) { run += v[i]; v[i] = run; }
+}
+
+}  // namespace
+
+hipError_t launch_block_mask_build(const BlocksLaunch& a, hipStream_t stream) {
+    const i64 nrows = a.copies * a.mask.lq;
+    if (nrows > 0)
+        hipLaunchKernelGGL(rows_kernel, dim3((unsigned)((nrows + 255) / 256)), dim3(256), 0, stream, a);
+    const i64 waves = a.copies * a.n_qblocks;
+    const unsigned grid = (unsigned)((waves + 3) / 4);
+    if (waves > 0) hipLaunchKernelGGL(runs_kernel<false>, dim3(grid), dim3(256), 0, stream, a);
+    if (a.copies > 0)
+        hipLaunchKernelGGL(scan_kernel, dim3((unsigned)a.copies), dim3(1024), 0, stream, a);
+    if (waves > 0) hipLaunchKernelGGL(runs_kernel<true>, dim3(grid), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace bwa

@@ -1,0 +1,137 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bwattn.h"
+
+namespace bwa {
+
+typedef int64_t i64;
+
+// Resolved mask passed to kernels by value.  All positions are in the
+// problem's own coordinates; q_valid/kv_valid are already clamped to
+// [0, lq] / [0, lk].
+struct MaskDev {
+    i64 lq, lk;
+    i64 kv_offset;
+    i64 q_valid, kv_valid;
+    int causal;
+    int window;
+    int seg_mode;  // 0 none, 1 cu_seqlens, 2 per-token segment ids
+    int num_segments;
+    const int* cu_q;
+    const int* cu_kv;
+    const int* ids_q;   // [B][lq]
+    const int* ids_kv;  // [B][lk]
+};
+
+// Keys visible to query row i of batch element b form one interval [lo, hi):
+// every term of the mask bounds it from below or above (padding, segment,
+// causal and window terms of the visibility rule in bwattn.h).  Rows that see
+// nothing return (0, 0).  Segment lookups are binary searches over the
+// cumulative lengths or the (non-decreasing) per-token ids; nothing is
+// tabulated per token.
+__device__ inline void row_interval(const MaskDev& m, i64 b, i64 i, int& out_lo, int& out_hi) {
+    i64 lo = 0, hi = m.kv_valid;
+    bool ok = (i >= 0) && (i < m.q_valid);
+    if (ok && m.seg_mode == 1) {
+        const int S = m.num_segments;
+        if (i < (i64)m.cu_q[0] || i >= (i64)m.cu_q[S]) {
+            ok = false;
+        } else {
+            int a = 0, c = S;  // largest s in [0, S) with cu_q[s] <= i
+            while (c - a > 1) {
+                int mid = (a + c) >> 1;
+                if ((i64)m.cu_q[mid] <= i) a = mid; else c = mid;
+            }
+            lo = max(lo, (i64)m.cu_kv[a]);
+            hi = min(hi, (i64)m.cu_kv[a + 1]);
+        }
+    } else if (ok && m.seg_mode == 2) {
+        const int sid = m.ids_q[b * m.lq + i];
+        const int* ids = m.ids_kv + b * m.lk;
+        i64 a = 0, c = m.lk;  // first key with id >= sid
+        while (a < c) {
+            i64 mid = (a + c) >> 1;
+            if (ids[mid] < sid) a = mid + 1; else c = mid;
+        }
+        i64 first = a;
+        c = m.lk;  // first key with id > sid
+        while (a < c) {
+            i64 mid = (a + c) >> 1;
+            if (ids[mid] <= sid) a = mid + 1; else c = mid;
+        }
+        lo = max(lo, first);
+        hi = min(hi, a);
+    }
+    if (m.causal) hi = min(hi, i - m.kv_offset + 1);
+    if (m.window > 0) lo = max(lo, i - m.kv_offset - (i64)m.window + 1);
+    lo = max(lo, (i64)0);
+    if (!ok || lo >= hi) { lo = 0; hi = 0; }
+    out_lo = (int)lo;
+    out_hi = (int)hi;
+}
+
+// ---- launchers (implemented next to their kernels) ------------------------
+
+struct AttnLaunch {
+    const void* q; const void* k; const void* v;
+    i64 q_sB, q_sL, q_sH, k_sB, k_sL, k_sH, v_sB, v_sL, v_sH;
+    void* o; i64 o_sB, o_sL, o_sH;
+    float* lse;
+    int B, H, D;
+    i64 Lq, Lk;
+    int in_dtype, out_dtype;
+    float scale;
+    int mode;
+    const float* m;
+    const uint8_t* gate;
+    // run lists (have_blocks != 0)
+    int have_blocks;
+    const i64* row_ptr; const int* run_begin; const int* run_end; const uint8_t* run_kind;
+    const int* row_lo; const int* row_hi;
+    i64 list_batch, capacity, n_qblocks;
+    int bkv_list;
+    MaskDev mask;
+};
+hipError_t launch_attn_fwd(const AttnLaunch& a, hipStream_t stream);
+
+struct BlocksLaunch {
+    MaskDev mask;
+    i64 copies;      // list copies (1 or B)
+    int bq, bkv;
+    i64 n_qblocks, capacity;
+    i64* row_ptr; int* run_begin; int* run_end; uint8_t* run_kind;
+    int* row_lo; int* row_hi;
+};
+hipError_t launch_block_mask_build(const BlocksLaunch& a, hipStream_t stream);
+
+constexpr int kMaxChunks = 16;
+struct BoundTensor { const void* ptr; i64 L, sB, sL, sH, valid; };
+struct BoundLaunch {
+    BoundTensor q;
+    BoundTensor k[kMaxChunks];
+    int n_chunks;
+    int B, H, D, dtype;
+    const float* kmax_in;
+    float scale, tau;
+    float* kmax_out; float* mmax_out; float* m_out; uint8_t* gate_out;
+};
+hipError_t launch_fixed_m_bound(const BoundLaunch& a, hipStream_t stream);
+
+constexpr int kMaxParts = 16;
+struct MergeLaunch {
+    const float* o[kMaxParts];
+    const float* lse[kMaxParts];
+    i64 sB[kMaxParts], sL[kMaxParts], sH[kMaxParts];
+    int n_parts;
+    int B, H, D;
+    i64 L;
+    void* out; i64 out_sB, out_sL, out_sH; int out_dtype;
+    float* lse_out;
+};
+hipError_t launch_lse_merge(const MergeLaunch& a, hipStream_t stream);
+
+}  // namespace bwa

@@ -1,0 +1,251 @@
+/*
+ * bwattn.h -- C ABI of the blockwise attention forward library (MI355X, gfx950).
+ *
+ * The library computes blockwise scaled-dot-product attention forward with
+ * online softmax or with a fixed per-query bound in place of the running max,
+ * the log-sum-exp merge of key-chunk partials, the fixed-m bound and gate,
+ * and the tile run lists that let the attention kernel skip whole tiles.
+ *
+ * Pages the operations follow (cited by title and section):
+ *  [FIXEDM]  "Fixed-m softmax for 2D-ring x Ulysses attention (WAN 2.2)"
+ *            (maxdiffusion pull request 452): description, Result, Notes, Tests.
+ *  [SPLASH]  "Let splash attention exceed 524,288 tokens when packing is off"
+ *            (maxtext pull request 4929): description, Effect, review.
+ *  [DKORDER] "Add more optimal dk order optional arg" (flash-attention pull
+ *            request 2512): "Sliding window perf issue", "A simplish fix".
+ *  [H3]      sglang pull request 47566 (H3 packed sequence): Motivation,
+ *            Modifications.
+ *  [ULYRING] maxdiffusion pull request 404 (ulysses_ring review): padding
+ *            mask from global positions; validation of the layout.
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are token-major [B, L, H, D] with the last dimension contiguous;
+ *    strides are in elements.  Base pointers and the B/L/H strides must be
+ *    multiples of 16 bytes.  Per-row statistics (lse, m) are dense
+ *    fp32 [B, H, L].
+ *  - Every pointer inside a tensor or mask, and every output pointer, is a
+ *    device pointer unless the argument says "host".  The caller allocates
+ *    and owns every buffer; the library allocates no device memory and keeps
+ *    no state between calls.
+ *  - Every call is asynchronous on the given stream (a hipStream_t; NULL is
+ *    the null stream) and never synchronises.  Argument errors are detected
+ *    on the host before any launch and return a nonzero status with nothing
+ *    enqueued; bwa_last_error() then describes the problem.  A failed launch
+ *    returns BWA_ERR_HIP.  No C++ exception crosses the ABI.
+ *  - Unsupported input returns BWA_ERR_UNSUPPORTED; there is no fallback to
+ *    any other implementation.
+ *  - Calls are deterministic: the same inputs give the same bits.
+ */
+#ifndef BWATTN_H
+#define BWATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BWATTN_VERSION 1
+
+/* Status codes. */
+enum {
+    BWA_OK = 0,
+    BWA_ERR_NULL_ARG = 1,     /* a required pointer is NULL */
+    BWA_ERR_BAD_SHAPE = 2,    /* sizes disagree or are negative */
+    BWA_ERR_BAD_STRIDE = 3,   /* misaligned pointer or stride */
+    BWA_ERR_BAD_DTYPE = 4,    /* dtype code unknown or not allowed here */
+    BWA_ERR_BAD_MASK = 5,     /* inconsistent mask description */
+    BWA_ERR_UNSUPPORTED = 6,  /* valid input this build does not handle (e.g. D not 64/128) */
+    BWA_ERR_CAPACITY = 7,     /* caller-provided list storage too small */
+    BWA_ERR_HIP = 8           /* the HIP runtime reported an error */
+};
+
+/* Element types. */
+enum { BWA_F32 = 0, BWA_BF16 = 1 };
+
+/* Attention modes. */
+enum {
+    BWA_MODE_ONLINE = 0,  /* running row max and rescale [FIXEDM description] */
+    BWA_MODE_FIXED_M = 1  /* precomputed per-row bound m in place of the max [FIXEDM] */
+};
+
+/* Tile kinds in run lists [DKORDER "Sliding window perf issue"]. */
+enum { BWA_TILE_SKIP = 0, BWA_TILE_FULL = 1, BWA_TILE_PARTIAL = 2 };
+
+/* A dense [B, L, H, D] tensor; d-stride is 1; strides in elements. */
+typedef struct bwa_tensor {
+    void* ptr;       /* device pointer to element [0,0,0,0] */
+    int32_t dtype;   /* BWA_F32 or BWA_BF16 */
+    int32_t reserved;
+    int64_t B, L, H, D;
+    int64_t sB, sL, sH;
+} bwa_tensor;
+
+/*
+ * Mask description.  Query row i sits at position i and key j at position
+ * j + kv_offset.  Key j is visible to row i iff all of:
+ *   j < kv_valid and i < q_valid         -- padding at the end of the global
+ *                                           sequence [ULYRING]; alignment rows
+ *                                           are zeroed [H3 Modifications]
+ *   seg_q(i) == seg_kv(j)                -- packing / varlen [SPLASH; H3]
+ *   causal     => j + kv_offset <= i
+ *   window > 0 => i - (j + kv_offset) < window   (requires causal)
+ * A row with no visible key gets O = 0 and LSE = -inf.
+ *
+ * Segments come either from cumulative lengths (cu_seqlens_q/kv, shared by
+ * every batch element; segment s covers [cu[s], cu[s+1]); positions covered
+ * by no segment see nothing) or from per-token segment ids ([B][L],
+ * non-decreasing along L, equal ids see each other).  Leave both NULL for an
+ * unsegmented mask.  Segments are turned into per-row key intervals before
+ * any attention tile runs, so no per-token table is ever held on chip and the
+ * sequence length is bounded by memory only; one segment covering every
+ * token gives exactly the unsegmented result [SPLASH description].
+ */
+typedef struct bwa_mask {
+    int32_t causal;                 /* 0 or 1 */
+    int32_t window;                 /* 0 = no window; > 0 needs causal */
+    int64_t kv_offset;              /* key j is at position j + kv_offset (ring hop, bottom-right) */
+    int64_t q_valid;                /* rows >= q_valid see nothing; < 0 means Lq */
+    int64_t kv_valid;               /* keys >= kv_valid are invisible; < 0 means Lk */
+    int32_t num_segments;           /* segments in cu_seqlens (0 when not used) */
+    int32_t reserved;
+    const int32_t* cu_seqlens_q;    /* device [num_segments + 1], non-decreasing */
+    const int32_t* cu_seqlens_kv;   /* device [num_segments + 1]; NULL = cu_seqlens_q */
+    const int32_t* segment_ids_q;   /* device [B][Lq] non-decreasing, or NULL */
+    const int32_t* segment_ids_kv;  /* device [B][Lk]; NULL = segment_ids_q (needs Lq == Lk) */
+} bwa_mask;
+
+/*
+ * Tile run lists and per-row key intervals ([DKORDER]: partial and full
+ * tiles; "A simplish fix": one ordered list).  For every query block of bq
+ * rows, the key blocks of bkv keys that hold at least one visible pair are
+ * listed in ascending order as maximal runs [begin, end) of one kind:
+ * FULL (every pair visible) or PARTIAL.  Tiles are clipped to
+ * [0, lq) x [0, lk).  row_lo/row_hi hold each row's visible keys [lo, hi)
+ * ((0, 0) when the row sees nothing).  All arrays are device memory owned by
+ * the caller and sized with bwa_block_mask_size.
+ */
+typedef struct bwa_blocks {
+    int32_t bq, bkv;      /* tile sizes the lists are built for */
+    int64_t lq, lk;       /* problem size the lists describe */
+    int64_t batch;        /* list copies: 1 (shared by all batch elements) or B */
+    int64_t n_qblocks;    /* ceil(lq / bq) */
+    int64_t capacity;     /* run slots per copy */
+    int64_t* row_ptr;     /* [batch][n_qblocks + 1] CSR offsets into the runs */
+    int32_t* run_begin;   /* [batch][capacity] first key block of the run */
+    int32_t* run_end;     /* [batch][capacity] one past the last key block */
+    uint8_t* run_kind;    /* [batch][capacity] BWA_TILE_FULL or BWA_TILE_PARTIAL */
+    int32_t* row_lo;      /* [batch][lq] */
+    int32_t* row_hi;      /* [batch][lq] */
+} bwa_blocks;
+
+/* Human-readable name of a status code (static string). */
+const char* bwa_status_string(int32_t status);
+
+/* Detail of the last failure in the calling thread (static per thread). */
+const char* bwa_last_error(void);
+
+/* BWATTN_VERSION of the built library. */
+int32_t bwa_version(void);
+
+/* Tile sizes the attention kernel uses for (dtype, D): *bq rows per query
+ * block, key blocks a multiple of *bkv.  Lists passed to bwa_attn_fwd must be
+ * built with this bq and a bkv that is a multiple of this bkv.  Host only. */
+int32_t bwa_attn_tile(int32_t dtype, int64_t D, int32_t* bq, int32_t* bkv);
+
+/*
+ * Storage needed by bwa_block_mask_build (host only, no launch, reads no
+ * device memory).  Outputs: *n_qblocks = ceil(lq / bq); *list_batch = copies
+ * (B with per-token segment ids, else 1); *capacity = run slots per copy that
+ * is always enough: 3 per query block without segments (a partial edge, a
+ * full middle, a partial edge), min(n_kblocks, bq + 2) per query block with
+ * segments.
+ */
+int32_t bwa_block_mask_size(const bwa_mask* mask, int64_t B, int64_t lq, int64_t lk,
+                            int32_t bq, int32_t bkv, int64_t* n_qblocks,
+                            int64_t* capacity, int64_t* list_batch);
+
+/*
+ * Build tile run lists and row intervals for mask on a [B, lq] x [B, lk]
+ * problem ([DKORDER]; the forward analogue of its partial/full block lists).
+ * out->bq, bkv, lq, lk, batch, n_qblocks and capacity must hold the values
+ * from bwa_block_mask_size (capacity may be larger) and its pointers the
+ * caller's device buffers.  bq and bkv must be positive multiples of 64.
+ * Results are exact integers (bit-exact against any correct implementation).
+ * Preconditions checked on the device only by construction: cu_seqlens and
+ * segment ids non-decreasing; violating them gives unspecified (but
+ * in-bounds) lists.
+ */
+int32_t bwa_block_mask_build(const bwa_mask* mask, int64_t B, int64_t lq, int64_t lk,
+                             bwa_blocks* out, void* stream);
+
+/*
+ * Fixed-m bound and gate [FIXEDM description and Notes].
+ *   kmax[b,h]  = max over chunks c and keys j < kv_valid[c] of ||k_c[b,j,h,:]||_2,
+ *                folded with max over c of kmax_in[c][b][h] when kmax_in is not
+ *                NULL (a caller's per-shard max||k|| promoted to the global bound);
+ *   m[b,h,i]   = scale * ||q[b,i,h,:]||_2 * kmax[b,h]   (natural-log units);
+ *   mmax[b,h]  = max over i < q_valid of m[b,h,i]   (0 when q_valid == 0);
+ *   gate[b,h]  = 1 if mmax[b,h] <= tau else 0   (a tie passes).
+ * q: [B, Lq, H, D]; k_chunks: host array of n_chunks tensors [B, Lk_c, H, D]
+ * with q's dtype, B, H and D; kv_valid: host array [n_chunks] (NULL = all
+ * keys valid; entries < 0 mean Lk_c); kmax_in: device [n_chunks][B][H] or
+ * NULL; q_valid < 0 means Lq.  Outputs are device arrays: kmax_out [B][H],
+ * mmax_out [B][H], m_out [B][H][Lq] (fp32), gate_out [B][H] (uint8).
+ * Norms are fp32 sums of squares (bf16 products are exact in fp32).
+ */
+int32_t bwa_fixed_m_bound(const bwa_tensor* q, const bwa_tensor* k_chunks, int32_t n_chunks,
+                          const float* kmax_in, const int64_t* kv_valid, int64_t q_valid,
+                          float scale, float tau, float* kmax_out, float* mmax_out,
+                          float* m_out, uint8_t* gate_out, void* stream);
+
+/*
+ * Blockwise attention forward on one key chunk.
+ *   O[b,i,h,:] = sum_j p_ij v[b,j,h,:] / sum_j p_ij over visible keys j,
+ *   LSE[b,h,i] = ln sum_j exp(scale * q_i . k_j)  (natural log),
+ * computed tile by tile over the listed key blocks with
+ *   BWA_MODE_ONLINE : a running row max and rescale of the partial sums,
+ *   BWA_MODE_FIXED_M: p_ij = exp(scale * q_i . k_j - m[b,h,i]) with the
+ *                     caller's per-row bound m (from bwa_fixed_m_bound); no
+ *                     max and no rescale [FIXEDM description].  The result
+ *                     is exact in real arithmetic whenever m bounds the row's
+ *                     scores; m is trusted, not checked.
+ * q: [B, Lq, H, D]; k, v: [B, Lk, H, D]; q, k, v share a dtype (BWA_BF16
+ * computes Q K^T and P V on bf16 matrix cores with fp32 accumulation and
+ * rounds P to bf16; BWA_F32 computes in fp32 throughout).  D is 64 or 128.
+ * o: [B, Lq, H, D] in fp32 or in q's dtype; lse: device fp32 [B][H][Lq].
+ * mask: required.  blocks: run lists from bwa_block_mask_build for this mask
+ * and shape (bq and bkv as bwa_attn_tile requires), or NULL to derive the
+ * tile walk from the mask inside the kernel (always correct; per-token
+ * segment ids then cost a per-row binary search).
+ * gate: device uint8 [B][H] or NULL.  When given, an online call processes
+ * only heads with gate == 0 and a fixed-m call only heads with gate != 0;
+ * the other heads' outputs are left untouched, so a gated pair of calls on
+ * the same outputs covers every head with one branch-free body each
+ * [FIXEDM Notes].
+ * Rows with no visible key (padding, alignment rows) get O = 0 and
+ * LSE = -inf and cost no tile work [H3 Modifications].
+ */
+int32_t bwa_attn_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
+                     const bwa_mask* mask, const bwa_blocks* blocks, float scale,
+                     int32_t mode, const float* m, const uint8_t* gate,
+                     bwa_tensor* o, float* lse, void* stream);
+
+/*
+ * Log-sum-exp merge of attention partials over disjoint key chunks
+ * [FIXEDM Notes: the fallback merge in LSE space, invariant to the overshoot]:
+ *   lse[b,h,i] = ln sum_t exp(lse_t[b,h,i])            (-inf if all are -inf)
+ *   O[b,i,h,:] = sum_t exp(lse_t - lse) O_t[b,i,h,:]    (0 if lse is -inf)
+ * n_parts in [1, 16]; o_parts: host array of n_parts fp32 tensors of one
+ * shape; lse_parts: host array of n_parts device pointers to fp32 [B][H][L];
+ * o_out: same B, L, H, D in fp32 or bf16 (may alias no input); lse_out:
+ * device fp32 [B][H][L] (may be NULL).
+ */
+int32_t bwa_lse_merge(int32_t n_parts, const bwa_tensor* o_parts, const float* const* lse_parts,
+                      bwa_tensor* o_out, float* lse_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BWATTN_H */

@@ -1,0 +1,67 @@
+"""Shared test helpers: oracle runs over [B, L, H, D] tensors and tolerance checks.
+
+Tolerances: bf16 inputs with fp32 accumulation -> output max-abs <= 2e-2 and
+mean-abs <= 2e-3; fp32 inputs -> max-abs <= 1e-5.  LSE: 1e-3 (bf16 inputs),
+1e-5 (fp32 inputs).  Rows that see nothing must be exactly 0 with LSE -inf.
+"""
+
+import numpy as np
+import torch
+
+import oracle
+
+TOL = {
+    torch.bfloat16: dict(max=2e-2, mean=2e-3, lse=1e-3),
+    torch.float32: dict(max=1e-5, mean=1e-5, lse=1e-5),
+}
+
+
+def np64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def mask_for_batch(mask, b):
+    m = dict(mask or {})
+    for key in ("segment_ids_q", "segment_ids_kv"):
+        if m.get(key) is not None:
+            a = np.asarray(m[key])
+            m[key] = a[b] if a.ndim == 2 else a
+    return m
+
+
+def oracle_attention(q, k, v, mask, scale, rows=None, heads=None):
+    """Oracle O [B, R, H', D] and LSE [B, H', R] for tensors in [B, L, H, D]."""
+    qn, kn, vn = np64(q), np64(k), np64(v)
+    B, Lq, H, D = qn.shape
+    heads = list(range(H)) if heads is None else list(heads)
+    rows = np.arange(Lq) if rows is None else np.asarray(rows)
+    O = np.zeros((B, len(rows), len(heads), D))
+    L = np.zeros((B, len(heads), len(rows)))
+    for b in range(B):
+        m = mask_for_batch(mask, b)
+        for n, h in enumerate(heads):
+            o, l = oracle.attention_rows(qn[b, :, h], kn[b, :, h], vn[b, :, h], m, scale, rows)
+            O[b, :, n] = o
+            L[b, n] = l
+    return O, L
+
+
+def assert_close(o_gpu, lse_gpu, o_ref, lse_ref, in_dtype, what=""):
+    tol = TOL[in_dtype]
+    o = o_gpu if isinstance(o_gpu, np.ndarray) else np64(o_gpu)
+    lse = lse_gpu if isinstance(lse_gpu, np.ndarray) else np64(lse_gpu)
+    assert o.shape == o_ref.shape, (o.shape, o_ref.shape)
+    dead = np.isneginf(lse_ref)  # [B, H, R]
+    assert np.array_equal(np.isneginf(lse), dead), f"{what}: -inf LSE rows differ"
+    dead_o = np.transpose(dead, (0, 2, 1))[..., None] & np.ones_like(o, dtype=bool)
+    assert np.all(o[dead_o] == 0), f"{what}: rows that see nothing must be exactly 0"
+    err = np.abs(o - o_ref)
+    assert np.all(np.isfinite(o)), f"{what}: non-finite output"
+    mx, mean = float(err.max(initial=0)), float(err.mean()) if err.size else 0.0
+    assert mx <= tol["max"], f"{what}: max abs err {mx:.3e} > {tol['max']}"
+    assert mean <= tol["mean"], f"{what}: mean abs err {mean:.3e} > {tol['mean']}"
+    live = ~dead
+    if live.any():
+        le = float(np.abs(lse[live] - lse_ref[live]).max())
+        assert le <= tol["lse"], f"{what}: LSE max abs err {le:.3e} > {tol['lse']}"
+    return mx, mean

@@ -1,0 +1,168 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry
+point, its struct layouts match the header, and argument errors come back as
+status codes before anything touches a GPU (no compute calls here).
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bwattn.h")
+
+bw = pytest.importorskip("blockwise_attention_forward_amd")
+L = bw._lib
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(bwa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 9
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    for n in ("bwa_attn_fwd", "bwa_lse_merge", "bwa_fixed_m_bound", "bwa_block_mask_build"):
+        assert n in names
+
+
+def test_struct_layout_matches_header():
+    src = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "bwattn.h"
+int main(void) {
+  printf("%zu %zu %zu %zu\n", sizeof(bwa_tensor), offsetof(bwa_tensor, B), offsetof(bwa_tensor, sH), sizeof(bwa_mask));
+  printf("%zu %zu %zu %zu\n", offsetof(bwa_mask, num_segments), offsetof(bwa_mask, segment_ids_kv), sizeof(bwa_blocks), offsetof(bwa_blocks, row_hi));
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as d:
+        c, exe = os.path.join(d, "t.c"), os.path.join(d, "t")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()
+    got = list(map(int, out))
+    want = [ctypes.sizeof(bw._Tensor), bw._Tensor.B.offset, bw._Tensor.sH.offset, ctypes.sizeof(bw._Mask),
+            bw._Mask.num_segments.offset, bw._Mask.segment_ids_kv.offset, ctypes.sizeof(bw._Blocks),
+            bw._Blocks.row_hi.offset]
+    assert got == want
+
+
+def test_version_and_status_strings():
+    assert bw.bwa_version() == 1
+    for code in range(9):
+        assert bw.bwa_status_string(code) != "unknown status"
+    assert bw.bwa_status_string(99) == "unknown status"
+
+
+def _t(ptr=0x10000, dtype=1, B=1, L=256, H=2, D=128, sB=None, sL=None, sH=None):
+    sH = D if sH is None else sH
+    sL = H * D if sL is None else sL
+    sB = L * H * D if sB is None else sB
+    return bw._Tensor(ptr, dtype, 0, B, L, H, D, sB, sL, sH)
+
+
+def _mask(**kw):
+    m = bw._Mask(0, 0, 0, -1, -1, 0, 0, None, None, None, None)
+    for k, v in kw.items():
+        setattr(m, k, v)
+    return m
+
+
+def _attn(q, k, v, o, mask=None, mode=0, m=None, lse=0x20000):
+    mask = mask or _mask()
+    return L.bwa_attn_fwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(mask), None, 0.1,
+                          mode, m, None, ctypes.byref(o), lse, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(q=dict(D=96), k=dict(D=96), v=dict(D=96), o=dict(D=96)), 6),
+    (dict(q=dict(ptr=0x10008)), 3),
+    (dict(q=dict(sL=2 * 128 + 4)), 3),
+    (dict(q=dict(ptr=0)), 1),
+    (dict(k=dict(dtype=0)), 4),
+    (dict(k=dict(dtype=7)), 4),
+    (dict(o=dict(L=255)), 2),
+    (dict(v=dict(L=100)), 2),
+    (dict(k=dict(H=3), v=dict(H=3)), 2),
+])
+def test_attn_fwd_argument_errors(case, code):
+    args = {n: _t(**case.get(n, {})) for n in ("q", "k", "v", "o")}
+    assert _attn(args["q"], args["k"], args["v"], args["o"]) == code
+    assert bw.bwa_last_error() != ""
+
+
+@pytest.mark.parametrize("mask,code", [
+    (dict(window=128), 5),                    # window needs causal
+    (dict(causal=2), 5),
+    (dict(q_valid=300), 5),                   # > Lq
+    (dict(kv_valid=300), 5),
+    (dict(num_segments=2), 5),                # segments without cu_seqlens
+    (dict(cu_seqlens_q=0x30000), 5),          # cu_seqlens without num_segments
+    (dict(cu_seqlens_q=0x30000, num_segments=1, segment_ids_q=0x40000), 5),
+])
+def test_mask_errors(mask, code):
+    q = _t()
+    assert _attn(q, _t(), _t(), _t(), mask=_mask(**mask)) == code
+
+
+def test_fixed_m_needs_m_and_lse():
+    q = _t()
+    assert _attn(q, _t(), _t(), _t(), mode=1, m=None) == 1
+    assert _attn(q, _t(), _t(), _t(), lse=None) == 1
+    assert _attn(q, _t(), _t(), _t(), mode=5) == 2
+
+
+def test_block_mask_size():
+    n, c, b = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    m = _mask(causal=1, window=512)
+    st = L.bwa_block_mask_size(ctypes.byref(m), 1, 4096, 4096, 128, 128, ctypes.byref(n), ctypes.byref(c),
+                               ctypes.byref(b))
+    assert st == 0 and n.value == 32 and c.value == 96 and b.value == 1
+    assert L.bwa_block_mask_size(ctypes.byref(m), 1, 4096, 4096, 100, 128, ctypes.byref(n), ctypes.byref(c),
+                                 ctypes.byref(b)) == 2
+    seg = _mask(cu_seqlens_q=0x30000, num_segments=3)
+    assert L.bwa_block_mask_size(ctypes.byref(seg), 1, 33024, 33024, 128, 128, ctypes.byref(n),
+                                 ctypes.byref(c), ctypes.byref(b)) == 0
+    assert n.value == 258 and c.value == 258 * 130 and b.value == 1
+    ids = _mask(segment_ids_q=0x30000)
+    assert L.bwa_block_mask_size(ctypes.byref(ids), 4, 512, 512, 128, 128, ctypes.byref(n),
+                                 ctypes.byref(c), ctypes.byref(b)) == 0
+    assert b.value == 4 and c.value == 4 * 4
+
+
+def test_block_mask_build_checks_capacity():
+    m = _mask(causal=1)
+    blk = bw._Blocks(128, 128, 1024, 1024, 1, 8, 23, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    assert L.bwa_block_mask_build(ctypes.byref(m), 1, 1024, 1024, ctypes.byref(blk), None) == 7
+    blk.n_qblocks = 9
+    assert L.bwa_block_mask_build(ctypes.byref(m), 1, 1024, 1024, ctypes.byref(blk), None) == 2
+
+
+def test_merge_and_bound_errors():
+    parts = (bw._Tensor * 1)(_t(dtype=0))
+    lps = (ctypes.c_void_p * 1)(0x20000)
+    out = _t()
+    assert L.bwa_lse_merge(0, parts, lps, ctypes.byref(out), None, None) == 2
+    assert L.bwa_lse_merge(17, parts, lps, ctypes.byref(out), None, None) == 2
+    bad = (bw._Tensor * 1)(_t(dtype=1))
+    assert L.bwa_lse_merge(1, bad, lps, ctypes.byref(out), None, None) == 4
+    q = _t()
+    ks = (bw._Tensor * 1)(_t(H=3))
+    assert L.bwa_fixed_m_bound(ctypes.byref(q), ks, 1, None, None, -1, 0.1, 106.5, 0x1000, 0x1000,
+                               0x1000, 0x1000, None) == 2
+    assert L.bwa_fixed_m_bound(ctypes.byref(q), ks, 17, None, None, -1, 0.1, 106.5, 0x1000, 0x1000,
+                               0x1000, 0x1000, None) == 2
+
+
+def test_attn_tile():
+    assert bw.bwa_attn_tile(1, 128) == (128, 64)
+    with pytest.raises(bw.BwaError):
+        bw.bwa_attn_tile(1, 80)

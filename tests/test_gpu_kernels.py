@@ -1,0 +1,213 @@
+"""GPU parity of every entry point against the fp64 oracle at small sizes.
+
+Sizes span several 128-row query blocks and 64-key tiles with ragged tails;
+every mask kind, both dtypes, both head dims, online and fixed-m, with and
+without precomputed run lists.  All calls go through the C ABI.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import assert_close, np64, oracle_attention
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU hosts too
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import blockwise_attention_forward_amd as bw  # noqa: E402
+
+DEV = "cuda"
+
+
+def _rand(shape, seed, dtype):
+    return synth.normal(shape, seed, DEV, dtype)
+
+
+def test_tiny_fp32_dense_and_chunk_merge():
+    t = synth.make_tiny(DEV)
+    q, k, v, scale = t["q"], t["k"], t["v"], t["scale"]
+    o, lse = bw.bwa_attn_fwd(q, k, v, {}, scale=scale)
+    o_ref, l_ref = oracle_attention(q, k, v, {}, scale)
+    assert_close(o, lse, o_ref, l_ref, torch.float32, "tiny fp32")
+    parts = []
+    for a, e in t["chunks"]:
+        parts.append(bw.bwa_attn_fwd(q, k[:, a:e], v[:, a:e], {"kv_offset": a}, scale=scale))
+    om, lm = bw.bwa_lse_merge([p[0] for p in parts], [p[1] for p in parts], out_dtype=torch.float32)
+    assert_close(om, lm, o_ref, l_ref, torch.float32, "tiny fp32 merged")
+
+
+MASKS = [
+    {},
+    {"causal": True},
+    {"causal": True, "window": 100},
+    {"causal": True, "window": 1},
+    {"causal": True, "kv_offset": 37},
+    {"causal": True, "kv_offset": -120, "window": 200},
+    {"q_valid": 290, "kv_valid": 301},
+    {"q_valid": 0},
+    {"kv_valid": 0},
+    {"cu_seqlens_q": [0, 70, 200, 333], "cu_seqlens_kv": [0, 70, 200, 333]},
+    {"cu_seqlens_q": [0, 150, 333], "cu_seqlens_kv": [0, 150, 333], "causal": True, "q_valid": 300},
+    {"cu_seqlens_q": [5, 100, 300], "cu_seqlens_kv": [0, 60, 333], "causal": True, "window": 50},
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mi", range(len(MASKS)))
+def test_masks_against_oracle(mi, D, dtype):
+    mask = MASKS[mi]
+    B, H, Lq, Lk = 2, 3, 333, 333
+    q = _rand((B, Lq, H, D), 10 + mi, dtype)
+    k = _rand((B, Lk, H, D), 20 + mi, dtype)
+    v = _rand((B, Lk, H, D), 30 + mi, dtype)
+    scale = 1 / math.sqrt(D)
+    o_ref, l_ref = oracle_attention(q, k, v, mask, scale)
+    o1, l1 = bw.bwa_attn_fwd(q, k, v, mask, scale=scale)
+    assert_close(o1, l1, o_ref, l_ref, dtype, f"inline walk {mask}")
+    bq, bkv = bw.bwa_attn_tile(dtype, D)
+    blocks = bw.bwa_block_mask_build(mask, B, Lq, Lk, bq, 128)
+    o2, l2 = bw.bwa_attn_fwd(q, k, v, mask, blocks=blocks, scale=scale)
+    assert_close(o2, l2, o_ref, l_ref, dtype, f"run lists {mask}")
+    # the two tile walks visit the same tiles in the same order
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("Lq,Lk", [(1, 1), (5, 700), (700, 5), (129, 64), (64, 129)])
+def test_shapes(Lq, Lk):
+    B, H, D = 1, 2, 128
+    q, k, v = (_rand((B, L, H, D), s, torch.bfloat16) for L, s in ((Lq, 1), (Lk, 2), (Lk, 3)))
+    for mask in ({}, {"causal": True, "kv_offset": Lq - Lk}):
+        o_ref, l_ref = oracle_attention(q, k, v, mask, 0.1)
+        o, l = bw.bwa_attn_fwd(q, k, v, mask, scale=0.1)
+        assert_close(o, l, o_ref, l_ref, torch.bfloat16, f"{Lq}x{Lk} {mask}")
+
+
+def test_empty_inputs():
+    q = _rand((1, 0, 2, 128), 1, torch.bfloat16)
+    k = _rand((1, 10, 2, 128), 2, torch.bfloat16)
+    o, l = bw.bwa_attn_fwd(q, k, k, {})
+    assert o.shape[1] == 0
+    q = _rand((1, 50, 2, 128), 1, torch.bfloat16)
+    k0 = _rand((1, 0, 2, 128), 2, torch.bfloat16)
+    o, l = bw.bwa_attn_fwd(q, k0, k0, {})
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(l))
+
+
+def test_segment_ids_per_batch_and_strided_views():
+    B, H, L, D = 2, 2, 300, 128
+    ids = np.stack([np.sort(np.random.default_rng(s).integers(0, 4, L)) for s in (1, 2)]).astype(np.int32)
+    mask = {"segment_ids_q": ids, "segment_ids_kv": ids, "causal": True}
+    qkv = _rand((B, L, 3 * H, D), 5, torch.bfloat16)  # packed projection: strided views
+    q, k, v = qkv[:, :, :H], qkv[:, :, H:2 * H], qkv[:, :, 2 * H:]
+    o_ref, l_ref = oracle_attention(q, k, v, mask, 0.09)
+    o, l = bw.bwa_attn_fwd(q, k, v, mask, scale=0.09)
+    assert_close(o, l, o_ref, l_ref, torch.bfloat16, "segment ids, inline")
+    blocks = bw.bwa_block_mask_build(mask, B, L, L, 128, 64)
+    o2, l2 = bw.bwa_attn_fwd(q, k, v, mask, blocks=blocks, scale=0.09)
+    assert torch.equal(o, o2) and torch.equal(l, l2)
+
+
+@pytest.mark.parametrize("mi", range(len(MASKS)))
+@pytest.mark.parametrize("bq,bkv", [(128, 128), (128, 64), (64, 192)])
+def test_block_lists_bit_exact(mi, bq, bkv):
+    mask = MASKS[mi]
+    Lq = Lk = 333
+    bl = bw.bwa_block_mask_build(mask, 1, Lq, Lk, bq, bkv)
+    rp, b, e, k = bl.host()
+    want = oracle.block_lists(mask, Lq, Lk, bq, bkv)
+    assert np.array_equal(rp, want[0]) and np.array_equal(b, want[1])
+    assert np.array_equal(e, want[2]) and np.array_equal(k, want[3])
+    lo, hi = oracle.row_intervals_bruteforce(Lq, Lk, mask)
+    assert np.array_equal(bl.row_lo[:Lq].cpu().numpy(), lo)
+    assert np.array_equal(bl.row_hi[:Lq].cpu().numpy(), hi)
+
+
+def test_fixed_m_bound_and_gate():
+    B, H, D = 2, 4, 128
+    q = _rand((B, 300, H, D), 40, torch.bfloat16)
+    ks = [_rand((B, n, H, D), 41 + i, torch.bfloat16) for i, n in enumerate((200, 170))]
+    ks[1][1, 7, 2] *= 50  # sink key in (b=1, h=2)
+    kv_valid = [200, 160]
+    ks[1][0, 165, 0] *= 1e3  # past kv_valid: must not enter the bound
+    kmax_in = torch.zeros(2, B, H, device=DEV)
+    kmax_in[0, 0, 3] = 400.0  # promoted to the global bound of (b=0, h=3)
+    scale = 1 / math.sqrt(D)
+    kmax, mmax, m, gate = bw.bwa_fixed_m_bound(q, ks, scale, 106.5, kmax_in=kmax_in, kv_valid=kv_valid,
+                                               q_valid=290)
+    for b in range(B):
+        for h in range(H):
+            km, mr, mm, g = oracle.fixed_m_bound(np64(q[b, :, h]), [np64(c[b, :, h]) for c in ks], scale,
+                                                 106.5, q_valid=290, kv_valid=kv_valid,
+                                                 kmax_in=np64(kmax_in[:, b, h]))
+            np.testing.assert_allclose(kmax[b, h].item(), km, rtol=1e-6)
+            np.testing.assert_allclose(np64(m[b, h]), mr, rtol=2e-6)
+            np.testing.assert_allclose(mmax[b, h].item(), mm, rtol=2e-6)
+            assert bool(gate[b, h].item()) == g
+    assert gate[1, 2].item() == 0 and gate[0, 3].item() == 0
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_fixed_m_attention_and_gated_pair(D):
+    B, H, Lq, Lk = 1, 4, 300, 400
+    scale = 1 / math.sqrt(D)
+    q = _rand((B, Lq, H, D), 50, torch.bfloat16)
+    k = _rand((B, Lk, H, D), 51, torch.bfloat16)
+    v = _rand((B, Lk, H, D), 52, torch.bfloat16)
+    k[0, 11, 1] *= 50  # head 1 fails the gate
+    for mask in ({}, {"causal": True, "kv_offset": -100}):
+        kmax, mmax, m, gate = bw.bwa_fixed_m_bound(q, [k], scale, 106.5)
+        assert gate[0].tolist() == [1, 0, 1, 1]
+        o_ref, l_ref = oracle_attention(q, k, v, mask, scale)
+        # every head in fixed-m mode: exact for the eligible heads
+        o, l = bw.bwa_attn_fwd(q, k, v, mask, scale=scale, mode=bw.BWA_MODE_FIXED_M, m=m,
+                               out_dtype=torch.float32)
+        for h in (0, 2, 3):
+            assert_close(o[:, :, h:h + 1], l[:, h:h + 1], o_ref[:, :, h:h + 1], l_ref[:, h:h + 1],
+                         torch.bfloat16, f"fixed-m head {h}")
+        # gated pair: fixed-m on passing heads, online on the failing head
+        o2 = torch.full_like(o, float("nan"))
+        l2 = torch.full_like(l, float("nan"))
+        bw.bwa_attn_fwd(q, k, v, mask, scale=scale, mode=bw.BWA_MODE_FIXED_M, m=m, gate=gate, o=o2, lse=l2)
+        bw.bwa_attn_fwd(q, k, v, mask, scale=scale, mode=bw.BWA_MODE_ONLINE, gate=gate, o=o2, lse=l2)
+        assert_close(o2, l2, o_ref, l_ref, torch.bfloat16, "gated pair")
+
+
+@pytest.mark.parametrize("n_parts", [1, 2, 3])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_lse_merge_against_oracle(n_parts, out_dtype):
+    B, L, H, D = 2, 77, 3, 128
+    g = torch.Generator(device=DEV).manual_seed(60 + n_parts)
+    os_ = [torch.randn(B, L, H, D, device=DEV, generator=g) for _ in range(n_parts)]
+    ls = [torch.randn(B, H, L, device=DEV, generator=g) * 5 for _ in range(n_parts)]
+    for t in range(n_parts):
+        ls[t][0, 0, :10] = -float("inf")  # rows some chunk did not see
+    ls[0][1, 2, 5] = -float("inf")
+    if n_parts > 1:
+        for t in range(n_parts):
+            ls[t][1, 1, 3] = -float("inf")  # row no chunk saw
+            os_[t][1, 3, 1] = 0
+    o, l = bw.bwa_lse_merge(os_, ls, out_dtype=out_dtype)
+    ref_o, ref_l = oracle.lse_merge([(np64(a).transpose(0, 2, 1, 3), np64(b)) for a, b in zip(os_, ls)])
+    ref_o = ref_o.transpose(0, 2, 1, 3)
+    got_l = np64(l)
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(ref_l))
+    f = np.isfinite(ref_l)
+    np.testing.assert_allclose(got_l[f], ref_l[f], atol=1e-5, rtol=0)
+    tol = 1e-5 if out_dtype == torch.float32 else 1e-2
+    np.testing.assert_allclose(np64(o), ref_o, atol=tol, rtol=0 if out_dtype == torch.float32 else 8e-3)
+
+
+def test_deterministic_repeat():
+    B, H, L, D = 1, 4, 500, 128
+    q, k, v = (_rand((B, L, H, D), s, torch.bfloat16) for s in (70, 71, 72))
+    mask = {"causal": True, "window": 200}
+    outs = [bw.bwa_attn_fwd(q, k, v, mask) for _ in range(2)]
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])

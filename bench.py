@@ -1,0 +1,279 @@
+"""Benchmark of the blockwise attention forward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dit_share]
+
+Prints ONE JSON line.  A step is one pass of the whole hot path over one
+batch of synthetic input already resident in HBM.  The default workload is
+one rank's share of 2-ring x 2-Ulysses video-DiT self-attention (720p
+81-frame latent grid 21x45x80 = 75,600 tokens; this rank: 20 heads, the
+query shard of 37,800 tokens, keys as 2 sequential hops of 37,800), and a
+step runs: tile run lists for each hop, the fixed-m bound and gate over both
+key chunks, per hop one gated attention launch (fixed-m loop for the heads
+that pass the gate, online loop for the rest: one sink head), and the LSE
+merge of the two hop partials into the bf16 output.
+
+value      = counted attention FLOPs per step / step time (TFLOP/s), FLOPs
+             counted on a 128x128 tile grid over non-skipped tiles, 4*D per
+             visible (row, key) pair of those tiles.
+roofline   = the dominant kernel (the gated attention launch of one hop):
+             algorithmic FLOPs per launch / its mean launch time (HIP events on
+             the launch stream), against the bf16 dense matrix-core peak.
+cpu_baseline = the fp64 oracle timed on the host on a bounded sample of the
+             same workload (rank 0, N = 1 only).
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def _counted_flops(blocks, D, heads, lq, lk):
+    """FLOPs on the 128x128 counting grid from a run list built at 128x128."""
+    import numpy as np
+    s = blocks.struct
+    assert s.bq == 128 and s.bkv == 128
+    total = 0.0
+    for copy in range(s.batch):
+        rp, b, e, _ = blocks.host(copy)
+        for qb in range(s.n_qblocks):
+            rows = min(lq, (qb + 1) * 128) - qb * 128
+            for r in range(rp[qb], rp[qb + 1]):
+                c0, c1 = int(b[r]) * 128, min(lk, int(e[r]) * 128)
+                total += rows * (c1 - c0)
+    return 4.0 * D * heads * total
+
+
+class Timer:
+    """HIP events recorded on the current (launch) stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def start(self, key):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return (key, e)
+
+    def stop(self, tok):
+        key, s = tok
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.setdefault(key, []).append((s, e))
+
+    def mean_ms(self, key):
+        ps = self.pairs.get(key, [])
+        return sum(s.elapsed_time(e) for s, e in ps) / len(ps) if ps else float("nan")
+
+    def reset(self):
+        self.pairs = {}
+
+
+def _source_sha():
+    p = os.path.join(ROOT, "blockwise_attention_forward_amd", "csrc", "attn_fwd.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def _traffic(kernel_key):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+    p = os.path.join(ROOT, "profiles", "attn_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    rec = d.get(kernel_key)
+    if not rec or rec.get("source_sha") != _source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def setup_dit_share(torch, bw, synth):
+    d = synth.make_dit_share("cuda")
+    q, ks, vs = d["q"], d["k_chunks"], d["v_chunks"]
+    B, Lq, H, D = q.shape
+    Lc = ks[0].shape[1]
+    scale, tau = d["scale"], d["tau"]
+    masks = [bw.Mask("cuda", kv_offset=off) for off in d["kv_offsets"]]
+    bq, _ = bw.bwa_attn_tile(q.dtype, D)
+    blocks = [bw.bwa_block_mask_build(m, B, Lq, Lc, bq, 128) for m in masks]
+    count_lists = bw.bwa_block_mask_build(masks[0], B, Lq, Lc, 128, 128)
+    bound_out = (torch.empty(B, H, device="cuda"), torch.empty(B, H, device="cuda"),
+                 torch.empty(B, H, Lq, device="cuda"), torch.empty(B, H, dtype=torch.uint8, device="cuda"))
+    o_parts = [torch.empty(B, Lq, H, D, device="cuda") for _ in ks]
+    l_parts = [torch.empty(B, H, Lq, device="cuda") for _ in ks]
+    o_out = torch.empty(B, Lq, H, D, dtype=torch.bfloat16, device="cuda")
+    l_out = torch.empty(B, H, Lq, device="cuda")
+    torch.cuda.synchronize()
+    flops_hop = _counted_flops(count_lists, D, H, Lq, Lc)
+    gate_host = None
+
+    def step(timer=None):
+        for t, m in enumerate(masks):
+            bw.bwa_block_mask_build(m, B, Lq, Lc, bq, 128, out=blocks[t])
+        tb = timer.start("bound") if timer else None
+        kmax, mmax, mm, gate = bw.bwa_fixed_m_bound(q, ks, scale, tau, out=bound_out)
+        if timer:
+            timer.stop(tb)
+        for t in range(len(ks)):
+            tok = timer.start("hop") if timer else None
+            bw.bwa_attn_fwd(q, ks[t], vs[t], m=mm, mask=masks[t], blocks=blocks[t], scale=scale,
+                            mode=bw.BWA_MODE_GATED, gate=gate, o=o_parts[t], lse=l_parts[t])
+            if timer:
+                timer.stop(tok)
+        tm = timer.start("merge") if timer else None
+        bw.bwa_lse_merge(o_parts, l_parts, o_out, l_out)
+        if timer:
+            timer.stop(tm)
+
+    def online_hop(timer):
+        tok = timer.start("online_hop")
+        bw.bwa_attn_fwd(q, ks[0], vs[0], mask=masks[0], blocks=blocks[0], scale=scale,
+                        mode=bw.BWA_MODE_ONLINE, o=o_parts[0], lse=l_parts[0])
+        timer.stop(tok)
+        # every head through the branch-free fixed-m body (timing only: the
+        # sink head's output from this launch is not used)
+        tok = timer.start("fixed_hop")
+        bw.bwa_attn_fwd(q, ks[0], vs[0], mask=masks[0], blocks=blocks[0], scale=scale, m=bound_out[2],
+                        mode=bw.BWA_MODE_FIXED_M, o=o_parts[0], lse=l_parts[0])
+        timer.stop(tok)
+
+    step()
+    torch.cuda.synchronize()
+    gate_host = bound_out[3].cpu()
+    n_fixed = int(gate_host.sum())
+    info = dict(
+        workload="dit_share: one rank's share of ring2 x uly2 video-DiT self-attention "
+                 "(21x45x80 latent tokens), B=1 H=20 D=128 bf16, Lq=37800 vs 2 KV hops of 37800, "
+                 "fixed-m (gate 106.5) with one sink head on online fallback in one gated launch per hop, "
+                 "LSE merge to bf16",
+        B=B, H=H, D=D, Lq=Lq, Lk_per_hop=Lc, hops=len(ks), heads_fixed_m=n_fixed,
+        sink_head=d["sink_head"])
+    flops_step = flops_hop * len(ks)
+    bytes_merge = (len(ks) * (B * Lq * H * D * 4 + B * H * Lq * 4) + B * Lq * H * D * 2 + B * H * Lq * 4)
+    bytes_bound = (B * Lq * H * D * 2 + sum(B * k.shape[1] * H * D * 2 for k in ks) + B * H * Lq * 4 * 3)
+
+    def sample_oracle():
+        """fp64 oracle on a bounded sample: rows of one head against all 75,600 keys."""
+        import numpy as np
+        import oracle
+        h = 0
+        rows = synth.sample_rows(Lq, 256, seed=11, must=[0, Lq - 1])
+        qh = q[0, :, h].double().cpu().numpy()
+        kh = torch.cat([k[0, :, h] for k in ks]).double().cpu().numpy()
+        vh = torch.cat([v[0, :, h] for v in vs]).double().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.attention_rows(qh, kh, vh, {}, scale, rows)
+        dt = time.perf_counter() - t0
+        fl = 4.0 * D * len(rows) * kh.shape[0]
+        return fl, dt, f"head 0, {len(rows)} seeded query rows x all {kh.shape[0]} keys (both hops), fp64"
+
+    return dict(step=step, online_hop=online_hop, flops_step=flops_step, flops_dominant=flops_hop,
+                dominant="hop", info=info, bytes_merge=bytes_merge, bytes_bound=bytes_bound,
+                sample_oracle=sample_oracle, hops=len(ks))
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dit_share", choices=["dit_share"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share only (one MI355X); multi-GPU runs are not part of "
+              "this build: run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import blockwise_attention_forward_amd as bw
+    import synth
+
+    torch.cuda.set_device(0)
+    W = setup_dit_share(torch, bw, synth)
+    timer = Timer(torch)
+    for _ in range(args.warmup):
+        W["step"]()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    for _ in range(args.steps):
+        W["step"](timer)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    value = W["flops_step"] / (ms_step * 1e-3) / 1e12
+    ms_hop = timer.mean_ms("hop")
+    ms_fixed = timer.mean_ms(W["dominant"])
+    ms_merge = timer.mean_ms("merge")
+    ms_bound = timer.mean_ms("bound")
+    achieved = W["flops_dominant"] / (ms_fixed * 1e-3) / 1e12
+
+    t2 = Timer(torch)
+    for _ in range(5):
+        W["online_hop"](t2)
+    torch.cuda.synchronize()
+    ms_online_hop = t2.mean_ms("online_hop")
+    ms_fixed_hop = t2.mean_ms("fixed_hop")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        fl, dt, what = W["sample_oracle"]()
+        cpu = {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+               "sample": what, "seconds": round(dt, 3),
+               "host_cores_available": len(os.sched_getaffinity(0))}
+
+    out = {
+        "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak; ms per KV hop",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": W["info"],
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "ms_per_kv_hop": round(ms_hop, 4),
+        "online_only_ms_per_kv_hop": round(ms_online_hop, 4),
+        "fixed_m_all_heads_ms_per_kv_hop": round(ms_fixed_hop, 4),
+        "merge_ms": round(ms_merge, 4),
+        "merge_GBps": round(W["bytes_merge"] / (ms_merge * 1e-3) / 1e9, 1),
+        "bound_ms": round(ms_bound, 4),
+        "bound_GBps": round(W["bytes_bound"] / (ms_bound * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic("attn_fwd_bf16_gated")},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

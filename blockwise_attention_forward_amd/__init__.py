@@ -16,7 +16,7 @@ import os
 import torch
 
 __all__ = [
-    "BWA_F32", "BWA_BF16", "BWA_MODE_ONLINE", "BWA_MODE_FIXED_M",
+    "BWA_F32", "BWA_BF16", "BWA_MODE_ONLINE", "BWA_MODE_FIXED_M", "BWA_MODE_GATED",
     "BWA_TILE_SKIP", "BWA_TILE_FULL", "BWA_TILE_PARTIAL", "BwaError", "Mask", "BlockLists",
     "lib_path", "bwa_version", "bwa_status_string", "bwa_last_error", "bwa_attn_tile",
     "bwa_block_mask_size", "bwa_block_mask_build", "bwa_fixed_m_bound", "bwa_attn_fwd",
@@ -24,7 +24,7 @@ __all__ = [
 ]
 
 BWA_F32, BWA_BF16 = 0, 1
-BWA_MODE_ONLINE, BWA_MODE_FIXED_M = 0, 1
+BWA_MODE_ONLINE, BWA_MODE_FIXED_M, BWA_MODE_GATED = 0, 1, 2
 BWA_TILE_SKIP, BWA_TILE_FULL, BWA_TILE_PARTIAL = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

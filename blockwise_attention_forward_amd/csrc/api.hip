@@ -122,7 +122,7 @@ int32_t bwa_attn_tile(int32_t dtype, int64_t D, int32_t* bq, int32_t* bkv) {
     if (!bq || !bkv) return fail(BWA_ERR_NULL_ARG, "bq/bkv output is NULL");
     if (dtype != BWA_F32 && dtype != BWA_BF16) return fail(BWA_ERR_BAD_DTYPE, "unknown dtype %d", dtype);
     if (D != 64 && D != 128) return fail(BWA_ERR_UNSUPPORTED, "head dim %lld", (long long)D);
-    *bq = 128;
+    *bq = bwa::attn_rows_per_block(dtype, (int)D);
     *bkv = 64;
     return ok();
 }
@@ -234,11 +234,13 @@ int32_t bwa_attn_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor*
     if (k->L != v->L) return fail(BWA_ERR_BAD_SHAPE, "k and v lengths differ");
     if (o->B != q->B || o->L != q->L || o->H != q->H || o->D != q->D)
         return fail(BWA_ERR_BAD_SHAPE, "o must have q's shape");
-    if (mode != BWA_MODE_ONLINE && mode != BWA_MODE_FIXED_M) return fail(BWA_ERR_BAD_SHAPE, "unknown mode %d", mode);
+    if (mode != BWA_MODE_ONLINE && mode != BWA_MODE_FIXED_M && mode != BWA_MODE_GATED)
+        return fail(BWA_ERR_BAD_SHAPE, "unknown mode %d", mode);
     const i64 B = q->B, H = q->H, Lq = q->L, Lk = k->L;
     const i64 rows = B * H * Lq;
     if (rows > 0 && !lse) return fail(BWA_ERR_NULL_ARG, "lse is NULL");
-    if (mode == BWA_MODE_FIXED_M && rows > 0 && !m) return fail(BWA_ERR_NULL_ARG, "fixed-m mode needs m");
+    if (mode != BWA_MODE_ONLINE && rows > 0 && !m) return fail(BWA_ERR_NULL_ARG, "fixed-m and gated modes need m");
+    if (mode == BWA_MODE_GATED && rows > 0 && !gate) return fail(BWA_ERR_NULL_ARG, "gated mode needs gate");
     bwa::AttnLaunch a;
     memset(&a, 0, sizeof(a));
     if ((st = resolve_mask(mask, B, Lq, Lk, a.mask))) return st;

@@ -97,6 +97,7 @@ struct AttnLaunch {
     MaskDev mask;
 };
 hipError_t launch_attn_fwd(const AttnLaunch& a, hipStream_t stream);
+int attn_rows_per_block(int dtype, int D);
 
 struct BlocksLaunch {
     MaskDev mask;

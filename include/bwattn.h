@@ -66,7 +66,8 @@ enum { BWA_F32 = 0, BWA_BF16 = 1 };
 /* Attention modes. */
 enum {
     BWA_MODE_ONLINE = 0,  /* running row max and rescale [FIXEDM description] */
-    BWA_MODE_FIXED_M = 1  /* precomputed per-row bound m in place of the max [FIXEDM] */
+    BWA_MODE_FIXED_M = 1, /* precomputed per-row bound m in place of the max [FIXEDM] */
+    BWA_MODE_GATED = 2    /* per head: fixed-m where gate != 0, online elsewhere [FIXEDM Notes] */
 };
 
 /* Tile kinds in run lists [DKORDER "Sliding window perf issue"]. */
@@ -149,8 +150,9 @@ const char* bwa_last_error(void);
 int32_t bwa_version(void);
 
 /* Tile sizes the attention kernel uses for (dtype, D): *bq rows per query
- * block, key blocks a multiple of *bkv.  Lists passed to bwa_attn_fwd must be
- * built with this bq and a bkv that is a multiple of this bkv.  Host only. */
+ * block (256 for bf16 with D = 128, else 128), key tiles of *bkv (64).  Lists
+ * passed to bwa_attn_fwd must be built with this bq and a bkv that is a
+ * multiple of this bkv.  Host only. */
 int32_t bwa_attn_tile(int32_t dtype, int64_t D, int32_t* bq, int32_t* bkv);
 
 /*
@@ -222,7 +224,10 @@ int32_t bwa_fixed_m_bound(const bwa_tensor* q, const bwa_tensor* k_chunks, int32
  * only heads with gate == 0 and a fixed-m call only heads with gate != 0;
  * the other heads' outputs are left untouched, so a gated pair of calls on
  * the same outputs covers every head with one branch-free body each
- * [FIXEDM Notes].
+ * [FIXEDM Notes].  BWA_MODE_GATED (gate and m required) does both in one
+ * launch: each query block runs the fixed-m loop if its head passed the gate
+ * and the online loop otherwise (two separate loops, one per workgroup), so
+ * a single failing head does not leave a small second grid.
  * Rows with no visible key (padding, alignment rows) get O = 0 and
  * LSE = -inf and cost no tile work [H3 Modifications].
  */

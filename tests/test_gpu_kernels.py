@@ -110,7 +110,8 @@ def test_segment_ids_per_batch_and_strided_views():
     o_ref, l_ref = oracle_attention(q, k, v, mask, 0.09)
     o, l = bw.bwa_attn_fwd(q, k, v, mask, scale=0.09)
     assert_close(o, l, o_ref, l_ref, torch.bfloat16, "segment ids, inline")
-    blocks = bw.bwa_block_mask_build(mask, B, L, L, 128, 64)
+    bq, _ = bw.bwa_attn_tile(torch.bfloat16, D)
+    blocks = bw.bwa_block_mask_build(mask, B, L, L, bq, 64)
     o2, l2 = bw.bwa_attn_fwd(q, k, v, mask, blocks=blocks, scale=0.09)
     assert torch.equal(o, o2) and torch.equal(l, l2)
 
@@ -178,6 +179,10 @@ def test_fixed_m_attention_and_gated_pair(D):
         bw.bwa_attn_fwd(q, k, v, mask, scale=scale, mode=bw.BWA_MODE_FIXED_M, m=m, gate=gate, o=o2, lse=l2)
         bw.bwa_attn_fwd(q, k, v, mask, scale=scale, mode=bw.BWA_MODE_ONLINE, gate=gate, o=o2, lse=l2)
         assert_close(o2, l2, o_ref, l_ref, torch.bfloat16, "gated pair")
+        # one gated launch: the same two loops chosen per workgroup, same bits
+        o3, l3 = bw.bwa_attn_fwd(q, k, v, mask, scale=scale, mode=bw.BWA_MODE_GATED, m=m, gate=gate,
+                                 out_dtype=torch.float32)
+        assert torch.equal(o3, o2) and torch.equal(l3, l2)
 
 
 @pytest.mark.parametrize("n_parts", [1, 2, 3])

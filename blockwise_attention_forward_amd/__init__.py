@@ -74,7 +74,7 @@ def _load():
         "bwa_attn_tile": (I32, [I32, I64, I32P, I32P]),
         "bwa_block_mask_size": (I32, [MP, I64, I64, I64, I32, I32, I64P, I64P, I64P]),
         "bwa_block_mask_build": (I32, [MP, I64, I64, I64, BP, P]),
-        "bwa_fixed_m_bound": (I32, [TP, TP, I32, P, I64P, I64, F32, F32, P, P, P, P, P]),
+        "bwa_fixed_m_bound": (I32, [TP, TP, I32, P, I32, I64P, I64, F32, F32, P, P, P, P, P]),
         "bwa_attn_fwd": (I32, [TP, TP, TP, MP, BP, F32, I32, P, P, TP, P, P]),
         "bwa_lse_merge": (I32, [I32, TP, ctypes.POINTER(ctypes.c_void_p), TP, P, P]),
     }
@@ -217,7 +217,10 @@ def bwa_block_mask_build(mask, B, lq, lk, bq=128, bkv=128, device="cuda", out=No
 
 
 def bwa_fixed_m_bound(q, k_chunks, scale, tau, kmax_in=None, kv_valid=None, q_valid=-1, out=None):
-    """Per-row bound m, per-head key max, max bound and gate.  Returns (kmax, mmax, m, gate)."""
+    """Per-row bound m, per-head key max, max bound and gate.  Returns (kmax, mmax, m, gate).
+
+    kmax_in: optional [S, B, H] fp32 device tensor of other shards' max||k||.
+    """
     B, Lq, H, _ = q.shape
     if out is None:
         out = (torch.empty(B, H, dtype=torch.float32, device=q.device),
@@ -231,7 +234,10 @@ def bwa_fixed_m_bound(q, k_chunks, scale, tau, kmax_in=None, kv_valid=None, q_va
     if kv_valid is not None:
         kv = (ctypes.c_int64 * n)(*[int(x) for x in kv_valid])
     qt = _tensor(q)
-    _check(_lib.bwa_fixed_m_bound(ctypes.byref(qt), arr, n, _ptr(kmax_in), kv, int(q_valid),
+    n_in = 0 if kmax_in is None else int(kmax_in.numel() // max(1, B * H))
+    if kmax_in is not None:
+        kmax_in = kmax_in.to(torch.float32).contiguous()
+    _check(_lib.bwa_fixed_m_bound(ctypes.byref(qt), arr, n, _ptr(kmax_in), n_in, kv, int(q_valid),
                                   float(scale), float(tau), _ptr(kmax), _ptr(mmax), _ptr(m),
                                   _ptr(gate), _stream(q.device)), "bwa_fixed_m_bound")
     return kmax, mmax, m, gate

@@ -132,8 +132,8 @@ int32_t bwa_block_mask_size(const bwa_mask* mask, int64_t B, int64_t lq, int64_t
     if (!n_qblocks || !capacity || !list_batch) return fail(BWA_ERR_NULL_ARG, "size outputs are NULL");
     if (B < 0 || lq < 0 || lk < 0) return fail(BWA_ERR_BAD_SHAPE, "negative size");
     if (lq > kMaxLen || lk > kMaxLen) return fail(BWA_ERR_UNSUPPORTED, "length exceeds 2^30");
-    if (bq <= 0 || bkv <= 0 || bq % 64 || bkv % 64)
-        return fail(BWA_ERR_BAD_SHAPE, "bq and bkv must be positive multiples of 64");
+    if (bq <= 0 || bkv <= 0 || bq % 64 || bkv % 64 || bq > 512)
+        return fail(BWA_ERR_BAD_SHAPE, "bq and bkv must be positive multiples of 64 (bq <= 512)");
     bwa::MaskDev md;
     int32_t st = resolve_mask(mask, B, lq, lk, md);
     if (st) return st;
@@ -174,7 +174,8 @@ int32_t bwa_block_mask_build(const bwa_mask* mask, int64_t B, int64_t lq, int64_
 }
 
 int32_t bwa_fixed_m_bound(const bwa_tensor* q, const bwa_tensor* k_chunks, int32_t n_chunks,
-                          const float* kmax_in, const int64_t* kv_valid, int64_t q_valid, float scale,
+                          const float* kmax_in, int32_t n_kmax_in, const int64_t* kv_valid, int64_t q_valid,
+                          float scale,
                           float tau, float* kmax_out, float* mmax_out, float* m_out, uint8_t* gate_out,
                           void* stream) {
     int32_t st = check_tensor(q, "q");
@@ -183,6 +184,8 @@ int32_t bwa_fixed_m_bound(const bwa_tensor* q, const bwa_tensor* k_chunks, int32
         return fail(BWA_ERR_BAD_SHAPE, "n_chunks must be in [0, %d]", bwa::kMaxChunks);
     if (n_chunks > 0 && !k_chunks) return fail(BWA_ERR_NULL_ARG, "k_chunks is NULL");
     if (q_valid > q->L) return fail(BWA_ERR_BAD_SHAPE, "q_valid > Lq");
+    if (n_kmax_in < 0) return fail(BWA_ERR_BAD_SHAPE, "n_kmax_in < 0");
+    if (n_kmax_in > 0 && !kmax_in) return fail(BWA_ERR_NULL_ARG, "kmax_in is NULL with n_kmax_in > 0");
     const i64 BH = q->B * q->H;
     if (BH > 0 && (!kmax_out || !mmax_out || !gate_out || (q->L > 0 && !m_out)))
         return fail(BWA_ERR_NULL_ARG, "bound outputs must be non-NULL");
@@ -208,7 +211,8 @@ int32_t bwa_fixed_m_bound(const bwa_tensor* q, const bwa_tensor* k_chunks, int32
     a.H = (int)q->H;
     a.D = (int)q->D;
     a.dtype = q->dtype;
-    a.kmax_in = kmax_in;
+    a.kmax_in = n_kmax_in > 0 ? kmax_in : nullptr;
+    a.n_kmax_in = n_kmax_in;
     a.scale = scale;
     a.tau = tau;
     a.kmax_out = kmax_out;

@@ -29,7 +29,14 @@ __global__ __launch_bounds__(256) void rows_kernel(const BlocksLaunch a) {
     a.row_hi[idx] = hi;
 }
 
-// One wavefront per (copy, query block).  Each lane holds bq/64 rows.
+// One wavefront per (copy, query block); each lane keeps bq/64 rows'
+// intervals in registers.  A key block is FULL iff every row of the block
+// covers it, i.e. j0 >= max lo and min(j0 + bkv, lk) <= min hi over the
+// block's rows (all non-empty), so the FULL blocks form one range computed
+// directly.  Only the blocks outside it are tested one by one (a block is
+// visited iff some row's interval meets it), with wave ballots.
+constexpr int kMaxRowsPerLane = 8;  // bq <= 512
+
 template <bool FILL>
 __global__ __launch_bounds__(256) void runs_kernel(const BlocksLaunch a) {
     const i64 wg = (i64)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -38,67 +45,85 @@ __global__ __launch_bounds__(256) void runs_kernel(const BlocksLaunch a) {
     const int lane = threadIdx.x & 63;
     const i64 copy = wg / nqb, qb = wg % nqb;
     const i64 lq = a.mask.lq, lk = a.mask.lk;
-    const int* rlo = a.row_lo + copy * lq;
-    const int* rhi = a.row_hi + copy * lq;
     const int per_lane = a.bq / 64;
-
-    // Range of key blocks any row of this block can meet.
-    int mn_lo = 0x7fffffff, mx_hi = 0;
-    for (int t = 0; t < per_lane; ++t) {
+    int rlo[kMaxRowsPerLane], rhi[kMaxRowsPerLane];
+    bool rex[kMaxRowsPerLane];
+    int mn_lo = 0x7fffffff, mx_hi = 0, mx_lo = 0, mn_hi = 0x7fffffff;
+#pragma unroll
+    for (int t = 0; t < kMaxRowsPerLane; ++t) {
         const i64 r = qb * a.bq + lane + 64 * t;
-        if (r < lq) {
-            const int lo = rlo[r], hi = rhi[r];
-            if (lo < hi) { mn_lo = min(mn_lo, lo); mx_hi = max(mx_hi, hi); }
+        rex[t] = t < per_lane && r < lq;
+        rlo[t] = rex[t] ? a.row_lo[copy * lq + r] : 0;
+        rhi[t] = rex[t] ? a.row_hi[copy * lq + r] : 0;
+        if (rex[t]) {
+            const bool ne = rlo[t] < rhi[t];
+            if (ne) { mn_lo = min(mn_lo, rlo[t]); mx_hi = max(mx_hi, rhi[t]); }
+            mx_lo = max(mx_lo, ne ? rlo[t] : 0x7fffffff);  // an empty row rules out FULL
+            mn_hi = min(mn_hi, ne ? rhi[t] : -1);
         }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         mn_lo = min(mn_lo, __shfl_xor(mn_lo, o));
         mx_hi = max(mx_hi, __shfl_xor(mx_hi, o));
+        mx_lo = max(mx_lo, __shfl_xor(mx_lo, o));
+        mn_hi = min(mn_hi, __shfl_xor(mn_hi, o));
     }
     i64* rp = a.row_ptr + copy * (nqb + 1);
-    i64 out = 0;
-    if (FILL) out = rp[qb];
+    const i64 out = FILL ? rp[qb] : 0;
     i64 n = 0;
+    int cur_kind = 0, cur_b = 0, cur_e = 0;
+    auto emit = [&]() {
+        if (FILL && lane == 0) {
+            const i64 slot = out + n;
+            if (slot < a.capacity) {
+                a.run_begin[copy * a.capacity + slot] = cur_b;
+                a.run_end[copy * a.capacity + slot] = cur_e;
+                a.run_kind[copy * a.capacity + slot] = (uint8_t)cur_kind;
+            }
+        }
+        ++n;
+    };
+    auto push = [&](int kb, int kind) {
+        if (kind == BWA_TILE_SKIP) {
+            if (cur_kind) { emit(); cur_kind = 0; }
+        } else if (cur_kind == kind && cur_e == kb) {
+            cur_e = kb + 1;
+        } else {
+            if (cur_kind) emit();
+            cur_kind = kind; cur_b = kb; cur_e = kb + 1;
+        }
+    };
+    auto partial_range = [&](int k0, int k1) {  // blocks known not to be FULL
+        for (int kb = k0; kb < k1; ++kb) {
+            const i64 j0 = (i64)kb * a.bkv, j1 = min(j0 + a.bkv, lk);
+            bool meets = false;
+#pragma unroll
+            for (int t = 0; t < kMaxRowsPerLane; ++t)
+                meets |= rex[t] && rlo[t] < rhi[t] && rlo[t] < j1 && rhi[t] > j0;
+            push(kb, __ballot(meets) != 0 ? BWA_TILE_PARTIAL : BWA_TILE_SKIP);
+        }
+    };
     if (mx_hi > 0) {
+        const int nkb = (int)((lk + a.bkv - 1) / a.bkv);
         const int kb_lo = mn_lo / a.bkv;
         const int kb_hi = (int)((mx_hi + (i64)a.bkv - 1) / a.bkv);
-        int cur_kind = 0, cur_b = 0, cur_e = 0;
-        auto emit = [&]() {
-            if (FILL && lane == 0) {
-                const i64 slot = out + n;
-                if (slot < a.capacity) {
-                    a.run_begin[copy * a.capacity + slot] = cur_b;
-                    a.run_end[copy * a.capacity + slot] = cur_e;
-                    a.run_kind[copy * a.capacity + slot] = (uint8_t)cur_kind;
-                }
-            }
-            ++n;
-        };
-        for (int kb = kb_lo; kb < kb_hi; ++kb) {
-            const i64 j0 = (i64)kb * a.bkv;
-            const i64 j1 = min(j0 + a.bkv, lk);
-            bool meets = false, covers = true;
-            for (int t = 0; t < per_lane; ++t) {
-                const i64 r = qb * a.bq + lane + 64 * t;
-                if (r < lq) {
-                    const int lo = rlo[r], hi = rhi[r];
-                    const bool ne = lo < hi;
-                    meets |= ne && lo < j1 && hi > j0;
-                    covers &= ne && lo <= j0 && hi >= j1;
-                }
-            }
-            const bool any_meet = __ballot(meets) != 0;
-            const bool all_cover = __ballot(!covers) == 0;
-            const int kind = all_cover ? BWA_TILE_FULL : (any_meet ? BWA_TILE_PARTIAL : BWA_TILE_SKIP);
-            if (kind == BWA_TILE_SKIP) {
-                if (cur_kind) { emit(); cur_kind = 0; }
-            } else if (cur_kind == kind && cur_e == kb) {
-                cur_e = kb + 1;
+        int f0 = 0, f1 = 0;
+        if (mx_lo != 0x7fffffff && mn_hi >= 0) {
+            f0 = (mx_lo + a.bkv - 1) / a.bkv;
+            f1 = (mn_hi >= lk) ? nkb : mn_hi / a.bkv;
+        }
+        if (f0 < f1) {
+            partial_range(kb_lo, f0);
+            if (cur_kind == BWA_TILE_FULL && cur_e == f0) {  // cannot happen after a PARTIAL block; kept exact
+                cur_e = f1;
             } else {
                 if (cur_kind) emit();
-                cur_kind = kind; cur_b = kb; cur_e = kb + 1;
+                cur_kind = BWA_TILE_FULL; cur_b = f0; cur_e = f1;
             }
+            partial_range(f1, kb_hi);
+        } else {
+            partial_range(kb_lo, kb_hi);
         }
         if (cur_kind) emit();
     }

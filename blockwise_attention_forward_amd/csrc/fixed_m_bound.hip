@@ -15,6 +15,8 @@
 // IEEE bits, which orders non-negative floats exactly (order-independent,
 // so the result is deterministic).  Three launches: init, norms, finalize.
 
+#include <algorithm>
+
 #include "internal.h"
 
 namespace bwa {
@@ -32,7 +34,7 @@ __global__ __launch_bounds__(256) void init_kernel(const BoundLaunch a) {
     if (bh >= a.B * a.H) return;
     float km = 0.0f;
     if (a.kmax_in)
-        for (int c = 0; c < a.n_chunks; ++c) km = fmaxf(km, a.kmax_in[(i64)c * a.B * a.H + bh]);
+        for (int c = 0; c < a.n_kmax_in; ++c) km = fmaxf(km, a.kmax_in[(i64)c * a.B * a.H + bh]);
     a.kmax_out[bh] = km;
     a.mmax_out[bh] = 0.0f;  // holds max ||q_i|| until finalize
 }
@@ -141,8 +143,8 @@ hipError_t launch_fixed_m_bound(const BoundLaunch& a, hipStream_t stream) {
             else launch_norms<128, BWA_F32>(nt, tasks, stream);
         }
     }
-    hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((a.q.L + 1023) / 1024) > 0 ? (unsigned)((a.q.L + 1023) / 1024) : 1u, BH),
-                       dim3(256), 0, stream, a);
+    const unsigned fin_x = (unsigned)std::max<i64>(1, (a.q.L + 1023) / 1024);  // >= 1: the gate is always written
+    hipLaunchKernelGGL(finalize_kernel, dim3(fin_x, BH), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

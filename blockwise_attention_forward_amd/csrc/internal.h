@@ -117,6 +117,7 @@ struct BoundLaunch {
     int n_chunks;
     int B, H, D, dtype;
     const float* kmax_in;
+    int n_kmax_in;
     float scale, tau;
     float* kmax_out; float* mmax_out; float* m_out; uint8_t* gate_out;
 };

@@ -172,7 +172,8 @@ int32_t bwa_block_mask_size(const bwa_mask* mask, int64_t B, int64_t lq, int64_t
  * problem ([DKORDER]; the forward analogue of its partial/full block lists).
  * out->bq, bkv, lq, lk, batch, n_qblocks and capacity must hold the values
  * from bwa_block_mask_size (capacity may be larger) and its pointers the
- * caller's device buffers.  bq and bkv must be positive multiples of 64.
+ * caller's device buffers.  bq and bkv must be positive multiples of 64,
+ * bq at most 512.
  * Results are exact integers (bit-exact against any correct implementation).
  * Preconditions checked on the device only by construction: cu_seqlens and
  * segment ids non-decreasing; violating them gives unspecified (but
@@ -184,20 +185,21 @@ int32_t bwa_block_mask_build(const bwa_mask* mask, int64_t B, int64_t lq, int64_
 /*
  * Fixed-m bound and gate [FIXEDM description and Notes].
  *   kmax[b,h]  = max over chunks c and keys j < kv_valid[c] of ||k_c[b,j,h,:]||_2,
- *                folded with max over c of kmax_in[c][b][h] when kmax_in is not
- *                NULL (a caller's per-shard max||k|| promoted to the global bound);
+ *                folded with max over s of kmax_in[s][b][h], s < n_kmax_in
+ *                (per-shard max||k|| values of shards this call does not see,
+ *                e.g. other ring ranks', promoted to the global bound);
  *   m[b,h,i]   = scale * ||q[b,i,h,:]||_2 * kmax[b,h]   (natural-log units);
  *   mmax[b,h]  = max over i < q_valid of m[b,h,i]   (0 when q_valid == 0);
  *   gate[b,h]  = 1 if mmax[b,h] <= tau else 0   (a tie passes).
  * q: [B, Lq, H, D]; k_chunks: host array of n_chunks tensors [B, Lk_c, H, D]
  * with q's dtype, B, H and D; kv_valid: host array [n_chunks] (NULL = all
- * keys valid; entries < 0 mean Lk_c); kmax_in: device [n_chunks][B][H] or
- * NULL; q_valid < 0 means Lq.  Outputs are device arrays: kmax_out [B][H],
+ * keys valid; entries < 0 mean Lk_c); kmax_in: device [n_kmax_in][B][H]
+ * (NULL when n_kmax_in == 0); q_valid < 0 means Lq.  Outputs are device arrays: kmax_out [B][H],
  * mmax_out [B][H], m_out [B][H][Lq] (fp32), gate_out [B][H] (uint8).
  * Norms are fp32 sums of squares (bf16 products are exact in fp32).
  */
 int32_t bwa_fixed_m_bound(const bwa_tensor* q, const bwa_tensor* k_chunks, int32_t n_chunks,
-                          const float* kmax_in, const int64_t* kv_valid, int64_t q_valid,
+                          const float* kmax_in, int32_t n_kmax_in, const int64_t* kv_valid, int64_t q_valid,
                           float scale, float tau, float* kmax_out, float* mmax_out,
                           float* m_out, uint8_t* gate_out, void* stream);
 

@@ -30,9 +30,11 @@ def mask_for_batch(mask, b):
 
 
 def oracle_attention(q, k, v, mask, scale, rows=None, heads=None):
-    """Oracle O [B, R, H', D] and LSE [B, H', R] for tensors in [B, L, H, D]."""
-    qn, kn, vn = np64(q), np64(k), np64(v)
-    B, Lq, H, D = qn.shape
+    """Oracle O [B, R, H', D] and LSE [B, H', R] for tensors in [B, L, H, D].
+
+    Converts one (batch, head) at a time to fp64, so long sequences fit.
+    """
+    B, Lq, H, D = q.shape
     heads = list(range(H)) if heads is None else list(heads)
     rows = np.arange(Lq) if rows is None else np.asarray(rows)
     O = np.zeros((B, len(rows), len(heads), D))
@@ -40,10 +42,22 @@ def oracle_attention(q, k, v, mask, scale, rows=None, heads=None):
     for b in range(B):
         m = mask_for_batch(mask, b)
         for n, h in enumerate(heads):
-            o, l = oracle.attention_rows(qn[b, :, h], kn[b, :, h], vn[b, :, h], m, scale, rows)
+            o, l = oracle.attention_rows(np64(q[b, :, h]), np64(k[b, :, h]), np64(v[b, :, h]), m, scale, rows)
             O[b, :, n] = o
             L[b, n] = l
     return O, L
+
+
+def gpu_rows(o, lse, rows, heads=None):
+    """Sampled rows of GPU outputs as fp64: O [B, R, H', D], LSE [B, H', R]."""
+    idx = torch.as_tensor(np.asarray(rows), device=o.device, dtype=torch.long)
+    os_ = o.index_select(1, idx)
+    ls = lse.index_select(2, idx)
+    if heads is not None:
+        hidx = torch.as_tensor(list(heads), device=o.device, dtype=torch.long)
+        os_ = os_.index_select(2, hidx)
+        ls = ls.index_select(1, hidx)
+    return np64(os_), np64(ls)
 
 
 def assert_close(o_gpu, lse_gpu, o_ref, lse_ref, in_dtype, what=""):

@@ -156,10 +156,13 @@ def test_merge_and_bound_errors():
     assert L.bwa_lse_merge(1, bad, lps, ctypes.byref(out), None, None) == 4
     q = _t()
     ks = (bw._Tensor * 1)(_t(H=3))
-    assert L.bwa_fixed_m_bound(ctypes.byref(q), ks, 1, None, None, -1, 0.1, 106.5, 0x1000, 0x1000,
+    assert L.bwa_fixed_m_bound(ctypes.byref(q), ks, 1, None, 0, None, -1, 0.1, 106.5, 0x1000, 0x1000,
                                0x1000, 0x1000, None) == 2
-    assert L.bwa_fixed_m_bound(ctypes.byref(q), ks, 17, None, None, -1, 0.1, 106.5, 0x1000, 0x1000,
+    assert L.bwa_fixed_m_bound(ctypes.byref(q), ks, 17, None, 0, None, -1, 0.1, 106.5, 0x1000, 0x1000,
                                0x1000, 0x1000, None) == 2
+    ok1 = (bw._Tensor * 1)(_t())
+    assert L.bwa_fixed_m_bound(ctypes.byref(q), ok1, 1, None, 2, None, -1, 0.1, 106.5, 0x1000, 0x1000,
+                               0x1000, 0x1000, None) == 1
 
 
 def test_attn_tile():

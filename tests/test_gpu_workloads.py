@@ -1,0 +1,264 @@
+"""GPU parity at the full workload sizes, against the fp64 oracle.
+
+Workloads (synthetic stand-ins for the pages' models and data, see synth):
+  * tiny     B=1 H=2 L=256 D=64 fp32, dense, and split in 2 KV chunks + LSE merge
+  * varlen   H3 packed request, cu_seqlens [0, 33002, 33024], 24 heads
+  * window   causal bands W in {512, 1024, 2048} on 4096^2, 4096x8192, 8192^2
+  * dit      one rank's share of ring2 x uly2 video-DiT attention (2 KV hops,
+             fixed-m with a sink head on online fallback, LSE merge)
+  * long     1,048,576-token causal attention, single segment and packed
+
+Large outputs are checked on a seeded sample of 512 query rows per head
+(always holding the first and last valid rows, segment-boundary rows and an
+invalid row where one exists); integer outputs (run lists, row intervals,
+gates, zero rows) are checked exactly.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import assert_close, gpu_rows, np64, oracle_attention
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import blockwise_attention_forward_amd as bw  # noqa: E402
+
+DEV = "cuda"
+BF16 = torch.bfloat16
+
+
+def _lists_match_oracle(bl, mask, Lq, Lk, bq, bkv, qblocks=None):
+    """GPU run lists and row intervals equal the oracle's (interval method)."""
+    lo, hi = oracle.row_intervals(Lq, Lk, mask)
+    assert np.array_equal(bl.row_lo[:Lq].cpu().numpy(), lo)
+    assert np.array_equal(bl.row_hi[:Lq].cpu().numpy(), hi)
+    rp, b, e, k = bl.host()
+    nqb = (Lq + bq - 1) // bq
+    qblocks = np.arange(nqb) if qblocks is None else np.asarray(qblocks)
+    kinds = oracle.block_kinds_intervals(lo, hi, Lq, Lk, bq, bkv, qblocks=qblocks)
+    for n, qb in enumerate(qblocks):
+        got = (b[rp[qb]:rp[qb + 1]], e[rp[qb]:rp[qb + 1]], k[rp[qb]:rp[qb + 1]])
+        w = oracle.runs_from_kinds(kinds[n:n + 1])
+        assert np.array_equal(got[0], w[1]) and np.array_equal(got[1], w[2]) and np.array_equal(got[2], w[3]), qb
+    return kinds
+
+
+def _gpu_tile_counts(bl, Lq, Lk, bq, bkv):
+    rp, b, e, k = bl.host()
+    n_tiles = int((e - b).astype(np.int64).sum())
+    n_partial = int(((e - b) * (k == bw.BWA_TILE_PARTIAL)).astype(np.int64).sum())
+    return n_tiles, n_partial
+
+
+# ------------------------------------------------------------------- tiny
+def test_tiny_dense_and_two_chunk_merge():
+    t = synth.make_tiny(DEV)
+    q, k, v, scale = t["q"], t["k"], t["v"], t["scale"]
+    o_ref, l_ref = oracle_attention(q, k, v, {}, scale)
+    o, l = bw.bwa_attn_fwd(q, k, v, {}, scale=scale)
+    assert_close(o, l, o_ref, l_ref, torch.float32, "tiny")
+    parts = [bw.bwa_attn_fwd(q, k[:, a:e], v[:, a:e], {"kv_offset": a}, scale=scale) for a, e in t["chunks"]]
+    om, lm = bw.bwa_lse_merge([p[0] for p in parts], [p[1] for p in parts], out_dtype=torch.float32)
+    assert_close(om, lm, o_ref, l_ref, torch.float32, "tiny merged")
+
+
+# ------------------------------------------------------------------- varlen
+def test_varlen_packed_request():
+    w = synth.make_varlen(DEV)
+    q, k, v, mask, scale = w["q"], w["k"], w["v"], w["mask"], w["scale"]
+    L = q.shape[1]
+    bl128 = bw.bwa_block_mask_build(mask, 1, L, L, 128, 128)
+    kinds = _lists_match_oracle(bl128, mask, L, L, 128, 128)
+    assert (kinds != oracle.SKIP).sum() == 66564 and (kinds == oracle.PARTIAL).sum() == 515
+    bq, _ = bw.bwa_attn_tile(BF16, 128)
+    blocks = bw.bwa_block_mask_build(mask, 1, L, L, bq, 128)
+    _lists_match_oracle(blocks, mask, L, L, bq, 128)
+    o, l = bw.bwa_attn_fwd(q, k, v, mask, blocks=blocks, scale=scale)
+    o2, l2 = bw.bwa_attn_fwd(q, k, v, mask, scale=scale)
+    assert torch.equal(o, o2) and torch.equal(l, l2)
+    # the 22 alignment rows are written as zeros with LSE -inf, in every head
+    assert torch.all(o[:, 33002:] == 0) and torch.all(torch.isneginf(l[:, :, 33002:]))
+    rows = synth.sample_rows(L, 512, seed=21, must=[0, 127, 128, 255, 256, 32895, 32896, 33001, 33002, 33023])
+    o_ref, l_ref = oracle_attention(q, k, v, mask, scale, rows)
+    assert_close(*gpu_rows(o, l, rows), o_ref, l_ref, BF16, "varlen")
+
+
+# ------------------------------------------------------------------- window
+WINDOW_COUNTS = {(4096, 4096): (150, 252, 408), (4096, 8192): (160, 288, 544), (8192, 8192): (310, 540, 952)}
+
+
+@pytest.mark.parametrize("W", [512, 1024, 2048])
+@pytest.mark.parametrize("Lq,Lk", [(4096, 4096), (4096, 8192), (8192, 8192)])
+def test_sliding_window(Lq, Lk, W):
+    w = synth.make_window(Lq, Lk, W, DEV)
+    q, k, v, mask, scale = w["q"], w["k"], w["v"], w["mask"], w["scale"]
+    bl128 = bw.bwa_block_mask_build(mask, 1, Lq, Lk, 128, 128)
+    want = oracle.block_lists(mask, Lq, Lk, 128, 128)  # element predicate, brute force
+    got = bl128.host()
+    for g, x in zip(got, want):
+        assert np.array_equal(g, x)
+    n_tiles, _ = _gpu_tile_counts(bl128, Lq, Lk, 128, 128)
+    assert n_tiles == WINDOW_COUNTS[(Lq, Lk)][(512, 1024, 2048).index(W)]
+    bq, _ = bw.bwa_attn_tile(BF16, 128)
+    blocks = bw.bwa_block_mask_build(mask, 1, Lq, Lk, bq, 128)
+    _lists_match_oracle(blocks, mask, Lq, Lk, bq, 128)
+    o, l = bw.bwa_attn_fwd(q, k, v, mask, blocks=blocks, scale=scale)
+    rows = synth.sample_rows(Lq, 512, seed=22, must=[0, 1, W - 1, W, Lq - 1])
+    o_ref, l_ref = oracle_attention(q, k, v, mask, scale, rows)
+    assert_close(*gpu_rows(o, l, rows), o_ref, l_ref, BF16, f"window {Lq}x{Lk} W={W}")
+
+
+# ------------------------------------------------------------------- dit share
+@pytest.fixture(scope="module")
+def dit():
+    return synth.make_dit_share(DEV)
+
+
+def _hops(d, mode, m=None, gate=None):
+    q = d["q"]
+    B, Lq, H, D = q.shape
+    bq, _ = bw.bwa_attn_tile(BF16, D)
+    parts = []
+    for k, v, off in zip(d["k_chunks"], d["v_chunks"], d["kv_offsets"]):
+        mask = {"kv_offset": off}
+        blocks = bw.bwa_block_mask_build(mask, B, Lq, k.shape[1], bq, 128)
+        parts.append(bw.bwa_attn_fwd(q, k, v, mask, blocks=blocks, scale=d["scale"], mode=mode, m=m, gate=gate,
+                                     out_dtype=torch.float32))
+    return bw.bwa_lse_merge([p[0] for p in parts], [p[1] for p in parts], out_dtype=BF16)
+
+
+def _dit_oracle(d, rows):
+    k = torch.cat(d["k_chunks"], dim=1)
+    v = torch.cat(d["v_chunks"], dim=1)
+    return oracle_attention(d["q"], k, v, {}, d["scale"], rows)
+
+
+def test_dit_bound_gate_and_promotion(dit):
+    q, ks, scale = dit["q"], dit["k_chunks"], dit["scale"]
+    H = q.shape[2]
+    kmax, mmax, m, gate = bw.bwa_fixed_m_bound(q, ks, scale, 106.5)
+    g = gate[0].cpu().numpy()
+    assert g[dit["sink_head"]] == 0 and g.sum() == H - 1
+    for h in range(H):
+        km, mr, mm, gh = oracle.fixed_m_bound(np64(q[0, :, h]), [np64(c[0, :, h]) for c in ks], scale, 106.5)
+        np.testing.assert_allclose(kmax[0, h].item(), km, rtol=1e-6)
+        np.testing.assert_allclose(np64(m[0, h]), mr, rtol=2e-6)
+        np.testing.assert_allclose(mmax[0, h].item(), mm, rtol=2e-6)
+        assert bool(g[h]) == gh
+    # a caller's per-shard max||k|| promoted to the global bound: the bound
+    # over chunk 0 alone with both shards' maxima equals the two-chunk bound
+    per = torch.stack([bw.bwa_fixed_m_bound(q, [c], scale, 106.5)[0] for c in ks])
+    k2, mm2, m2, g2 = bw.bwa_fixed_m_bound(q, [ks[0]], scale, 106.5, kmax_in=per)
+    assert torch.equal(k2, kmax) and torch.equal(m2, m) and torch.equal(g2, gate) and torch.equal(mm2, mmax)
+
+
+def test_dit_gated_and_online_hops(dit):
+    q = dit["q"]
+    Lq = q.shape[1]
+    kmax, mmax, m, gate = bw.bwa_fixed_m_bound(q, dit["k_chunks"], dit["scale"], 106.5)
+    o_g, l_g = _hops(dit, bw.BWA_MODE_GATED, m=m, gate=gate)
+    o_o, l_o = _hops(dit, bw.BWA_MODE_ONLINE)
+    rows = synth.sample_rows(Lq, 512, seed=23, must=[0, 1, 127, 128, Lq - 41, Lq - 1])
+    o_ref, l_ref = _dit_oracle(dit, rows)
+    assert_close(*gpu_rows(o_g, l_g, rows), o_ref, l_ref, BF16, "dit gated")
+    assert_close(*gpu_rows(o_o, l_o, rows), o_ref, l_ref, BF16, "dit online")
+
+
+def test_dit_all_heads_eligible():
+    d = synth.make_dit_share(DEV, seed=1013, sink=False)
+    q = d["q"]
+    kmax, mmax, m, gate = bw.bwa_fixed_m_bound(q, d["k_chunks"], d["scale"], 106.5)
+    assert torch.all(gate == 1)
+    o, l = _hops(d, bw.BWA_MODE_FIXED_M, m=m)  # branch-free fixed-m body for every head
+    rows = synth.sample_rows(q.shape[1], 512, seed=24, must=[0, q.shape[1] - 1])
+    o_ref, l_ref = _dit_oracle(d, rows)
+    assert_close(*gpu_rows(o, l, rows), o_ref, l_ref, BF16, "dit all eligible")
+
+
+def test_dit_ragged_padded_last_shard(dit):
+    # padding only at the end of the global sequence: the last shard's tail
+    q, ks, vs = dit["q"], dit["k_chunks"], dit["v_chunks"]
+    Lc = ks[1].shape[1]
+    n_valid = Lc - 1000
+    kmax, mmax, m, gate = bw.bwa_fixed_m_bound(q, ks, dit["scale"], 106.5, kv_valid=[Lc, n_valid])
+    parts = []
+    for t, (k, v) in enumerate(zip(ks, vs)):
+        mask = {"kv_offset": t * Lc, "kv_valid": Lc if t == 0 else n_valid}
+        parts.append(bw.bwa_attn_fwd(q, k, v, mask, scale=dit["scale"], mode=bw.BWA_MODE_GATED, m=m, gate=gate,
+                                     out_dtype=torch.float32))
+    o, l = bw.bwa_lse_merge([p[0] for p in parts], [p[1] for p in parts])
+    rows = synth.sample_rows(q.shape[1], 128, seed=25, must=[0, q.shape[1] - 1])
+    k_all = torch.cat([ks[0], ks[1][:, :n_valid]], dim=1)
+    v_all = torch.cat([vs[0], vs[1][:, :n_valid]], dim=1)
+    o_ref, l_ref = oracle_attention(q, k_all, v_all, {}, dit["scale"], rows)
+    assert_close(*gpu_rows(o, l, rows), o_ref, l_ref, BF16, "dit padded shard")
+
+
+# ------------------------------------------------------------------- 1M tokens
+@pytest.fixture(scope="module")
+def long():
+    return synth.make_long_causal(DEV)
+
+
+@pytest.mark.timeout(900)
+def test_long_causal_single_segment(long):
+    q, k, v, scale = long["q"], long["k"], long["v"], long["scale"]
+    L = q.shape[1]
+    bq, _ = bw.bwa_attn_tile(BF16, 128)
+    plain = {"causal": True}
+    seg1 = {"causal": True, "cu_seqlens_q": [0, L], "cu_seqlens_kv": [0, L]}
+    b0 = bw.bwa_block_mask_build(plain, 1, L, L, bq, 128)
+    b1 = bw.bwa_block_mask_build(seg1, 1, L, L, bq, 128)
+    for x, y in zip(b0.host(), b1.host()):
+        assert np.array_equal(x, y)
+    o0, l0 = bw.bwa_attn_fwd(q, k, v, plain, blocks=b0, scale=scale)
+    o1, l1 = bw.bwa_attn_fwd(q, k, v, seg1, blocks=b1, scale=scale)
+    torch.cuda.synchronize()
+    # one segment through the segmented path gives the unsegmented bits
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    bl128 = bw.bwa_block_mask_build(plain, 1, L, L, 128, 128)
+    n_tiles, n_partial = _gpu_tile_counts(bl128, L, L, 128, 128)
+    assert n_tiles == 8192 * 8193 // 2 and n_partial == 8192
+    qbs = np.unique(np.concatenate([[0, 1, 8191], np.random.default_rng(3).choice(8192, 61, replace=False)]))
+    _lists_match_oracle(bl128, plain, L, L, 128, 128, qblocks=qbs)
+    rows = synth.sample_rows(L, 512, seed=26, must=[0, 1, 255, 256, L - 1])
+    o_ref, l_ref = oracle_attention(q, k, v, plain, scale, rows)
+    assert_close(*gpu_rows(o0, l0, rows), o_ref, l_ref, BF16, "1M causal")
+
+
+@pytest.mark.timeout(900)
+def test_long_causal_packed(long):
+    q, k, v, scale = long["q"], long["k"], long["v"], long["scale"]
+    L, H = q.shape[1], q.shape[2]
+    cu = synth.long_causal_segments(L)
+    mask = {"causal": True, "cu_seqlens_q": cu, "cu_seqlens_kv": cu}
+    bq, _ = bw.bwa_attn_tile(BF16, 128)
+    blocks = bw.bwa_block_mask_build(mask, 1, L, L, bq, 128)
+    o, l = bw.bwa_attn_fwd(q, k, v, mask, blocks=blocks, scale=scale)
+    bl128 = bw.bwa_block_mask_build(mask, 1, L, L, 128, 128)
+    qbs = np.unique(np.concatenate([[0, 8191], [c // 128 for c in cu[1:-1]],
+                                    np.random.default_rng(4).choice(8192, 48, replace=False)]))
+    _lists_match_oracle(bl128, mask, L, L, 128, 128, qblocks=qbs)
+    must = [0, L - 1] + [c for c in cu[1:-1]] + [c - 1 for c in cu[1:-1]]
+    rows = synth.sample_rows(L, 512, seed=27, must=must)
+    # The oracle runs each sampled row inside its own segment (keys of other
+    # segments are invisible by the definition): same rule, fewer keys.
+    seg = np.searchsorted(np.asarray(cu), rows, side="right") - 1
+    got_o, got_l = gpu_rows(o, l, rows)
+    ref_o = np.zeros_like(got_o)
+    ref_l = np.zeros_like(got_l)
+    for s in np.unique(seg):
+        a, e = cu[s], cu[s + 1]
+        sel = np.nonzero(seg == s)[0]
+        oo, ll = oracle_attention(q[:, a:e], k[:, a:e], v[:, a:e], {"causal": True}, scale, rows[sel] - a)
+        ref_o[:, sel] = oo
+        ref_l[:, :, sel] = ll
+    assert_close(got_o, got_l, ref_o, ref_l, BF16, "1M packed")

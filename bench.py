@@ -200,6 +200,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dit_share", choices=["dit_share"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run 3 plain device copies of MIB MiB (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share only (one MI355X); multi-GPU runs are not part of "
@@ -211,6 +213,14 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     W = setup_dit_share(torch, bw, synth)
     timer = Timer(torch)
     for _ in range(args.warmup):

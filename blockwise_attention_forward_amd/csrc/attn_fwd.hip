@@ -52,6 +52,12 @@ constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 
 
 enum { BODY_ONLINE = 0, BODY_FIXED = 1, MODE_GATED = 2 };
 
+// Waves per workgroup of the bf16 kernel (32 query rows each).
+#ifndef BWA_BF16_WAVES
+#define BWA_BF16_WAVES 8
+#endif
+constexpr int kBf16Waves = BWA_BF16_WAVES;
+
 __device__ inline i64 xcd_remap(i64 id, i64 n) {
     // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
     // contiguous range of logical work so that the query blocks of one head
@@ -145,9 +151,11 @@ __device__ inline void block_reduce4(int& mn_lo, int& mx_hi, int& mx_lo, int& mn
     mn_lo = uni(mn_lo); mx_hi = uni(mx_hi); mx_lo = uni(mx_lo); mn_hi = uni(mn_hi);
 }
 
-// Walk of query block qb (BQ rows).  lo/hi: this lane's row interval.
+// Walk of query block qb.  The lane-level bounds over the lane's rows:
+// mn_lo/mx_hi over rows that see something, mx_lo/mn_hi over existing rows
+// (0x7fffffff / -1 when such a row sees nothing, which rules out FULL tiles).
 template <int TILE, int NT>
-__device__ inline Walk make_walk(const AttnLaunch& p, i64 b, i64 qb, int lo, int hi, bool row_exists,
+__device__ inline Walk make_walk(const AttnLaunch& p, i64 b, i64 qb, int mn_lo, int mx_hi, int mx_lo, int mn_hi,
                                  int* red) {
     Walk w;
     w.Lk = (int)p.Lk;
@@ -169,10 +177,6 @@ __device__ inline Walk make_walk(const AttnLaunch& p, i64 b, i64 qb, int lo, int
     // [min lo, max hi) and the tiles inside [max lo, min hi) are full.
     // Visiting a tile with no visible pair is harmless (it is masked), so
     // the walk is correct for any interval mask.
-    const bool ne = row_exists && lo < hi;
-    int mn_lo = ne ? lo : 0x7fffffff, mx_hi = ne ? hi : 0;
-    int mx_lo = row_exists ? (ne ? lo : 0x7fffffff) : 0;
-    int mn_hi = row_exists ? (ne ? hi : -1) : 0x7fffffff;
     block_reduce4<NT>(mn_lo, mx_hi, mx_lo, mn_hi, red);
     w.nruns = 3;
     if (mx_hi == 0) { w.nruns = 0; return w; }  // no row of this block sees anything
@@ -286,22 +290,42 @@ __device__ inline void store_out(const AttnLaunch& p, f32x16 (&acc)[D / 32], flo
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel: NW waves (BQ = 32*NW rows), 64-key tiles, 32x32x16 bf16 MFMA.
+// bf16 kernel: NW waves of 32 query rows (BQ = 32*NW rows per workgroup),
+// 64-key tiles, 32x32x16 bf16 MFMA.
+//
+// K and V tiles go from HBM straight into LDS (buffer loads with an LDS
+// destination: lane i of an instruction fills bytes [16i, 16i+16) of a 1 KB
+// run, and lanes past the buffer's range write zeros).  Each lane picks the
+// global 16-byte chunk that belongs at its LDS slot, so the tiles land
+// already swizzled and no register staging, transpose or LDS store remains.
+//   K tile: row r (key), D/8 chunks, swizzled by k_swz.  The Q K^T operand
+//           read (lane: row kb*32 + l%32, chunk ds*2 + l/32) hits distinct
+//           chunks of each 256-byte bank window.
+//   V tile: row r (key), D/8 chunks, swizzled by v_swz.
+//           The P V operand needs V^T (8 keys of one d per lane); it is read
+//           with two transposing 64-bit LDS reads: in each group of 16 lanes,
+//           lane i receives element i%4 of the 4-element rows addressed by
+//           lanes i/4 + 4s (s = 0..3).  Lane 16g + 4s + u therefore points at
+//           V[key0 + s][dbase + 16*(g&1) + 4u], and lane l receives
+//           V[key0 + 0..3][dbase + l%32]; the XOR puts the 4 rows each
+//           half-wave touches in disjoint banks.
 // ---------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <int D, int NW>
 struct Bf16Cfg {
     static constexpr int TILE = 64;
     static constexpr int NT = NW * 64;
     static constexpr int BQ = NW * 32;
-    static constexpr int NCH = D / 8;               // 16-byte chunks per K row
-    static constexpr int NDB = D / 32;              // 32-wide d blocks of O^T
-    static constexpr int NDS = D / 16;              // 16-deep steps of Q K^T
-    static constexpr int KCH = TILE * NCH;          // K chunks per tile
-    static constexpr int KL = (KCH + NT - 1) / NT;  // K chunks per thread
-    static constexpr int VK = (TILE * NCH) / NT >= 4 ? 4 : 2;  // keys per V task
-    static constexpr int VT = (TILE / VK) * NCH;    // V tasks per tile
-    static constexpr int VL = (VT + NT - 1) / NT;   // V tasks per thread
-    static constexpr int TILE_BYTES = TILE * D * 2;
+    static constexpr int NCH = D / 8;                 // 16-byte chunks per row
+    static constexpr int NDB = D / 32;                // 32-wide d blocks of O^T
+    static constexpr int NDS = D / 16;                // 16-deep steps of Q K^T
+    static constexpr int TILE_BYTES = TILE * D * 2;   // one K or V tile
+    static constexpr int RUNS = TILE_BYTES / 1024;    // 1 KB load runs per tile
+    static constexpr int RUNS_PER_WAVE = (RUNS + NW - 1) / NW;
+    static constexpr int NBUF = NW == 8 ? 3 : 2;      // K/V tile buffers in the copy ring
 };
 
 template <int D, int NW>
@@ -311,16 +335,24 @@ struct Bf16State {
     f32x16 acc[C::NDB];
     float m_run, l_run, m_fixed, m_l2, scale_l2;
     int lo, hi;
-    uint4 sk[C::KL];
-    uint4 sv[C::VL][C::VK];
 };
 
+// Swizzles of the 16-byte chunk index c of row r.  A 256-byte bank window
+// holds one row of D = 128 or two rows of D = 64; the XOR spreads the rows a
+// matrix-core operand read touches over distinct chunks of the window.
+template <int D> __device__ inline int k_swz(int r, int c) {
+    return D == 128 ? c ^ (r & 15) : c ^ ((r >> 1) & 7);
+}
+template <int D> __device__ inline int v_swz(int r, int c) {
+    return D == 128 ? c ^ ((r & 3) << 2) : c ^ (((r >> 1) & 1) << 2);
+}
+
+// Issue the HBM -> LDS copies of one K and one V tile (rows past kv_lim read as zero).
 template <int D, int NW>
-__device__ inline void bf16_load_tile(const AttnLaunch& p, Bf16State<D, NW>& st, const __bf16* kbase,
-                                      const __bf16* vbase, int j0, int kv_lim) {
+__device__ inline void bf16_issue_tile(const AttnLaunch& p, const __bf16* kbase, const __bf16* vbase, int j0,
+                                       int kv_lim, uint8_t* kl, uint8_t* vl) {
     using C = Bf16Cfg<D, NW>;
-    const int tid = threadIdx.x;
-    // Range of the buffer resources: the tile's rows below kv_lim (wave-uniform).
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nvalid = uni(min(max(kv_lim - j0, 0), C::TILE));
     const int kbytes = uni((int)(nvalid * p.k_sL * 2)), vbytes = uni((int)(nvalid * p.v_sL * 2));
     const __amdgpu_buffer_rsrc_t kr =
@@ -328,151 +360,267 @@ __device__ inline void bf16_load_tile(const AttnLaunch& p, Bf16State<D, NW>& st,
     const __amdgpu_buffer_rsrc_t vr =
         __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (i64)j0 * p.v_sL), 0, vbytes, kRsrcFlags);
 #pragma unroll
-    for (int it = 0; it < C::KL; ++it) {
-        const int lin = it * C::NT + tid, r = lin / C::NCH, c = lin % C::NCH;
-        if (C::KCH % C::NT == 0 || lin < C::KCH)
-            st.sk[it] = __builtin_bit_cast(
-                uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, (int)(r * p.k_sL * 2 + c * 16), 0, 0));
-    }
-#pragma unroll
-    for (int it = 0; it < C::VL; ++it) {
-        const int task = it * C::NT + tid, g = task / C::NCH, cd = task % C::NCH;
-        if (C::VT % C::NT == 0 || task < C::VT) {
-#pragma unroll
-            for (int e = 0; e < C::VK; ++e)
-                st.sv[it][e] = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                               vr, (int)((g * C::VK + e) * p.v_sL * 2 + cd * 16), 0, 0));
+    for (int it = 0; it < C::RUNS_PER_WAVE; ++it) {
+        const int run = wave * C::RUNS_PER_WAVE + it;
+        if (C::RUNS % NW == 0 || run < C::RUNS) {
+            const int slot = run * 64 + lane;  // 16-byte slot in the tile
+            const int r = slot / C::NCH, pc = slot % C::NCH;
+            const int kc = k_swz<D>(r, pc), vc = v_swz<D>(r, pc);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kl + run * 1024), 16,
+                                                     (unsigned)(r * p.k_sL * 2 + kc * 16), 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vl + run * 1024), 16,
+                                                     (unsigned)(r * p.v_sL * 2 + vc * 16), 0, 0, 0);
         }
     }
 }
 
-// V^T tile layout: row d (D rows of TILE keys, 128 bytes), 8 chunks of 16
-// bytes.  Chunk kk*2 + hb holds keys kk*16 + {hb*4 + 0..3, 8 + hb*4 + 0..3},
-// the 8 keys the matrix-core operand of lane half hb needs for k-step kk;
-// the chunk index is XOR-swizzled with (d ^ d>>3) & 7.
-__device__ inline int vt_offset(int d, int key) {
-    const int kk = key >> 4, kin = key & 15;
-    const int hb = (kin >> 2) & 1, half = kin >> 3, pos = kin & 3;
-    const int chunk = kk * 2 + hb;
-    return d * 128 + ((chunk ^ ((d ^ (d >> 3)) & 7)) * 16) + half * 8 + pos * 2;
+// Fragment reads run kPrefetch matrix-core steps ahead of their use.
+constexpr int kPrefetch = 4;
+// Online softmax keeps its reference max until a row's max grows by more
+// than 2^kLazy (base-2 units); probabilities then stay below 2^kLazy, and the
+// rescale of O and l is skipped for most tiles.  The result is the same in
+// real arithmetic for any reference point.
+constexpr float kLazy = 8.0f;
+
+// Softmax of one 32-key half (16 values per lane) in four slices of four
+// values, so that the slices can be interleaved with matrix-core work.
+struct Half {
+    f32x16 s;   // scores, then probabilities
+    float rs;   // running row sum of this half (per lane)
+    uint4 pb[2];  // bf16 probabilities: keys 0..15 and 16..31 of the half
+};
+
+__device__ inline void half_mask(Half& x, int j0, int kb, int lo, int hi) {
+    const int hb = (threadIdx.x >> 5) & 1;
+    const int lo_rel = lo - (j0 + kb * 32 + hb * 4);
+    const unsigned span = (unsigned)max(hi - lo, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        x.s[r] = ((unsigned)(off - lo_rel) < span) ? x.s[r] : kNegInf;
+    }
 }
 
-template <int D, int NW>
-__device__ inline void bf16_store_tile(uint8_t* kl, uint8_t* vl, const Bf16State<D, NW>& st) {
-    using C = Bf16Cfg<D, NW>;
-    const int tid = threadIdx.x;
+// exp of slice q (values 4q..4q+3) and its packing; ms = reference * scale_l2.
+__device__ inline void half_exp_slice(Half& x, int q, float scale_l2, float ms) {
 #pragma unroll
-    for (int it = 0; it < C::KL; ++it) {
-        const int lin = it * C::NT + tid, r = lin / C::NCH, c = lin % C::NCH;
-        if (C::KCH % C::NT == 0 || lin < C::KCH)
-            *(uint4*)(kl + r * (D * 2) + ((c ^ (r & (C::NCH - 1))) * 16)) = st.sk[it];
+    for (int r = 4 * q; r < 4 * q + 4; ++r) {
+        const float e = fast_exp2(__builtin_fmaf(x.s[r], scale_l2, -ms));
+        x.s[r] = e;
+        x.rs += e;
     }
+    const uint32_t a = pack_bf16x2(x.s[4 * q], x.s[4 * q + 1]);
+    const uint32_t b = pack_bf16x2(x.s[4 * q + 2], x.s[4 * q + 3]);
+    uint4& pb = x.pb[q >> 1];
+    if (q & 1) { pb.z = a; pb.w = b; } else { pb.x = a; pb.y = b; }
+}
+
+// Online reference update for one half: returns the factor acc and l must be
+// scaled by (1 when the reference stays), or sets rescale = false.
+__device__ inline float half_online_ref(const Half& x, float& m_run, float scale_l2, bool& rescale) {
+    float mx = kNegInf;
 #pragma unroll
-    for (int it = 0; it < C::VL; ++it) {
-        const int task = it * C::NT + tid, g = task / C::NCH, cd = task % C::NCH;
-        if (C::VT % C::NT == 0 || task < C::VT) {
-            const int key0 = g * C::VK;
-#pragma unroll
-            for (int wi = 0; wi < 4; ++wi)
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const int d = cd * 8 + wi * 2 + s;
-                    uint32_t w[C::VK];
-#pragma unroll
-                    for (int e = 0; e < C::VK; ++e) {
-                        const uint32_t x = ((const uint32_t*)&st.sv[it][e])[wi];
-                        w[e] = s ? (x >> 16) : (x & 0xffffu);
-                    }
-                    if (C::VK == 4) {
-                        uint2 val = {w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
-                        *(uint2*)(vl + vt_offset(d, key0)) = val;
-                    } else {
-                        *(uint32_t*)(vl + vt_offset(d, key0)) = w[0] | (w[1] << 16);
-                    }
-                }
-        }
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x.s[r]);
+    mx = pair_max(mx);
+    const bool need = mx * scale_l2 > (m_run == kNegInf ? kNegInf : m_run * scale_l2 + kLazy);
+    rescale = __builtin_amdgcn_ballot_w64(need) != 0;
+    float alpha = 1.0f;
+    if (rescale) {
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+        alpha = fast_exp2((m_run - m_use) * scale_l2);
+        m_run = m_new;
     }
+    return alpha;
 }
 
 template <int D, int NW, int BODY>
-__device__ inline void bf16_compute_tile(const uint8_t* kl, const uint8_t* vl, Bf16State<D, NW>& st,
-                                         int j0, bool masked) {
+__device__ inline void bf16_compute_tile(const uint8_t* kl, const uint8_t* vl, Bf16State<D, NW>& st, int j0,
+                                         bool masked) {
     using C = Bf16Cfg<D, NW>;
+    constexpr int NDS = C::NDS, NDB = C::NDB;
     const int lane = threadIdx.x & 63, l32 = lane & 31, hb = lane >> 5;
-    f32x16 s[2] = {f32x16{}, f32x16{}};
-    // K fragments: row kb*32 + l32, chunk ds*2 + hb (swizzled); prefetched one step ahead.
-    const int kr0 = l32, kr1 = 32 + l32;
-    auto kfrag = [&](int r, int ds) {
-        const int c = ds * 2 + hb;
-        return *(const uint4*)(kl + r * (D * 2) + ((c ^ (r & (C::NCH - 1))) * 16));
+    // K fragment of step i = kb*NDS + ds: row kb*32 + l32, chunk ds*2 + hb.
+    auto kfrag = [&](int i) {
+        const int kb = i / NDS, ds = i % NDS, r = kb * 32 + l32;
+        return *(const uint4*)(kl + r * (D * 2) + k_swz<D>(r, ds * 2 + hb) * 16);
     };
-    uint4 a0 = kfrag(kr0, 0), a1 = kfrag(kr1, 0);
-#pragma unroll
-    for (int ds = 0; ds < C::NDS; ++ds) {
-        uint4 n0 = a0, n1 = a1;
-        if (ds + 1 < C::NDS) { n0 = kfrag(kr0, ds + 1); n1 = kfrag(kr1, ds + 1); }
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0),
-                                                       __builtin_bit_cast(bf16x8, st.qf[ds]), s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1),
-                                                       __builtin_bit_cast(bf16x8, st.qf[ds]), s[1], 0, 0, 0);
-        a0 = n0; a1 = n1;
-    }
-    auto vfrag = [&](int db, int kk) {
-        const int d = db * 32 + l32, c = kk * 2 + hb;
-        return *(const uint4*)(vl + d * (C::TILE * 2) + ((c ^ ((d ^ (d >> 3)) & 7)) * 16));
+    // V^T fragment of step j = kk*NDB + db: keys kk*16 + {hb*4 + 0..3} then
+    // kk*16 + 8 + {hb*4 + 0..3}, for d = db*32 + l32.
+    const int g1 = (lane >> 4) & 1, s_row = (lane >> 2) & 3, u = lane & 3;
+    auto vfrag = [&](int j) {
+        const int kk = j / NDB, db = j % NDB;
+        const int c = db * 4 + g1 * 2 + (u >> 1);  // 16-byte chunk of d = db*32 + 16*g1 + 4u
+        const int r0 = kk * 16 + hb * 4 + s_row, r1 = r0 + 8;
+        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(vl + r0 * (D * 2) + v_swz<D>(r0, c) * 16 + (u & 1) * 8));
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(vl + r1 * (D * 2) + v_swz<D>(r1, c) * 16 + (u & 1) * 8));
+        uint4 out;
+        out.x = __builtin_bit_cast(uint2, x0).x;
+        out.y = __builtin_bit_cast(uint2, x0).y;
+        out.z = __builtin_bit_cast(uint2, x1).x;
+        out.w = __builtin_bit_cast(uint2, x1).y;
+        return out;
     };
-    uint4 vf = vfrag(0, 0);
-    if (masked) apply_mask<2>(s, j0, st.lo, st.hi);
-    if (BODY == BODY_FIXED) fixed_update<2>(s, st.l_run, st.scale_l2, st.m_l2);
-    else online_update<2, C::NDB>(s, st.acc, st.m_run, st.l_run, st.scale_l2);
+    auto qk = [&](Half& x, const uint4& kf, int ds) {
+        x.s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
+                                                      __builtin_bit_cast(bf16x8, st.qf[ds]), x.s, 0, 0, 0);
+    };
+    auto pv = [&](const uint4& vf, const uint4& pb, int db) {
+        st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf),
+                                                             __builtin_bit_cast(bf16x8, pb), st.acc[db], 0, 0, 0);
+    };
+    Half h0, h1;
+    h0.s = f32x16{}; h1.s = f32x16{};
+    h0.rs = 0.0f; h1.rs = 0.0f;
+
+    // A: S^T of keys 0..31 (half 0).
+    uint4 kf[2 * NDS];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        const int kb = kk >> 1, r0 = 8 * (kk & 1);
-        uint4 pb;
-        pb.x = pack_bf16x2(s[kb][r0 + 0], s[kb][r0 + 1]);
-        pb.y = pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]);
-        pb.z = pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]);
-        pb.w = pack_bf16x2(s[kb][r0 + 6], s[kb][r0 + 7]);
+    for (int i = 0; i < kPrefetch; ++i) kf[i] = kfrag(i);
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-            uint4 nv = vf;
-            const int step = kk * C::NDB + db + 1;
-            if (step < 4 * C::NDB) nv = vfrag(step % C::NDB, step / C::NDB);
-            st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pb), st.acc[db], 0, 0, 0);
-            vf = nv;
-        }
+    for (int ds = 0; ds < NDS; ++ds) {
+        kf[ds + kPrefetch] = kfrag(ds + kPrefetch);
+        qk(h0, kf[ds], ds);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    // B: S^T of keys 32..63 (half 1) under the softmax of half 0.
+    float ms = st.m_l2;  // fixed-m reference (scaled)
+    bool resc = false;
+    float alpha = 1.0f;
+    if (masked) half_mask(h0, j0, 0, st.lo, st.hi);
+    if (BODY == BODY_ONLINE) {
+        alpha = half_online_ref(h0, st.m_run, st.scale_l2, resc);
+        ms = (st.m_run == kNegInf ? 0.0f : st.m_run) * st.scale_l2;
+    }
+    uint4 vf[4 * NDB];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+        const int i = NDS + ds;
+        if (i + kPrefetch < 2 * NDS) kf[i + kPrefetch] = kfrag(i + kPrefetch);
+        else vf[i + kPrefetch - 2 * NDS] = vfrag(i + kPrefetch - 2 * NDS);
+        qk(h1, kf[i], ds);
+        if (ds < 4) half_exp_slice(h0, ds, st.scale_l2, ms);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (BODY == BODY_ONLINE && resc) {  // rare: the row max moved by more than 2^kLazy
+        st.l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) st.acc[d] *= alpha;
+    }
+    // C: O^T += V^T P^T for keys 0..31 under the softmax of half 1.
+    if (masked) half_mask(h1, j0, 1, st.lo, st.hi);
+    bool resc1 = false;
+    float alpha1 = 1.0f;
+    if (BODY == BODY_ONLINE) {
+        alpha1 = half_online_ref(h1, st.m_run, st.scale_l2, resc1);
+        ms = (st.m_run == kNegInf ? 0.0f : st.m_run) * st.scale_l2;
+    }
+#pragma unroll
+    for (int j = 0; j < 2 * NDB; ++j) {
+        if (j + kPrefetch < 4 * NDB) vf[j + kPrefetch] = vfrag(j + kPrefetch);
+        pv(vf[j], h0.pb[j / NDB], j % NDB);
+        if (j < 4) half_exp_slice(h1, j, st.scale_l2, ms);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (BODY == BODY_ONLINE && resc1) {
+        st.l_run = (st.l_run + h0.rs) * alpha1;
+        h0.rs = 0.0f;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) st.acc[d] *= alpha1;
+    }
+    // D: O^T += V^T P^T for keys 32..63.
+#pragma unroll
+    for (int j = 2 * NDB; j < 4 * NDB; ++j) {
+        if (j + kPrefetch < 4 * NDB) vf[j + kPrefetch] = vfrag(j + kPrefetch);
+        pv(vf[j], h1.pb[(j - 2 * NDB) / NDB], j % NDB);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    st.l_run += h0.rs + h1.rs;
+}
+
+// Wait until at most n of this wave's vector-memory operations are in flight
+// (the tile copies are the only ones in the loop; n is wave-uniform).
+__device__ inline void wait_vm(int n) {
+    // s_waitcnt fields (gfx9): vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8].
+    if (n <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+    else if (n <= 4) __builtin_amdgcn_s_waitcnt(0x0F74);
+    else if (n <= 8) __builtin_amdgcn_s_waitcnt(0x0F78);
+    else __builtin_amdgcn_s_waitcnt(0x0F7C);
+}
+
+// The copy ring: NBUF K/V tile buffers, each its own LDS object, visited in
+// a compile-time unrolled order.  Reads of buffer I can then be told apart
+// from the copies still landing in the other buffers, so they do not wait
+// for them; the explicit wait before each barrier covers the copies of the
+// tile about to be used.
+template <int D, int NW>
+struct Ring {
+    using C = Bf16Cfg<D, NW>;
+    uint8_t* k[C::NBUF];
+    uint8_t* v[C::NBUF];
+};
+
+template <int D, int NW, int BODY, int I>
+__device__ __attribute__((always_inline)) inline bool bf16_step(const AttnLaunch& p, Bf16State<D, NW>& st,
+                                                               const Walk& walk, const Ring<D, NW>& ring,
+                                                               Cursor<64>& cur, Cursor<64>& ahead, bool& more,
+                                                               int& n_after, const __bf16* kbase,
+                                                               const __bf16* vbase, int kv_lim) {
+    using C = Bf16Cfg<D, NW>;
+    constexpr int NB = C::NBUF;
+    constexpr int LOADS = 2 * C::RUNS_PER_WAVE;
+    const int j0 = cur.j0;
+    const bool masked = cur.masked(walk.Lk);
+    // This tile's copies are complete in every wave, and every wave is done
+    // with the buffer the next copy goes to (the previous tile's).
+    wait_vm(n_after * LOADS);
+    __syncthreads();
+    if (more) more = ahead.next(walk);
+    if (more) {
+        constexpr int J = (I + NB - 1) % NB;
+        bf16_issue_tile<D, NW>(p, kbase, vbase, ahead.j0, kv_lim, ring.k[J], ring.v[J]);
+        ++n_after;
+    }
+    bf16_compute_tile<D, NW, BODY>(ring.k[I], ring.v[I], st, j0, masked);
+    const bool have = cur.next(walk);
+    if (have) --n_after;
+    return have;
 }
 
 template <int D, int NW, int BODY, int OUT>
-__device__ inline void bf16_run(const AttnLaunch& p, Bf16State<D, NW>& st, const Walk& walk, uint8_t* lds,
-                                i64 b, i64 h, i64 row) {
+__device__ inline void bf16_run(const AttnLaunch& p, Bf16State<D, NW>& st, const Walk& walk,
+                                const Ring<D, NW>& ring, i64 b, i64 h, i64 row) {
     using C = Bf16Cfg<D, NW>;
+    constexpr int NB = C::NBUF;
+    static_assert(NB == 2 || NB == 3, "ring of 2 or 3 buffers");
+    static_assert(2 * C::RUNS_PER_WAVE * (NB - 2) <= 12, "wait_vm covers at most 12 outstanding copies");
     const __bf16* kbase = (const __bf16*)p.k + b * p.k_sB + h * p.k_sH;
     const __bf16* vbase = (const __bf16*)p.v + b * p.v_sB + h * p.v_sH;
     const int kv_lim = (int)p.mask.kv_valid;
-    Cursor<C::TILE> cur;
+    // Copies run NB - 1 tiles ahead of the compute.
+    Cursor<C::TILE> cur, ahead;
     bool have = cur.next(walk);
-    int buf = 0;
-    if (have) {
-        bf16_load_tile<D, NW>(p, st, kbase, vbase, cur.j0, kv_lim);
-        bf16_store_tile<D, NW>(lds, lds + C::TILE_BYTES, st);
-        __syncthreads();
+    ahead = cur;
+    bool more = have;
+    int n_after = 0;  // tiles issued beyond the current one
+    if (have) bf16_issue_tile<D, NW>(p, kbase, vbase, ahead.j0, kv_lim, ring.k[0], ring.v[0]);
+    if (NB == 3) {
+        if (more) more = ahead.next(walk);
+        if (more) {
+            bf16_issue_tile<D, NW>(p, kbase, vbase, ahead.j0, kv_lim, ring.k[1], ring.v[1]);
+            ++n_after;
+        }
     }
     while (have) {
-        const int j0 = cur.j0;
-        const bool masked = cur.masked(walk.Lk);
-        have = cur.next(walk);
-        if (have) bf16_load_tile<D, NW>(p, st, kbase, vbase, cur.j0, kv_lim);
-        const uint8_t* kl = lds + buf * 2 * C::TILE_BYTES;
-        bf16_compute_tile<D, NW, BODY>(kl, kl + C::TILE_BYTES, st, j0, masked);
-        if (have) {
-            uint8_t* nl = lds + (buf ^ 1) * 2 * C::TILE_BYTES;
-            bf16_store_tile<D, NW>(nl, nl + C::TILE_BYTES, st);
-            __syncthreads();
-            buf ^= 1;
+        have = bf16_step<D, NW, BODY, 0>(p, st, walk, ring, cur, ahead, more, n_after, kbase, vbase, kv_lim);
+        if (!have) break;
+        have = bf16_step<D, NW, BODY, 1>(p, st, walk, ring, cur, ahead, more, n_after, kbase, vbase, kv_lim);
+        if (NB == 3) {
+            if (!have) break;
+            have = bf16_step<D, NW, BODY, NB - 1>(p, st, walk, ring, cur, ahead, more, n_after, kbase, vbase,
+                                                  kv_lim);
         }
     }
     store_out<D, OUT, BODY>(p, st.acc, st.m_run, st.l_run, st.m_fixed, b, h, row);
@@ -481,7 +629,13 @@ __device__ inline void bf16_run(const AttnLaunch& p, Bf16State<D, NW>& st, const
 template <int D, int NW, int MODE, int OUT>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_bf16(const AttnLaunch p) {
     using C = Bf16Cfg<D, NW>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t k0[C::TILE_BYTES], v0[C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t k1[C::TILE_BYTES], v1[C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t k2[C::NBUF == 3 ? C::TILE_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t v2[C::NBUF == 3 ? C::TILE_BYTES : 16];
+    Ring<D, NW> ring;
+    ring.k[0] = k0; ring.v[0] = v0; ring.k[1] = k1; ring.v[1] = v1;
+    if (C::NBUF == 3) { ring.k[C::NBUF - 1] = k2; ring.v[C::NBUF - 1] = v2; }
     __shared__ int red[4 * NW];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -500,16 +654,18 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_bf16(const 
     Bf16State<D, NW> st;
     const i64 row = qb * C::BQ + wave * 32 + l32;
     const bool row_ok = row < p.Lq;
-    st.lo = 0; st.hi = 0;
+    int lo = 0, hi = 0;
     if (row_ok) {
         if (p.have_blocks) {
             const i64 lb = p.list_batch == 1 ? 0 : b;
-            st.lo = p.row_lo[lb * p.Lq + row];
-            st.hi = p.row_hi[lb * p.Lq + row];
+            lo = p.row_lo[lb * p.Lq + row];
+            hi = p.row_hi[lb * p.Lq + row];
         } else {
-            row_interval(p.mask, b, row, st.lo, st.hi);
+            row_interval(p.mask, b, row, lo, hi);
         }
     }
+    st.lo = lo;
+    st.hi = hi;
     // Q^T operand fragments: lane holds Q[row][ds*16 + hb*8 + 0..7].
     const __bf16* qp = (const __bf16*)p.q + b * p.q_sB + row * p.q_sL + h * p.q_sH;
 #pragma unroll
@@ -527,12 +683,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_bf16(const 
     }
     st.scale_l2 = p.scale * kLog2e;
 
-    const Walk walk = make_walk<C::TILE, C::NT>(p, b, qb, st.lo, st.hi, row_ok, red);
+    const bool ne = row_ok && lo < hi;
+    const Walk walk = make_walk<C::TILE, C::NT>(p, b, qb, ne ? lo : 0x7fffffff, ne ? hi : 0,
+                                                row_ok ? (ne ? lo : 0x7fffffff) : 0,
+                                                row_ok ? (ne ? hi : -1) : 0x7fffffff, red);
     if (MODE == MODE_GATED) {
-        if (fixed) bf16_run<D, NW, BODY_FIXED, OUT>(p, st, walk, lds, b, h, row);
-        else bf16_run<D, NW, BODY_ONLINE, OUT>(p, st, walk, lds, b, h, row);
+        if (fixed) bf16_run<D, NW, BODY_FIXED, OUT>(p, st, walk, ring, b, h, row);
+        else bf16_run<D, NW, BODY_ONLINE, OUT>(p, st, walk, ring, b, h, row);
     } else {
-        bf16_run<D, NW, MODE, OUT>(p, st, walk, lds, b, h, row);
+        bf16_run<D, NW, MODE, OUT>(p, st, walk, ring, b, h, row);
     }
 }
 
@@ -624,7 +783,10 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_f32(const AttnLaunch p) {
 #pragma unroll
     for (int ds = 0; ds < D / 2; ++ds) qf[ds] = row_ok ? qp[ds * 2 + hb] : 0.0f;
     const float m_fixed = (fixed && row_ok) ? p.m[bh * p.Lq + row] : 0.0f;
-    const Walk walk = make_walk<TILE, 256>(p, b, qb, lo, hi, row_ok, red);
+    const bool ne = row_ok && lo < hi;
+    const Walk walk = make_walk<TILE, 256>(p, b, qb, ne ? lo : 0x7fffffff, ne ? hi : 0,
+                                           row_ok ? (ne ? lo : 0x7fffffff) : 0,
+                                           row_ok ? (ne ? hi : -1) : 0x7fffffff, red);
     if (fixed) f32_run<D, BODY_FIXED, OUT>(p, walk, ks, vs, qf, lo, hi, m_fixed, b, h, row);
     else f32_run<D, BODY_ONLINE, OUT>(p, walk, ks, vs, qf, lo, hi, m_fixed, b, h, row);
 }
@@ -634,7 +796,7 @@ hipError_t launch_one(const AttnLaunch& a, hipStream_t stream) {
     const i64 grid = a.n_qblocks * (i64)a.B * a.H;
     if (grid == 0) return hipSuccess;
     if (a.in_dtype == BWA_BF16) {
-        constexpr int NW = D == 128 ? 8 : 4;
+        constexpr int NW = kBf16Waves;
         hipLaunchKernelGGL((attn_fwd_bf16<D, NW, MODE, OUT>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, a);
     } else {
         hipLaunchKernelGGL((attn_fwd_f32<D, MODE, OUT>), dim3((unsigned)grid), dim3(256), 0, stream, a);
@@ -657,7 +819,7 @@ hipError_t launch_d(const AttnLaunch& a, hipStream_t stream) {
 
 }  // namespace
 
-int attn_rows_per_block(int dtype, int D) { return (dtype == BWA_BF16 && D == 128) ? 256 : 128; }
+int attn_rows_per_block(int dtype, int D) { return dtype == BWA_BF16 ? 32 * kBf16Waves : 128; }
 
 hipError_t launch_attn_fwd(const AttnLaunch& a, hipStream_t stream) {
     if (a.D == 64) return launch_d<64>(a, stream);

@@ -157,6 +157,8 @@ int32_t bwa_block_mask_build(const bwa_mask* mask, int64_t B, int64_t lq, int64_
         return fail(BWA_ERR_CAPACITY, "capacity %lld < required %lld", (long long)out->capacity, (long long)cap);
     if (!out->row_ptr || !out->run_begin || !out->run_end || !out->run_kind || (lq > 0 && (!out->row_lo || !out->row_hi)))
         return fail(BWA_ERR_NULL_ARG, "blocks arrays must be non-NULL");
+    // One work-item per (copy, row) and one wave per (copy, q-block): under 2^32 work-items per launch.
+    if (lb * lq >= ((i64)1 << 32) - 256) return fail(BWA_ERR_UNSUPPORTED, "block list grid too large");
     bwa::BlocksLaunch a;
     resolve_mask(mask, B, lq, lk, a.mask);
     a.copies = lb;
@@ -273,7 +275,8 @@ int32_t bwa_attn_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor*
         a.capacity = blocks->capacity;
         a.bkv_list = blocks->bkv;
     }
-    if (B * H * ((Lq + bq - 1) / bq) >= ((i64)1 << 31)) return fail(BWA_ERR_UNSUPPORTED, "grid too large");
+    // One workgroup of up to 512 work-items per (b, h, q-block); a launch holds under 2^32 work-items.
+    if (B * H * ((Lq + bq - 1) / bq) >= ((i64)1 << 23)) return fail(BWA_ERR_UNSUPPORTED, "grid too large");
     a.q = q->ptr; a.k = k->ptr; a.v = v->ptr;
     a.q_sB = q->sB; a.q_sL = q->sL; a.q_sH = q->sH;
     a.k_sB = k->sB; a.k_sL = k->sL; a.k_sH = k->sH;
@@ -315,6 +318,9 @@ int32_t bwa_lse_merge(int32_t n_parts, const bwa_tensor* o_parts, const float* c
         a.lse[t] = lse_parts[t];
         a.sB[t] = p.sB; a.sL[t] = p.sL; a.sH[t] = p.sH;
     }
+    // One 256-work-item workgroup per 64 tokens of a (b, h); a launch holds under 2^32 work-items.
+    if (o_out->B * o_out->H * ((o_out->L + 63) / 64) >= ((i64)1 << 24))
+        return fail(BWA_ERR_UNSUPPORTED, "merge grid too large");
     a.n_parts = n_parts;
     a.B = (int)o_out->B; a.H = (int)o_out->H; a.D = (int)o_out->D;
     a.L = o_out->L;

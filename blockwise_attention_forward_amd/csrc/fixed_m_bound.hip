@@ -22,7 +22,10 @@
 namespace bwa {
 namespace {
 
-constexpr int kRowsPerTask = 256;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRowsPerTask = 1024;  // rows of the flattened [B, L, H] order per workgroup
+constexpr int kMaxHeadsLds = 256;   // per-head maxima kept in LDS up to this many heads
 
 struct NormTasks {
     BoundLaunch a;
@@ -39,32 +42,61 @@ __global__ __launch_bounds__(256) void init_kernel(const BoundLaunch a) {
     a.mmax_out[bh] = 0.0f;  // holds max ||q_i|| until finalize
 }
 
+// Rows are taken in memory order (token-major: all heads of a token are
+// adjacent), so each workgroup streams one contiguous stretch of the tensor.
+// Per-head maxima collect in LDS with integer max on the IEEE bits of the
+// non-negative norms, then one global atomic max per head and workgroup (a
+// workgroup whose rows straddle two batch elements goes straight to global).
 template <int D, int DT>
 __global__ __launch_bounds__(256) void norms_kernel(const NormTasks nt) {
     constexpr int EPL = DT == BWA_BF16 ? 8 : 4;  // elements per 16-byte load
     constexpr int TPR = D / EPL;                 // threads per row
     constexpr int RPP = 256 / TPR;               // rows per pass
-    __shared__ float red[4];
+    constexpr int UNROLL = 8;                    // passes in flight per thread
+    __shared__ unsigned hmax[kMaxHeadsLds];
     const BoundLaunch& a = nt.a;
     const i64 task = blockIdx.x;
     int t = 0;
     while (t <= a.n_chunks && task >= nt.task_off[t + 1]) ++t;
     const BoundTensor& T = (t == 0) ? a.q : a.k[t - 1];
-    const i64 local = task - nt.task_off[t];
-    const i64 nrb = (T.L + kRowsPerTask - 1) / kRowsPerTask;
-    const i64 bh = local / nrb, rb = local % nrb;
-    const i64 b = bh / a.H, h = bh % a.H;
+    const i64 rows = (i64)a.B * T.L * a.H;
+    const i64 r_begin = (task - nt.task_off[t]) * kRowsPerTask;
+    const int n_rows = (int)min<i64>(kRowsPerTask, rows - r_begin);
+    // Start of the stretch in (b, l, h); rows inside it are offsets of at most
+    // kRowsPerTask from here, so 32-bit division finds each row's indices.
+    const unsigned H = (unsigned)a.H, L = (unsigned)T.L;
+    const i64 tok0 = r_begin / H;
+    const unsigned h0 = (unsigned)(r_begin - tok0 * H);
+    const i64 b0 = tok0 / L;
+    const unsigned l0 = (unsigned)(tok0 - b0 * L);
+    const bool one_batch = (i64)l0 + (h0 + (unsigned)n_rows - 1) / H < (i64)L;
+    const bool in_lds = a.H <= kMaxHeadsLds && one_batch;
     const int tid = threadIdx.x, sub = tid % TPR;
-    float mx = 0.0f;
-    for (int pass = 0; pass < kRowsPerTask / RPP; ++pass) {
-        const i64 r = rb * kRowsPerTask + pass * RPP + tid / TPR;
-        float ss = 0.0f;
-        if (r < T.L) {
-            const uint8_t* rowp = (const uint8_t*)T.ptr +
-                                  (b * T.sB + r * T.sL + h * T.sH) * (DT == BWA_BF16 ? 2 : 4);
-            const uint4 w = *(const uint4*)(rowp + sub * 16);
+    for (int i = tid; i < kMaxHeadsLds; i += 256) hmax[i] = 0u;
+    __syncthreads();
+    const int es = DT == BWA_BF16 ? 2 : 4;
+    for (int j0 = 0; j0 < n_rows; j0 += RPP * UNROLL) {
+        u32x4 w[UNROLL];
+        unsigned hh[UNROLL], ll[UNROLL], bb[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int j = j0 + u * RPP + tid / TPR;
+            const unsigned x = h0 + (unsigned)j, y = l0 + x / H;
+            hh[u] = x % H;
+            ll[u] = y % L;
+            bb[u] = y / L;
+            w[u] = u32x4{0, 0, 0, 0};
+            if (j < n_rows) {
+                const i64 b = b0 + bb[u];
+                const uint8_t* rowp = (const uint8_t*)T.ptr + (b * T.sB + (i64)ll[u] * T.sL + (i64)hh[u] * T.sH) * es;
+                w[u] = __builtin_nontemporal_load((const u32x4*)(rowp + sub * 16));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            float ss = 0.0f;
             if (DT == BWA_BF16) {
-                const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+                const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float x0 = __uint_as_float(ws[i] << 16);
@@ -73,28 +105,34 @@ __global__ __launch_bounds__(256) void norms_kernel(const NormTasks nt) {
                     ss = __builtin_fmaf(x1, x1, ss);
                 }
             } else {
-                const float xs[4] = {__uint_as_float(w.x), __uint_as_float(w.y),
-                                     __uint_as_float(w.z), __uint_as_float(w.w)};
+                const float xs[4] = {__uint_as_float(w[u].x), __uint_as_float(w[u].y),
+                                     __uint_as_float(w[u].z), __uint_as_float(w[u].w)};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ss = __builtin_fmaf(xs[i], xs[i], ss);
             }
-        }
 #pragma unroll
-        for (int o = TPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-        const float nrm = __builtin_sqrtf(ss);
-        if (r < T.L && sub == 0) {
-            if (t == 0) a.m_out[bh * T.L + r] = nrm;
-            if (r < T.valid) mx = fmaxf(mx, nrm);
+            for (int o = TPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+            const int j = j0 + u * RPP + tid / TPR;
+            if (j < n_rows && sub == 0) {
+                const i64 b = b0 + bb[u], h = hh[u], l = ll[u];
+                const float nrm = __builtin_sqrtf(ss);
+                if (t == 0) a.m_out[(b * a.H + h) * T.L + l] = nrm;
+                if (l < T.valid) {
+                    if (in_lds) atomicMax(&hmax[h], __float_as_uint(nrm));
+                    else atomicMax((unsigned int*)((t == 0) ? &a.mmax_out[b * a.H + h] : &a.kmax_out[b * a.H + h]),
+                                   __float_as_uint(nrm));
+                }
+            }
         }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    if ((tid & 63) == 0) red[tid >> 6] = mx;
     __syncthreads();
-    if (tid == 0) {
-        mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-        float* dst = (t == 0) ? &a.mmax_out[bh] : &a.kmax_out[bh];
-        atomicMax((unsigned int*)dst, __float_as_uint(mx));
+    if (in_lds) {
+        for (int h = tid; h < a.H; h += 256) {
+            const unsigned v = hmax[h];
+            if (v == 0u) continue;
+            float* dst = (t == 0) ? &a.mmax_out[b0 * a.H + h] : &a.kmax_out[b0 * a.H + h];
+            atomicMax((unsigned int*)dst, v);
+        }
     }
 }
 
@@ -129,11 +167,12 @@ hipError_t launch_fixed_m_bound(const BoundLaunch& a, hipStream_t stream) {
     NormTasks nt;
     nt.a = a;
     nt.task_off[0] = 0;
-    nt.task_off[1] = (i64)BH * ((a.q.L + kRowsPerTask - 1) / kRowsPerTask);
+    nt.task_off[1] = ((i64)BH * a.q.L + kRowsPerTask - 1) / kRowsPerTask;
     for (int c = 0; c < a.n_chunks; ++c)
-        nt.task_off[c + 2] = nt.task_off[c + 1] + (i64)BH * ((a.k[c].L + kRowsPerTask - 1) / kRowsPerTask);
+        nt.task_off[c + 2] = nt.task_off[c + 1] + ((i64)BH * a.k[c].L + kRowsPerTask - 1) / kRowsPerTask;
     for (int c = a.n_chunks + 2; c < kMaxChunks + 2; ++c) nt.task_off[c] = nt.task_off[a.n_chunks + 1];
     const i64 tasks = nt.task_off[a.n_chunks + 1];
+    if (tasks >= ((i64)1 << 24)) return hipErrorInvalidConfiguration;  // 256 work-items each, < 2^32 in all
     if (tasks > 0) {
         if (a.D == 64) {
             if (a.dtype == BWA_BF16) launch_norms<64, BWA_BF16>(nt, tasks, stream);

@@ -6,10 +6,11 @@
 // from its true max.  For each row: lse = ln sum_t exp(lse_t) and
 // O = sum_t exp(lse_t - lse) O_t; a row no chunk saw stays O = 0, lse = -inf.
 //
-// Pure streaming (no reuse): D/4 lanes cover one row with 16-byte loads of
-// every partial, so a wavefront reads whole contiguous rows and the work is
-// bound by HBM bandwidth.  The per-row weights are computed redundantly by
-// the row's lanes from a broadcast load of the partial LSEs.
+// Pure streaming (no reuse), bound by HBM bandwidth.  A workgroup takes 64
+// consecutive tokens of one (b, h): their LSEs are contiguous, so the weight
+// pass reads and writes whole lines and leaves the weights in LDS; then D/4
+// lanes cover one output row with 16-byte loads, eight rows per thread in
+// flight, every partial read once with non-temporal loads.
 
 #include "internal.h"
 
@@ -19,58 +20,82 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-template <int D, int OUT>
-__global__ __launch_bounds__(256) void merge_kernel(const MergeLaunch a) {
-    constexpr int TPR = D / 4;        // lanes per row
-    constexpr int RPB = 256 / TPR;    // rows per workgroup
-    const i64 rows = (i64)a.B * a.L * a.H;
-    const i64 r = (i64)blockIdx.x * RPB + threadIdx.x / TPR;
-    if (r >= rows) return;
-    const int c = (threadIdx.x % TPR) * 4;
-    const i64 h = r % a.H;
-    const i64 l = (r / a.H) % a.L;
-    const i64 b = r / ((i64)a.H * a.L);
-    const i64 li = (b * a.H + h) * a.L + l;
+constexpr int kTok = 64;  // tokens of one (b, h) per workgroup
 
-    float lse_t[kMaxParts];
-    float mx = -__builtin_inff();
+template <int D, int OUT>
+__global__ __launch_bounds__(256) void merge_kernel(const MergeLaunch a, const i64 n_lblk) {
+    constexpr int TPR = D / 4;       // lanes per row (16-byte loads)
+    constexpr int RPP = 256 / TPR;   // rows per pass of the workgroup
+    constexpr int R = kTok / RPP;    // rows per thread
+    __shared__ float wts[kMaxParts][kTok];
+    const i64 bh = blockIdx.x / n_lblk;
+    const i64 l0 = (blockIdx.x % n_lblk) * kTok;
+    const i64 b = bh / a.H, h = bh % a.H;
+    const int tid = threadIdx.x;
+    const int n = a.n_parts;
+
+    // Per-row weights w_t = exp(lse_t - lse), computed once per row; the LSE
+    // of a (b, h) is contiguous over tokens, so these loads coalesce.
+    if (tid < kTok) {
+        const i64 l = l0 + tid;
+        if (l < a.L) {
+            const i64 li = bh * a.L + l;
+            float lt[kMaxParts];
+            float mx = -__builtin_inff();
 #pragma unroll
-    for (int t = 0; t < kMaxParts; ++t) {
-        if (t < a.n_parts) { lse_t[t] = a.lse[t][li]; mx = fmaxf(mx, lse_t[t]); }
-    }
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    float lse = -__builtin_inff();
-    if (mx != -__builtin_inff()) {
-        float tot = 0.0f;
+            for (int t = 0; t < kMaxParts; ++t)
+                if (t < n) { lt[t] = a.lse[t][li]; mx = fmaxf(mx, lt[t]); }
+            float tot = 0.0f;
 #pragma unroll
-        for (int t = 0; t < kMaxParts; ++t) {
-            if (t < a.n_parts) {
-                const float w = __expf(lse_t[t] - mx);
-                tot += w;
-                const f32x4 o = *(const f32x4*)(a.o[t] + b * a.sB[t] + l * a.sL[t] + h * a.sH[t] + c);
-                acc += w * o;
-            }
+            for (int t = 0; t < kMaxParts; ++t)
+                if (t < n) { lt[t] = mx == -__builtin_inff() ? 0.0f : __expf(lt[t] - mx); tot += lt[t]; }
+            const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
+#pragma unroll
+            for (int t = 0; t < kMaxParts; ++t)
+                if (t < n) wts[t][tid] = lt[t] * inv;
+            if (a.lse_out) a.lse_out[li] = tot > 0.0f ? mx + __logf(tot) : -__builtin_inff();
         }
-        acc *= 1.0f / tot;
-        lse = mx + __logf(tot);
     }
-    const i64 ob = b * a.out_sB + l * a.out_sL + h * a.out_sH + c;
-    if (OUT == BWA_F32) {
-        *(f32x4*)((float*)a.out + ob) = acc;
-    } else {
-        *(bf16x4*)((__bf16*)a.out + ob) = __builtin_convertvector(acc, bf16x4);
+    __syncthreads();
+
+    const int c = (tid % TPR) * 4, rr = tid / TPR;
+    f32x4 acc[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) acc[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 2
+    for (int t = 0; t < n; ++t) {
+        const float* base = a.o[t] + b * a.sB[t] + h * a.sH[t] + c;
+        const i64 sL = a.sL[t];
+        f32x4 o[R];
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const i64 l = l0 + rr + u * RPP;
+            o[u] = l < a.L ? __builtin_nontemporal_load((const f32x4*)(base + l * sL)) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const float w = wts[t][rr + u * RPP];
+            // A part with weight 0 (its LSE is -inf) adds nothing, whatever its O holds.
+            acc[u] += w * (w != 0.0f ? o[u] : f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+        }
     }
-    if (a.lse_out && c == 0) a.lse_out[li] = lse;
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const i64 l = l0 + rr + u * RPP;
+        if (l >= a.L) continue;
+        const i64 ob = b * a.out_sB + l * a.out_sL + h * a.out_sH + c;
+        if (OUT == BWA_F32) __builtin_nontemporal_store(acc[u], (f32x4*)((float*)a.out + ob));
+        else __builtin_nontemporal_store(__builtin_convertvector(acc[u], bf16x4), (bf16x4*)((__bf16*)a.out + ob));
+    }
 }
 
 template <int D>
 hipError_t launch_d(const MergeLaunch& a, hipStream_t stream) {
-    constexpr int RPB = 256 / (D / 4);
-    const i64 rows = (i64)a.B * a.L * a.H;
-    if (rows == 0) return hipSuccess;
-    const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
-    if (a.out_dtype == BWA_F32) hipLaunchKernelGGL((merge_kernel<D, BWA_F32>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((merge_kernel<D, BWA_BF16>), grid, dim3(256), 0, stream, a);
+    if ((i64)a.B * a.H * a.L == 0) return hipSuccess;
+    const i64 n_lblk = (a.L + kTok - 1) / kTok;
+    const dim3 grid((unsigned)(n_lblk * a.B * a.H));
+    if (a.out_dtype == BWA_F32) hipLaunchKernelGGL((merge_kernel<D, BWA_F32>), grid, dim3(256), 0, stream, a, n_lblk);
+    else hipLaunchKernelGGL((merge_kernel<D, BWA_BF16>), grid, dim3(256), 0, stream, a, n_lblk);
     return hipGetLastError();
 }
 

@@ -243,6 +243,8 @@ int32_t bwa_attn_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor*
  * [FIXEDM Notes: the fallback merge in LSE space, invariant to the overshoot]:
  *   lse[b,h,i] = ln sum_t exp(lse_t[b,h,i])            (-inf if all are -inf)
  *   O[b,i,h,:] = sum_t exp(lse_t - lse) O_t[b,i,h,:]    (0 if lse is -inf)
+ * A part whose lse_t is -inf on a row has weight 0 there and its O_t row is
+ * not used (it may hold anything, NaN included).
  * n_parts in [1, 16]; o_parts: host array of n_parts fp32 tensors of one
  * shape; lse_parts: host array of n_parts device pointers to fp32 [B][H][L];
  * o_out: same B, L, H, D in fp32 or bf16 (may alias no input); lse_out:

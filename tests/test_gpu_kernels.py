@@ -155,6 +155,29 @@ def test_fixed_m_bound_and_gate():
     assert gate[1, 2].item() == 0 and gate[0, 3].item() == 0
 
 
+@pytest.mark.parametrize("B,L,H,D,dtype", [
+    (3, 50, 4, 128, torch.bfloat16),   # several batch elements inside one workgroup's row stretch
+    (2, 1500, 5, 64, torch.bfloat16),  # stretches straddle batch boundaries
+    (2, 9, 300, 64, torch.float32),    # more heads than the per-head LDS table
+    (1, 4097, 3, 128, torch.float32),
+])
+def test_fixed_m_bound_batch_and_head_layouts(B, L, H, D, dtype):
+    q = _rand((B, L, H, D), 44, dtype)
+    ks = [_rand((B, L + 3, H, D), 45, dtype), _rand((B, max(L // 2, 1), H, D), 46, dtype)]
+    for b in range(B):
+        ks[b % 2][b, 1, b % H] *= 20.0  # a distinct maximum per batch element
+        q[b, L - 1, (b + 1) % H] *= 7.0
+    scale = 1 / math.sqrt(D)
+    kmax, mmax, m, gate = bw.bwa_fixed_m_bound(q, ks, scale, 106.5)
+    for b in range(B):
+        for h in range(H):
+            km, mr, mm, g = oracle.fixed_m_bound(np64(q[b, :, h]), [np64(c[b, :, h]) for c in ks], scale, 106.5)
+            np.testing.assert_allclose(kmax[b, h].item(), km, rtol=1e-6)
+            np.testing.assert_allclose(np64(m[b, h]), mr, rtol=2e-6)
+            np.testing.assert_allclose(mmax[b, h].item(), mm, rtol=2e-6)
+            assert bool(gate[b, h].item()) == g
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_fixed_m_attention_and_gated_pair(D):
     B, H, Lq, Lk = 1, 4, 300, 400
@@ -208,6 +231,35 @@ def test_lse_merge_against_oracle(n_parts, out_dtype):
     np.testing.assert_allclose(got_l[f], ref_l[f], atol=1e-5, rtol=0)
     tol = 1e-5 if out_dtype == torch.float32 else 1e-2
     np.testing.assert_allclose(np64(o), ref_o, atol=tol, rtol=0 if out_dtype == torch.float32 else 8e-3)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_lse_merge_dead_parts_and_strided_views(D):
+    # A part whose LSE is -inf on a row has weight 0 there: its O row is not
+    # used, so NaN in it must not reach the result.  Parts are strided views.
+    B, L, H = 2, 300, 3
+    g = torch.Generator(device=DEV).manual_seed(66)
+    big = [torch.randn(B, L, H + 1, 2 * D, device=DEV, generator=g) for _ in range(2)]
+    os_ = [x[:, :, 1:, :D] for x in big]
+    ls = [torch.randn(B, H, L, device=DEV, generator=g) * 3 for _ in range(2)]
+    ls[1][0, 1, 100:180] = -float("inf")
+    os_[1][0, 100:180, 1] = float("nan")
+    ls[0][1, 2, 250:] = -float("inf")
+    ls[1][1, 2, 250:] = -float("inf")
+    os_[0][1, 250:, 2] = float("nan")
+    out = torch.empty(B, L, H + 2, D, device=DEV)[:, :, 2:]
+    o, l = bw.bwa_lse_merge(os_, ls, o_out=out, out_dtype=torch.float32)
+    clean = [torch.where(torch.isneginf(lt).permute(0, 2, 1)[..., None], torch.zeros_like(ot), ot)
+             for ot, lt in zip(os_, ls)]
+    ref_o, ref_l = oracle.lse_merge([(np64(a).transpose(0, 2, 1, 3), np64(b)) for a, b in zip(clean, ls)])
+    ref_o = ref_o.transpose(0, 2, 1, 3)
+    got_o, got_l = np64(o), np64(l)
+    assert np.all(np.isfinite(got_o))
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(ref_l))
+    assert np.all(got_o[1, 250:, 2] == 0)
+    f = np.isfinite(ref_l)
+    np.testing.assert_allclose(got_l[f], ref_l[f], atol=1e-5, rtol=0)
+    np.testing.assert_allclose(got_o, ref_o, atol=1e-5, rtol=0)
 
 
 def test_deterministic_repeat():

@@ -169,7 +169,7 @@ def setup_dit_share(torch, bw, synth):
         import numpy as np
         import oracle
         h = 0
-        rows = synth.sample_rows(Lq, 256, seed=11, must=[0, Lq - 1])
+        rows = synth.sample_rows(Lq, 32768, seed=11, must=[0, Lq - 1])
         qh = q[0, :, h].double().cpu().numpy()
         kh = torch.cat([k[0, :, h] for k in ks]).double().cpu().numpy()
         vh = torch.cat([v[0, :, h] for v in vs]).double().cpu().numpy()
@@ -201,7 +201,7 @@ def main():
     ap.add_argument("--workload", default="dit_share", choices=["dit_share"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="first run 3 plain device copies of MIB MiB (scale for HBM byte counters)")
+                    help="first run 3 plain elementwise copies of MIB MiB (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share only (one MI355X); multi-GPU runs are not part of "
@@ -214,11 +214,13 @@ def main():
 
     torch.cuda.set_device(0)
     if args.copy_calibration > 0:
-        n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        # A plain elementwise kernel of known traffic (reads and writes MIB MiB
+        # each): the scale between HBM byte counters and bytes moved.
+        n = (args.copy_calibration << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
     W = setup_dit_share(torch, bw, synth)

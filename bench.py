@@ -80,8 +80,14 @@ class Timer:
 
 
 def _source_sha():
+    """Hash of the attention kernel source without comments and blank lines."""
     p = os.path.join(ROOT, "blockwise_attention_forward_amd", "csrc", "attn_fwd.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    code = []
+    for line in open(p, encoding="utf-8"):
+        line = line.split("//", 1)[0].rstrip()
+        if line:
+            code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def _traffic(kernel_key):

@@ -14,13 +14,17 @@
 // cores so that each lane ends up holding one query row's scores: the row
 // max and row sum are in-lane reductions plus one cross-half lane swap.  The
 // probabilities then feed O^T = V^T P^T straight from the registers the
-// scores came out in.  V is staged transposed in LDS (a register transpose
-// per thread while storing), K row-major; both use an XOR swizzle of 16-byte
-// chunks so that the matrix-core operand reads of a wave hit distinct banks.
-// Tiles are double-buffered: the global loads of the next tile are in flight
-// while the current tile is computed.  K/V rows are fetched through buffer
-// resources whose range ends at the last valid key, so rows past it read as
-// zero without a branch.
+// scores came out in.  K and V tiles go from HBM straight into LDS with
+// buffer loads that write LDS (no register staging), in an XOR swizzle of
+// 16-byte chunks chosen so that the operand reads of a wave hit distinct
+// banks; V is read back transposed by the LDS transpose-read instruction.
+// Tiles circulate in a ring of three (8-wave blocks) or two buffers: the
+// copies of the next tiles are in flight while the current one is computed.
+// Inside a wave, the tile is processed in halves of 32 keys so that the
+// exponentials of one half overlap the matrix-core work of the other.  K/V
+// rows are fetched through buffer resources whose range ends at the last
+// valid key, so rows past it read as zero without a branch.  The fp32 path
+// (32x32x2 fp32 matrix cores, 32-key tiles) stages through registers.
 //
 // Softmax bodies ("Fixed-m softmax for 2D-ring x Ulysses attention (WAN 2.2)",
 // description):

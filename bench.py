@@ -20,6 +20,9 @@ roofline   = the dominant kernel (the gated attention launch of one hop):
              the launch stream), against the bf16 dense matrix-core peak.
 cpu_baseline = the fp64 oracle timed on the host on a bounded sample of the
              same workload (rank 0, N = 1 only).
+measured_ceilings = what this device sustains, beside the published peaks: a
+             bf16 matrix-core probe (register operands only; libbwa_probe.so)
+             and a plain 1 GiB elementwise copy.
 """
 
 import argparse
@@ -190,6 +193,51 @@ def setup_dit_share(torch, bw, synth):
                 sample_oracle=sample_oracle, hops=len(ks))
 
 
+def _measured_ceilings(torch):
+    """What this device sustains: bf16 matrix-core throughput (probe library)
+    and the bandwidth of a plain elementwise copy (read N bytes, write N)."""
+    import ctypes
+    out = {}
+    probe = os.path.join(ROOT, "blockwise_attention_forward_amd", "libbwa_probe.so")
+    if os.path.exists(probe):
+        lib = ctypes.CDLL(probe)
+        f = lib.bwa_probe_mfma_bf16
+        f.restype = ctypes.c_int32
+        f.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        blocks, iters = 256 * 4, 20000  # four wavefronts per SIMD
+        sink = torch.empty(blocks * 256, device="cuda")
+        clocks = torch.zeros(2, dtype=torch.int64, device="cuda")
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        assert f(iters // 10, blocks, sink.data_ptr(), clocks.data_ptr(), stream) == 0
+        rates, ghz = [], []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            assert f(iters, blocks, sink.data_ptr(), clocks.data_ptr(), stream) == 0
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b)
+            rates.append(blocks * 4 * iters * 4 * 32768.0 / (ms * 1e-3) / 1e12)
+            cyc, ticks = (int(x) for x in clocks.cpu())
+            ghz.append(cyc / (ticks / 100e6) / 1e9 if ticks else float("nan"))
+        out["mfma_bf16_TFLOPs"] = round(sum(rates) / len(rates), 1)
+        out["mfma_probe_clock_GHz"] = round(sum(ghz) / len(ghz), 3)
+    n = (1 << 30) // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    b.record()
+    torch.cuda.synchronize()
+    out["copy_GBps"] = round(2.0 * n * 4 * 5 / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+    del src, dst
+    return out
+
+
 def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -256,6 +304,14 @@ def main():
     ms_online_hop = t2.mean_ms("online_hop")
     ms_fixed_hop = t2.mean_ms("fixed_hop")
 
+    meas = _measured_ceilings(torch)
+    if "mfma_bf16_TFLOPs" in meas:
+        meas["attn_pct_of_measured_mfma"] = round(100.0 * achieved / meas["mfma_bf16_TFLOPs"], 1)
+    merge_gbps = W["bytes_merge"] / (ms_merge * 1e-3) / 1e9
+    bound_gbps = W["bytes_bound"] / (ms_bound * 1e-3) / 1e9
+    meas["merge_pct_of_copy"] = round(100.0 * merge_gbps / meas["copy_GBps"], 1)
+    meas["bound_pct_of_copy"] = round(100.0 * bound_gbps / meas["copy_GBps"], 1)
+
     cpu = None
     if not args.no_cpu_baseline:
         fl, dt, what = W["sample_oracle"]()
@@ -282,9 +338,12 @@ def main():
         "online_only_ms_per_kv_hop": round(ms_online_hop, 4),
         "fixed_m_all_heads_ms_per_kv_hop": round(ms_fixed_hop, 4),
         "merge_ms": round(ms_merge, 4),
-        "merge_GBps": round(W["bytes_merge"] / (ms_merge * 1e-3) / 1e9, 1),
+        "merge_GBps": round(merge_gbps, 1),
+        "merge_pct_of_hbm_peak": round(100.0 * merge_gbps / PEAK_HBM_GBS, 1),
         "bound_ms": round(ms_bound, 4),
-        "bound_GBps": round(W["bytes_bound"] / (ms_bound * 1e-3) / 1e9, 1),
+        "bound_GBps": round(bound_gbps, 1),
+        "bound_pct_of_hbm_peak": round(100.0 * bound_gbps / PEAK_HBM_GBS, 1),
+        "measured_ceilings": meas,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": _traffic("attn_fwd_bf16_gated")},

@@ -13,6 +13,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libbwattn.so")
+PROBE_LIB = os.path.join(HERE, "libbwa_probe.so")  # measurement helper (matrix-core peak)
 ARCH = os.environ.get("BWATTN_ARCH", "gfx950")
 
 FLAGS = [
@@ -39,18 +40,25 @@ def _run(cmd):
     return out
 
 
+def _link(hipcc, srcs, objdir, lib, ex):
+    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
+    outs = list(ex.map(lambda so: _run([hipcc, *FLAGS, "-c", so[0], "-o", so[1]]), zip(srcs, objs)))
+    tmp = lib + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, lib)
+    return outs
+
+
 def build(verbose=False):
     hipcc = _hipcc()
     srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+    probe_srcs = sorted(glob.glob(os.path.join(HERE, "probe", "*.hip")))
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
     jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        outs = list(ex.map(lambda so: _run([hipcc, *FLAGS, "-c", so[0], "-o", so[1]]), zip(srcs, objs)))
-    tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+        outs = _link(hipcc, srcs, objdir, LIB, ex)
+        outs += _link(hipcc, probe_srcs, objdir, PROBE_LIB, ex)
     if verbose:
         for o in outs:
             if o.strip():

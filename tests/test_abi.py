@@ -18,8 +18,12 @@ bw = pytest.importorskip("blockwise_attention_forward_amd")
 L = bw._lib
 
 
-def _declared():
-    text = open(HEADER).read()
+PROBE_HEADER = os.path.join(ROOT, "include", "bwa_probe.h")
+PROBE_LIB = os.path.join(ROOT, "blockwise_attention_forward_amd", "libbwa_probe.so")
+
+
+def _declared(header=HEADER):
+    text = open(header).read()
     return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(bwa_\w+)\s*\(", text, flags=re.M)))
 
 
@@ -30,6 +34,28 @@ def test_exports_every_declared_symbol():
     assert not missing, missing
     for n in ("bwa_attn_fwd", "bwa_lse_merge", "bwa_fixed_m_bound", "bwa_block_mask_build"):
         assert n in names
+
+
+def test_every_header_is_covered():
+    # each header under include/ belongs to one of the two libraries checked here
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert headers == ["bwa_probe.h", "bwattn.h"]
+
+
+def test_probe_library_exports_and_rejects_bad_arguments():
+    if not os.path.exists(PROBE_LIB):
+        pytest.skip("libbwa_probe.so not built")
+    lib = ctypes.CDLL(PROBE_LIB)
+    names = _declared(PROBE_HEADER)
+    assert names == ["bwa_probe_mfma_bf16"]
+    assert all(hasattr(lib, n) for n in names)
+    f = lib.bwa_probe_mfma_bf16
+    f.restype = ctypes.c_int32
+    f.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    # argument errors are reported before any launch
+    assert f(0, 1, ctypes.c_void_p(16), None, None) == 1
+    assert f(1, 0, ctypes.c_void_p(16), None, None) == 1
+    assert f(1, 1, None, None, None) == 1
 
 
 def test_struct_layout_matches_header():

@@ -20,7 +20,7 @@ __all__ = [
     "BWA_TILE_SKIP", "BWA_TILE_FULL", "BWA_TILE_PARTIAL", "BwaError", "Mask", "BlockLists",
     "lib_path", "bwa_version", "bwa_status_string", "bwa_last_error", "bwa_attn_tile",
     "bwa_block_mask_size", "bwa_block_mask_build", "bwa_fixed_m_bound", "bwa_attn_fwd",
-    "bwa_lse_merge",
+    "bwa_attn_fwd_carry", "bwa_lse_merge",
 ]
 
 BWA_F32, BWA_BF16 = 0, 1
@@ -76,6 +76,7 @@ def _load():
         "bwa_block_mask_build": (I32, [MP, I64, I64, I64, BP, P]),
         "bwa_fixed_m_bound": (I32, [TP, TP, I32, P, I32, I64P, I64, F32, F32, P, P, P, P, P]),
         "bwa_attn_fwd": (I32, [TP, TP, TP, MP, BP, F32, I32, P, P, TP, P, P]),
+        "bwa_attn_fwd_carry": (I32, [TP, TP, TP, MP, BP, F32, I32, P, P, TP, P, TP, P, P]),
         "bwa_lse_merge": (I32, [I32, TP, ctypes.POINTER(ctypes.c_void_p), TP, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -259,6 +260,28 @@ def bwa_attn_fwd(q, k, v, mask=None, blocks=None, scale=None, mode=BWA_MODE_ONLI
     _check(_lib.bwa_attn_fwd(ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), ctypes.byref(mk.struct),
                              bs, float(scale), int(mode), _ptr(m), _ptr(gate), ctypes.byref(ot),
                              _ptr(lse), _stream(q.device)), "bwa_attn_fwd")
+    return o, lse
+
+
+def bwa_attn_fwd_carry(q, k, v, o_prev, lse_prev, mask=None, blocks=None, scale=None, mode=BWA_MODE_ONLINE,
+                       m=None, gate=None, o=None, lse=None, out_dtype=None):
+    """bwa_attn_fwd over k/v merged with the carried fp32 partial (o_prev,
+    lse_prev) of earlier key chunks.  o may be o_prev itself (fp32) and lse may
+    be lse_prev.  Returns (o, lse)."""
+    B, Lq, H, D = q.shape
+    if scale is None:
+        scale = D ** -0.5
+    if o is None:
+        o = torch.empty(B, Lq, H, D, dtype=out_dtype or q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, H, Lq, dtype=torch.float32, device=q.device)
+    mk = Mask.of(mask, q.device)
+    qt, kt, vt, ot, pt = _tensor(q), _tensor(k), _tensor(v), _tensor(o), _tensor(o_prev)
+    bs = ctypes.byref(blocks.struct) if blocks is not None else None
+    _check(_lib.bwa_attn_fwd_carry(ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), ctypes.byref(mk.struct),
+                                   bs, float(scale), int(mode), _ptr(m), _ptr(gate), ctypes.byref(pt),
+                                   _ptr(lse_prev), ctypes.byref(ot), _ptr(lse), _stream(q.device)),
+           "bwa_attn_fwd_carry")
     return o, lse
 
 

@@ -224,9 +224,10 @@ int32_t bwa_fixed_m_bound(const bwa_tensor* q, const bwa_tensor* k_chunks, int32
     return hip_status(bwa::launch_fixed_m_bound(a, (hipStream_t)stream), "fixed_m_bound launch");
 }
 
-int32_t bwa_attn_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v, const bwa_mask* mask,
-                     const bwa_blocks* blocks, float scale, int32_t mode, const float* m,
-                     const uint8_t* gate, bwa_tensor* o, float* lse, void* stream) {
+static int32_t attn_fwd_impl(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v, const bwa_mask* mask,
+                             const bwa_blocks* blocks, float scale, int32_t mode, const float* m,
+                             const uint8_t* gate, const bwa_tensor* o_prev, const float* lse_prev, bwa_tensor* o,
+                             float* lse, void* stream) {
     int32_t st;
     if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
         (st = check_tensor(o, "o")))
@@ -292,7 +293,34 @@ int32_t bwa_attn_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor*
     a.m = m;
     a.gate = gate;
     a.n_qblocks = (Lq + bq - 1) / bq;
+    if (o_prev) {
+        if ((st = check_tensor(o_prev, "o_prev"))) return st;
+        if (o_prev->dtype != BWA_F32) return fail(BWA_ERR_BAD_DTYPE, "o_prev must be fp32");
+        if (o_prev->B != q->B || o_prev->L != q->L || o_prev->H != q->H || o_prev->D != q->D)
+            return fail(BWA_ERR_BAD_SHAPE, "o_prev must have q's shape");
+        if (rows > 0 && !lse_prev) return fail(BWA_ERR_NULL_ARG, "lse_prev is NULL");
+        if (o_prev->ptr == o->ptr &&
+            (o->dtype != BWA_F32 || o_prev->sB != o->sB || o_prev->sL != o->sL || o_prev->sH != o->sH))
+            return fail(BWA_ERR_BAD_STRIDE, "o may alias o_prev only as the same fp32 tensor (same strides)");
+        a.o_prev = (const float*)o_prev->ptr;
+        a.op_sB = o_prev->sB; a.op_sL = o_prev->sL; a.op_sH = o_prev->sH;
+        a.lse_prev = rows > 0 ? lse_prev : nullptr;
+    }
     return hip_status(bwa::launch_attn_fwd(a, (hipStream_t)stream), "attn_fwd launch");
+}
+
+int32_t bwa_attn_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v, const bwa_mask* mask,
+                     const bwa_blocks* blocks, float scale, int32_t mode, const float* m,
+                     const uint8_t* gate, bwa_tensor* o, float* lse, void* stream) {
+    return attn_fwd_impl(q, k, v, mask, blocks, scale, mode, m, gate, nullptr, nullptr, o, lse, stream);
+}
+
+int32_t bwa_attn_fwd_carry(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v, const bwa_mask* mask,
+                           const bwa_blocks* blocks, float scale, int32_t mode, const float* m,
+                           const uint8_t* gate, const bwa_tensor* o_prev, const float* lse_prev, bwa_tensor* o,
+                           float* lse, void* stream) {
+    if (!o_prev) return fail(BWA_ERR_NULL_ARG, "o_prev is NULL");
+    return attn_fwd_impl(q, k, v, mask, blocks, scale, mode, m, gate, o_prev, lse_prev, o, lse, stream);
 }
 
 int32_t bwa_lse_merge(int32_t n_parts, const bwa_tensor* o_parts, const float* const* lse_parts,

@@ -269,15 +269,42 @@ __device__ inline void store_out(const AttnLaunch& p, f32x16 (&acc)[D / 32], flo
     const float l = pair_sum(l_run);
     if (row >= p.Lq) return;
     const bool any = l > 0.0f;
-    const float inv = any ? 1.0f / l : 0.0f;
+    // This call's partial: O = acc / l, LSE = reference + ln l (natural-log units).
+    float lse = any ? (BODY == BODY_FIXED ? m_fixed : m_run * p.scale) + __logf(l) : kNegInf;
+    float w_cur = any ? 1.0f / l : 0.0f, w_prev = 0.0f;
+    const i64 li = (b * p.H + h) * p.Lq + row;
+    if (p.lse_prev) {
+        // Carried partial of earlier key chunks ("Fixed-m softmax for 2D-ring x
+        // Ulysses attention (WAN 2.2)", Notes: hop partials combine in LSE
+        // space): lse = ln(e^lse + e^lse_prev), O = e^(lse_cur-lse) O_cur +
+        // e^(lse_prev-lse) O_prev.  A side whose LSE is -inf has weight 0.
+        const float lp = p.lse_prev[li];
+        const float mx = fmaxf(lse, lp);
+        if (mx != kNegInf) {  // once per row: the accurate exp and log
+            const float ec = any ? expf(lse - mx) : 0.0f;
+            const float ep = lp != kNegInf ? expf(lp - mx) : 0.0f;
+            const float tot = ec + ep;
+            w_cur *= ec / tot;
+            w_prev = ep / tot;
+            lse = mx + logf(tot);
+        }
+    }
     const i64 base = b * p.o_sB + row * p.o_sL + h * p.o_sH;
+    const i64 pbase = b * p.op_sB + row * p.op_sL + h * p.op_sH;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int d = db * 32 + 8 * g + hb * 4;
-            const float o0 = acc[db][4 * g] * inv, o1 = acc[db][4 * g + 1] * inv;
-            const float o2 = acc[db][4 * g + 2] * inv, o3 = acc[db][4 * g + 3] * inv;
+            float o0 = acc[db][4 * g] * w_cur, o1 = acc[db][4 * g + 1] * w_cur;
+            float o2 = acc[db][4 * g + 2] * w_cur, o3 = acc[db][4 * g + 3] * w_cur;
+            if (w_prev != 0.0f) {
+                const f32x4 pv = *(const f32x4*)(p.o_prev + pbase + d);
+                o0 += w_prev * pv[0];
+                o1 += w_prev * pv[1];
+                o2 += w_prev * pv[2];
+                o3 += w_prev * pv[3];
+            }
             if (OUT == BWA_F32) {
                 f32x4 v = {o0, o1, o2, o3};
                 *(f32x4*)((float*)p.o + base + d) = v;
@@ -286,11 +313,7 @@ __device__ inline void store_out(const AttnLaunch& p, f32x16 (&acc)[D / 32], flo
                 *(uint2*)((__bf16*)p.o + base + d) = v;
             }
         }
-    if (hb == 0) {
-        float lse = kNegInf;
-        if (any) lse = (BODY == BODY_FIXED ? m_fixed : m_run * p.scale) + __logf(l);
-        p.lse[(b * p.H + h) * p.Lq + row] = lse;
-    }
+    if (hb == 0) p.lse[li] = lse;
 }
 
 // ---------------------------------------------------------------------------

@@ -88,6 +88,9 @@ struct AttnLaunch {
     int mode;
     const float* m;
     const uint8_t* gate;
+    // carried partial of earlier key chunks (lse_prev != nullptr): merged in the epilogue
+    const float* o_prev; i64 op_sB, op_sL, op_sH;
+    const float* lse_prev;
     // run lists (have_blocks != 0)
     int have_blocks;
     const i64* row_ptr; const int* run_begin; const int* run_end; const uint8_t* run_kind;

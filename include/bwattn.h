@@ -239,6 +239,32 @@ int32_t bwa_attn_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor*
                      bwa_tensor* o, float* lse, void* stream);
 
 /*
+ * bwa_attn_fwd with a carried partial [FIXEDM Notes: hop partials combine in
+ * LSE space; the next step there is to fold the combine into the hop itself].
+ * Computes this call's attention over k/v exactly as bwa_attn_fwd does and
+ * merges it, in the epilogue, with a partial (o_prev, lse_prev) over other,
+ * disjoint key chunks of the same queries:
+ *   lse = ln(e^lse_this + e^lse_prev)
+ *   o   = e^(lse_this - lse) o_this + e^(lse_prev - lse) o_prev
+ * so a ring of hops needs no separate merge pass: each hop carries the
+ * running partial forward and the last hop can write the final output in
+ * bf16.  A side whose LSE is -inf has weight 0 (its O rows are not read);
+ * a row that both sides leave empty gets O = 0, LSE = -inf.
+ * o_prev: device fp32 tensor of q's shape (non-NULL); lse_prev: device fp32
+ * [B][H][Lq].  o may be the same tensor as o_prev (same pointer, fp32, same
+ * strides) and lse may be lse_prev: each row is read before it is written,
+ * by the same thread; any other overlap is not allowed.  With a gate, only
+ * the rows this call writes are merged.  Errors as for bwa_attn_fwd, plus
+ * BWA_ERR_NULL_ARG (o_prev or lse_prev NULL), BWA_ERR_BAD_DTYPE (o_prev not
+ * fp32), BWA_ERR_BAD_SHAPE, BWA_ERR_BAD_STRIDE (partial alias of o).
+ */
+int32_t bwa_attn_fwd_carry(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
+                           const bwa_mask* mask, const bwa_blocks* blocks, float scale,
+                           int32_t mode, const float* m, const uint8_t* gate,
+                           const bwa_tensor* o_prev, const float* lse_prev,
+                           bwa_tensor* o, float* lse, void* stream);
+
+/*
  * Log-sum-exp merge of attention partials over disjoint key chunks
  * [FIXEDM Notes: the fallback merge in LSE space, invariant to the overshoot]:
  *   lse[b,h,i] = ln sum_t exp(lse_t[b,h,i])            (-inf if all are -inf)

@@ -1,8 +1,11 @@
 """Shared test helpers: oracle runs over [B, L, H, D] tensors and tolerance checks.
 
 Tolerances: bf16 inputs with fp32 accumulation -> output max-abs <= 2e-2 and
-mean-abs <= 2e-3; fp32 inputs -> max-abs <= 1e-5.  LSE: 1e-3 (bf16 inputs),
-1e-5 (fp32 inputs).  Rows that see nothing must be exactly 0 with LSE -inf.
+mean-abs <= 2e-3; fp32 inputs -> max-abs <= 1e-5.  LSE: 1e-3 + 1e-5 |lse|
+(bf16 inputs), 1e-5 + 1e-6 |lse| (fp32 inputs): the LSE carries the rounding
+of an fp32 score, so above magnitude 1 its error grows with it (a score of
+about 660 times a scale of 1/sqrt(128) gives an LSE near 58, whose fp32 ulp is
+3.8e-6).  Rows that see nothing must be exactly 0 with LSE -inf.
 """
 
 import numpy as np
@@ -11,8 +14,8 @@ import torch
 import oracle
 
 TOL = {
-    torch.bfloat16: dict(max=2e-2, mean=2e-3, lse=1e-3),
-    torch.float32: dict(max=1e-5, mean=1e-5, lse=1e-5),
+    torch.bfloat16: dict(max=2e-2, mean=2e-3, lse=1e-3, lse_rel=1e-5),
+    torch.float32: dict(max=1e-5, mean=1e-5, lse=1e-5, lse_rel=1e-6),
 }
 
 
@@ -76,6 +79,9 @@ def assert_close(o_gpu, lse_gpu, o_ref, lse_ref, in_dtype, what=""):
     assert mean <= tol["mean"], f"{what}: mean abs err {mean:.3e} > {tol['mean']}"
     live = ~dead
     if live.any():
-        le = float(np.abs(lse[live] - lse_ref[live]).max())
-        assert le <= tol["lse"], f"{what}: LSE max abs err {le:.3e} > {tol['lse']}"
+        err_l = np.abs(lse[live] - lse_ref[live])
+        bound = tol["lse"] + tol["lse_rel"] * np.abs(lse_ref[live])
+        worst = int(np.argmax(err_l - bound))
+        assert np.all(err_l <= bound), (f"{what}: LSE err {err_l[worst]:.3e} > {bound[worst]:.3e} "
+                                        f"at |lse| = {abs(lse_ref[live][worst]):.3g}")
     return mx, mean

@@ -139,6 +139,26 @@ def test_mask_errors(mask, code):
     assert _attn(q, _t(), _t(), _t(), mask=_mask(**mask)) == code
 
 
+def _carry(q, k, v, o, o_prev, lse_prev=0x30000, lse=0x20000):
+    return L.bwa_attn_fwd_carry(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(_mask()), None,
+                                0.1, 0, None, None, ctypes.byref(o_prev) if o_prev is not None else None,
+                                lse_prev, ctypes.byref(o), lse, None)
+
+
+@pytest.mark.parametrize("o_prev,o,lse_prev,code", [
+    (None, {}, 0x30000, 1),                          # o_prev is required
+    (dict(dtype=1), {}, 0x30000, 4),                 # carried partial must be fp32
+    (dict(dtype=0, L=255), {}, 0x30000, 2),          # not q's shape
+    (dict(dtype=0), {}, None, 1),                    # lse_prev missing
+    (dict(dtype=0, ptr=0x50000), dict(ptr=0x50000), 0x30000, 3),   # alias with a bf16 output
+    (dict(dtype=0, ptr=0x50000, sH=256), dict(ptr=0x50000, dtype=0), 0x30000, 3),  # alias, other strides
+])
+def test_attn_fwd_carry_argument_errors(o_prev, o, lse_prev, code):
+    op = _t(**o_prev) if o_prev is not None else None
+    assert _carry(_t(), _t(), _t(), _t(**o), op, lse_prev=lse_prev) == code
+    assert bw.bwa_last_error() != ""
+
+
 def test_fixed_m_needs_m_and_lse():
     q = _t()
     assert _attn(q, _t(), _t(), _t(), mode=1, m=None) == 1

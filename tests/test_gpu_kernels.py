@@ -262,6 +262,73 @@ def test_lse_merge_dead_parts_and_strided_views(D):
     np.testing.assert_allclose(got_o, ref_o, atol=1e-5, rtol=0)
 
 
+@pytest.mark.parametrize("D,dtype", [(128, torch.bfloat16), (64, torch.bfloat16), (128, torch.float32)])
+@pytest.mark.parametrize("mode", ["online", "fixed", "gated"])
+def test_attn_fwd_carry_two_chunks(D, dtype, mode):
+    # Two key chunks of one causal sequence: chunk 0 = keys [0, 200), chunk 1 =
+    # keys [200, 370).  Hop 0 writes an fp32 partial, hop 1 merges into it.
+    B, H, Lq, L0, L1 = 2, 3, 300, 200, 170
+    scale = 1 / math.sqrt(D)
+    q = _rand((B, Lq, H, D), 80, dtype)
+    k = _rand((B, L0 + L1, H, D), 81, dtype)
+    v = _rand((B, L0 + L1, H, D), 82, dtype)
+    k[1, 5, 2] *= 30  # head 2 of batch 1 fails the gate
+    ks, vs = [k[:, :L0], k[:, L0:]], [v[:, :L0], v[:, L0:]]
+    masks = [{"causal": True, "kv_offset": 0, "q_valid": 290}, {"causal": True, "kv_offset": L0, "q_valid": 290}]
+    kmax, mmax, m, gate = bw.bwa_fixed_m_bound(q, ks, scale, 106.5, q_valid=290)
+    args = {"online": dict(mode=bw.BWA_MODE_ONLINE),
+            "fixed": dict(mode=bw.BWA_MODE_FIXED_M, m=m),
+            "gated": dict(mode=bw.BWA_MODE_GATED, m=m, gate=gate)}[mode]
+    o_ref, l_ref = oracle_attention(q, k, v, {"causal": True, "q_valid": 290}, scale)
+    heads = [0, 1, 2] if mode != "fixed" else [0, 1]  # fixed-m is exact only for heads that pass the gate
+    if mode == "fixed":
+        assert gate[0].tolist() == [1, 1, 1] and gate[1, 2].item() == 0
+    o0, l0 = bw.bwa_attn_fwd(q, ks[0], vs[0], masks[0], scale=scale, out_dtype=torch.float32, **args)
+    for out_dtype in (torch.float32, dtype):
+        o, l = bw.bwa_attn_fwd_carry(q, ks[1], vs[1], o0, l0, masks[1], scale=scale, out_dtype=out_dtype, **args)
+        assert_close(o[:, :, heads], l[:, heads], o_ref[:, :, heads], l_ref[:, heads], dtype, f"carry {mode}")
+    # same result as two partials merged by bwa_lse_merge
+    o1, l1 = bw.bwa_attn_fwd(q, ks[1], vs[1], masks[1], scale=scale, out_dtype=torch.float32, **args)
+    om, lm = bw.bwa_lse_merge([o0, o1], [l0, l1], out_dtype=torch.float32)
+    oc, lc = bw.bwa_attn_fwd_carry(q, ks[1], vs[1], o0, l0, masks[1], scale=scale, out_dtype=torch.float32, **args)
+    assert torch.equal(torch.isneginf(lc), torch.isneginf(lm))
+    fin = torch.isfinite(lm)
+    assert (lc[fin] - lm[fin]).abs().max().item() <= 1e-5
+    assert (oc - om).abs().max().item() <= 1e-5
+    # in place: the carried partial is overwritten by the merged result
+    oi, li = o0.clone(), l0.clone()
+    bw.bwa_attn_fwd_carry(q, ks[1], vs[1], oi, li, masks[1], scale=scale, o=oi, lse=li, **args)
+    assert torch.equal(oi, oc) and torch.equal(li, lc)
+
+
+def test_attn_fwd_carry_dead_sides_and_nan():
+    # Rows the carried partial never saw (lse_prev = -inf) ignore its O rows,
+    # NaN included; rows neither side sees come out 0 / -inf.
+    B, H, Lq, Lk, D = 1, 2, 200, 150, 128
+    scale = 1 / math.sqrt(D)
+    q = _rand((B, Lq, H, D), 90, torch.bfloat16)
+    k = _rand((B, Lk, H, D), 91, torch.bfloat16)
+    v = _rand((B, Lk, H, D), 92, torch.bfloat16)
+    mask = {"causal": True, "kv_offset": 40, "q_valid": 190}  # rows < 40 see nothing in this chunk
+    o_prev = torch.randn(B, Lq, H, D, device=DEV)
+    l_prev = torch.randn(B, H, Lq, device=DEV)
+    l_prev[0, 0, 100:] = -float("inf")
+    o_prev[0, 100:, 0] = float("nan")
+    l_prev[0, 1, :30] = -float("inf")  # rows 0..29 of head 1: empty on both sides
+    o, l = bw.bwa_attn_fwd_carry(q, k, v, o_prev, l_prev, mask, scale=scale, out_dtype=torch.float32)
+    cur_o, cur_l = oracle_attention(q, k, v, mask, scale)
+    prev_o = np64(o_prev).transpose(0, 2, 1, 3)
+    prev_o[np.isneginf(np64(l_prev))] = 0.0
+    ref_o, ref_l = oracle.lse_merge([(cur_o.transpose(0, 2, 1, 3), cur_l), (prev_o, np64(l_prev))])
+    got_o, got_l = np64(o), np64(l)
+    assert np.all(np.isfinite(got_o))
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(ref_l))
+    assert np.all(got_o[0, :30, 1] == 0) and np.all(np.isneginf(got_l[0, 1, :30]))
+    f = np.isfinite(ref_l)
+    np.testing.assert_allclose(got_l[f], ref_l[f], atol=1e-3, rtol=0)
+    np.testing.assert_allclose(got_o, ref_o.transpose(0, 2, 1, 3), atol=2e-2, rtol=0)
+
+
 def test_deterministic_repeat():
     B, H, L, D = 1, 4, 500, 128
     q, k, v = (_rand((B, L, H, D), s, torch.bfloat16) for s in (70, 71, 72))

@@ -172,6 +172,40 @@ def test_dit_gated_and_online_hops(dit):
     assert_close(*gpu_rows(o_o, l_o, rows), o_ref, l_ref, BF16, "dit online")
 
 
+def _hops_carry(d, mode, m=None, gate=None):
+    """The hops chained by the carried partial: hop 0 writes fp32, the last hop the bf16 result."""
+    q = d["q"]
+    B, Lq, H, D = q.shape
+    bq, _ = bw.bwa_attn_tile(BF16, D)
+    o = lse = None
+    n = len(d["k_chunks"])
+    for t, (k, v, off) in enumerate(zip(d["k_chunks"], d["v_chunks"], d["kv_offsets"])):
+        mask = {"kv_offset": off}
+        blocks = bw.bwa_block_mask_build(mask, B, Lq, k.shape[1], bq, 128)
+        kw = dict(mask=mask, blocks=blocks, scale=d["scale"], mode=mode, m=m, gate=gate,
+                  out_dtype=BF16 if t == n - 1 else torch.float32)
+        if t == 0:
+            o, lse = bw.bwa_attn_fwd(q, k, v, **kw)
+        else:
+            o, lse = bw.bwa_attn_fwd_carry(q, k, v, o, lse, **kw)
+    return o, lse
+
+
+def test_dit_hops_chained_by_carry(dit):
+    q = dit["q"]
+    Lq = q.shape[1]
+    kmax, mmax, m, gate = bw.bwa_fixed_m_bound(q, dit["k_chunks"], dit["scale"], 106.5)
+    o, l = _hops_carry(dit, bw.BWA_MODE_GATED, m=m, gate=gate)
+    assert o.dtype == BF16
+    rows = synth.sample_rows(Lq, 512, seed=26, must=[0, 1, 127, 128, Lq - 41, Lq - 1])
+    o_ref, l_ref = _dit_oracle(dit, rows)
+    assert_close(*gpu_rows(o, l, rows), o_ref, l_ref, BF16, "dit carried hops")
+    # and every row agrees with the separate merge pass to bf16 rounding
+    o_m, l_m = _hops(dit, bw.BWA_MODE_GATED, m=m, gate=gate)
+    assert (l - l_m).abs().max().item() <= 1e-5
+    assert (o.float() - o_m.float()).abs().max().item() <= 2 ** -7
+
+
 def test_dit_all_heads_eligible():
     d = synth.make_dit_share(DEV, seed=1013, sink=False)
     q = d["q"]

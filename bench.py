@@ -146,6 +146,27 @@ def setup_dit_share(torch, bw, synth):
         if timer:
             timer.stop(tm)
 
+    def step_carry(timer=None):
+        """The same step with the hops chained by the carried partial: hop 0
+        writes an fp32 partial, hop 1 merges into it in its epilogue and writes
+        the bf16 result, so there is no separate merge launch."""
+        for t, m in enumerate(masks):
+            bw.bwa_block_mask_build(m, B, Lq, Lc, bq, 128, out=blocks[t])
+        kmax, mmax, mm, gate = bw.bwa_fixed_m_bound(q, ks, scale, tau, out=bound_out)
+        tok = timer.start("hop0") if timer else None
+        bw.bwa_attn_fwd(q, ks[0], vs[0], m=mm, mask=masks[0], blocks=blocks[0], scale=scale,
+                        mode=bw.BWA_MODE_GATED, gate=gate, o=o_parts[0], lse=l_parts[0])
+        if timer:
+            timer.stop(tok)
+        for t in range(1, len(ks)):
+            last = t == len(ks) - 1
+            tok = timer.start("hop_carry") if timer else None
+            bw.bwa_attn_fwd_carry(q, ks[t], vs[t], o_parts[0], l_parts[0], m=mm, mask=masks[t], blocks=blocks[t],
+                                  scale=scale, mode=bw.BWA_MODE_GATED, gate=gate,
+                                  o=o_out if last else o_parts[0], lse=l_out if last else l_parts[0])
+            if timer:
+                timer.stop(tok)
+
     def online_hop(timer):
         tok = timer.start("online_hop")
         bw.bwa_attn_fwd(q, ks[0], vs[0], mask=masks[0], blocks=blocks[0], scale=scale,
@@ -188,9 +209,60 @@ def setup_dit_share(torch, bw, synth):
         fl = 4.0 * D * len(rows) * kh.shape[0]
         return fl, dt, f"head 0, {len(rows)} seeded query rows x all {kh.shape[0]} keys (both hops), fp64"
 
-    return dict(step=step, online_hop=online_hop, flops_step=flops_step, flops_dominant=flops_hop,
+    return dict(step=step, step_carry=step_carry, online_hop=online_hop, flops_step=flops_step, flops_dominant=flops_hop,
                 dominant="hop", info=info, bytes_merge=bytes_merge, bytes_bound=bytes_bound,
                 sample_oracle=sample_oracle, hops=len(ks))
+
+
+def setup_single(torch, bw, synth, name):
+    """One attention call of a masked workload (run lists + attention)."""
+    if name == "varlen":
+        d = synth.make_varlen("cuda")
+        desc = ("varlen: H3 packed request, B=1 H=24 D=128 bf16, 33,024 tokens, cu_seqlens [0, 33002, 33024], "
+                "22 alignment rows zeroed")
+    elif name == "window":
+        d = synth.make_window(8192, 8192, 2048, "cuda")
+        desc = "window: causal sliding window W=2048, B=1 H=16 D=128 bf16, Lq=Lk=8192"
+    elif name in ("long_causal", "long_causal_packed"):
+        d = synth.make_long_causal("cuda", packed=name.endswith("packed"))
+        desc = ("long_causal: B=1 H=8 D=128 bf16, Lq=Lk=1,048,576 causal"
+                + (", packed segments of U[4096, 131072] tokens" if name.endswith("packed") else ""))
+    else:
+        raise ValueError(name)
+    q, k, v, scale = d["q"], d["k"], d["v"], d["scale"]
+    B, Lq, H, D = q.shape
+    Lk = k.shape[1]
+    mask = bw.Mask.of(d["mask"], "cuda")
+    bq, _ = bw.bwa_attn_tile(q.dtype, D)
+    blocks = bw.bwa_block_mask_build(mask, B, Lq, Lk, bq, 128)
+    count_lists = bw.bwa_block_mask_build(mask, B, Lq, Lk, 128, 128)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, Lq, device="cuda")
+    torch.cuda.synchronize()
+    flops = _counted_flops(count_lists, D, H, Lq, Lk)
+
+    def step(timer=None):
+        bw.bwa_block_mask_build(mask, B, Lq, Lk, bq, 128, out=blocks)
+        tok = timer.start("hop") if timer else None
+        bw.bwa_attn_fwd(q, k, v, mask, blocks=blocks, scale=scale, o=o, lse=lse)
+        if timer:
+            timer.stop(tok)
+
+    def sample_oracle():
+        import oracle
+        rows = synth.sample_rows(Lq, 64, seed=11, must=[0, Lq - 1])
+        m = dict(d["mask"])
+        qh, kh, vh = (x[0, :, 0].double().cpu().numpy() for x in (q, k, v))
+        t0 = time.perf_counter()
+        oracle.attention_rows(qh, kh, vh, m, scale, rows)
+        dt = time.perf_counter() - t0
+        lo, hi = oracle.row_intervals(Lq, Lk, m)
+        fl = 4.0 * D * float(sum(max(0, int(hi[r]) - int(lo[r])) for r in rows))
+        return fl, dt, f"head 0, {len(rows)} seeded query rows against their visible keys, fp64"
+
+    info = dict(workload=desc, B=B, H=H, D=D, Lq=Lq, Lk=Lk)
+    return dict(step=step, flops_step=flops, flops_dominant=flops, dominant="hop", info=info,
+                sample_oracle=sample_oracle)
 
 
 def _measured_ceilings(torch):
@@ -252,7 +324,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="dit_share", choices=["dit_share"])
+    ap.add_argument("--workload", default="dit_share",
+                    choices=["dit_share", "varlen", "window", "long_causal", "long_causal_packed"],
+                    help="dit_share (default) is the measured configuration; the others time one masked call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 3 plain elementwise copies of MIB MiB (scale for HBM byte counters)")
@@ -277,6 +351,8 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    if args.workload != "dit_share":
+        return run_single(args, torch, bw, synth)
     W = setup_dit_share(torch, bw, synth)
     timer = Timer(torch)
     for _ in range(args.warmup):
@@ -303,6 +379,19 @@ def main():
     torch.cuda.synchronize()
     ms_online_hop = t2.mean_ms("online_hop")
     ms_fixed_hop = t2.mean_ms("fixed_hop")
+
+    # the step with the hops chained by the carried partial (no merge launch)
+    t3 = Timer(torch)
+    for _ in range(args.warmup):
+        W["step_carry"]()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    c0.record()
+    for _ in range(args.steps):
+        W["step_carry"](t3)
+    c1.record()
+    torch.cuda.synchronize()
+    ms_step_carry = c0.elapsed_time(c1) / args.steps
 
     meas = _measured_ceilings(torch)
     if "mfma_bf16_TFLOPs" in meas:
@@ -337,6 +426,10 @@ def main():
         "ms_per_kv_hop": round(ms_hop, 4),
         "online_only_ms_per_kv_hop": round(ms_online_hop, 4),
         "fixed_m_all_heads_ms_per_kv_hop": round(ms_fixed_hop, 4),
+        "carried_hops": {"ms_per_step": round(ms_step_carry, 4),
+                         "TFLOPs": round(W["flops_step"] / (ms_step_carry * 1e-3) / 1e12, 2),
+                         "ms_hop0": round(t3.mean_ms("hop0"), 4),
+                         "ms_carry_hop": round(t3.mean_ms("hop_carry"), 4)},
         "merge_ms": round(ms_merge, 4),
         "merge_GBps": round(merge_gbps, 1),
         "merge_pct_of_hbm_peak": round(100.0 * merge_gbps / PEAK_HBM_GBS, 1),
@@ -347,6 +440,43 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": _traffic("attn_fwd_bf16_gated")},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def run_single(args, torch, bw, synth):
+    """A masked workload: one attention call per step (bf16 in and out)."""
+    W = setup_single(torch, bw, synth, args.workload)
+    timer = Timer(torch)
+    for _ in range(args.warmup):
+        W["step"]()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        W["step"](timer)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    ms_hop = timer.mean_ms("hop")
+    value = W["flops_step"] / (ms_step * 1e-3) / 1e12
+    achieved = W["flops_dominant"] / (ms_hop * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        fl, dt, what = W["sample_oracle"]()
+        cpu = {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+               "sample": what, "seconds": round(dt, 3), "host_cores_available": len(os.sched_getaffinity(0))}
+    out = {
+        "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak; ms per call",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic", "config": W["info"],
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "ms_attention": round(ms_hop, 4),
+        "counted_TFLOP": round(W["flops_step"] / 1e12, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

@@ -445,10 +445,12 @@ __device__ inline void half_exp_slice(Half& x, int q, float scale_l2, float ms) 
 // Online reference update for one half: returns the factor acc and l must be
 // scaled by (1 when the reference stays), or sets rescale = false.
 __device__ inline float half_online_ref(const Half& x, float& m_run, float scale_l2, bool& rescale) {
-    float mx = kNegInf;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x.s[r]);
-    mx = pair_max(mx);
+    // Tree of three-way maxima: depth 3 instead of a chain of 8.
+    const float a0 = fmaxf(fmaxf(x.s[0], x.s[1]), x.s[2]), a1 = fmaxf(fmaxf(x.s[3], x.s[4]), x.s[5]);
+    const float a2 = fmaxf(fmaxf(x.s[6], x.s[7]), x.s[8]), a3 = fmaxf(fmaxf(x.s[9], x.s[10]), x.s[11]);
+    const float a4 = fmaxf(fmaxf(x.s[12], x.s[13]), x.s[14]);
+    const float b0 = fmaxf(fmaxf(a0, a1), a2), b1 = fmaxf(fmaxf(a3, a4), x.s[15]);
+    float mx = pair_max(fmaxf(b0, b1));
     const bool need = mx * scale_l2 > (m_run == kNegInf ? kNegInf : m_run * scale_l2 + kLazy);
     rescale = __builtin_amdgcn_ballot_w64(need) != 0;
     float alpha = 1.0f;
@@ -512,15 +514,13 @@ __device__ inline void bf16_compute_tile(const uint8_t* kl, const uint8_t* vl, B
         qk(h0, kf[ds], ds);
         __builtin_amdgcn_sched_barrier(0);
     }
-    // B: S^T of keys 32..63 (half 1) under the softmax of half 0.
+    // B: S^T of keys 32..63 (half 1) under the softmax of half 0.  The
+    // online reference of half 0 is settled after the first matrix-core
+    // step, which does not depend on it, so that its reduction runs under it.
     float ms = st.m_l2;  // fixed-m reference (scaled)
     bool resc = false;
     float alpha = 1.0f;
     if (masked) half_mask(h0, j0, 0, st.lo, st.hi);
-    if (BODY == BODY_ONLINE) {
-        alpha = half_online_ref(h0, st.m_run, st.scale_l2, resc);
-        ms = (st.m_run == kNegInf ? 0.0f : st.m_run) * st.scale_l2;
-    }
     uint4 vf[4 * NDB];
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
@@ -528,29 +528,41 @@ __device__ inline void bf16_compute_tile(const uint8_t* kl, const uint8_t* vl, B
         if (i + kPrefetch < 2 * NDS) kf[i + kPrefetch] = kfrag(i + kPrefetch);
         else vf[i + kPrefetch - 2 * NDS] = vfrag(i + kPrefetch - 2 * NDS);
         qk(h1, kf[i], ds);
-        if (ds < 4) half_exp_slice(h0, ds, st.scale_l2, ms);
+        if (BODY == BODY_ONLINE && ds == 0) {
+            alpha = half_online_ref(h0, st.m_run, st.scale_l2, resc);
+            ms = (st.m_run == kNegInf ? 0.0f : st.m_run) * st.scale_l2;
+        }
+        if (BODY == BODY_ONLINE ? (ds >= 1 && ds <= 4) : ds < 4)
+            half_exp_slice(h0, BODY == BODY_ONLINE ? ds - 1 : ds, st.scale_l2, ms);
         __builtin_amdgcn_sched_barrier(0);
     }
+    // Slices the loop had no step for (online body, fewer than 5 steps).
+#pragma unroll
+    for (int q = (BODY == BODY_ONLINE ? NDS - 1 : 4); q < 4; ++q) half_exp_slice(h0, q, st.scale_l2, ms);
     if (BODY == BODY_ONLINE && resc) {  // rare: the row max moved by more than 2^kLazy
         st.l_run *= alpha;
 #pragma unroll
         for (int d = 0; d < NDB; ++d) st.acc[d] *= alpha;
     }
-    // C: O^T += V^T P^T for keys 0..31 under the softmax of half 1.
+    // C: O^T += V^T P^T for keys 0..31 under the softmax of half 1 (its
+    // online reference settled under the first step, as above).
     if (masked) half_mask(h1, j0, 1, st.lo, st.hi);
     bool resc1 = false;
     float alpha1 = 1.0f;
-    if (BODY == BODY_ONLINE) {
-        alpha1 = half_online_ref(h1, st.m_run, st.scale_l2, resc1);
-        ms = (st.m_run == kNegInf ? 0.0f : st.m_run) * st.scale_l2;
-    }
 #pragma unroll
     for (int j = 0; j < 2 * NDB; ++j) {
         if (j + kPrefetch < 4 * NDB) vf[j + kPrefetch] = vfrag(j + kPrefetch);
         pv(vf[j], h0.pb[j / NDB], j % NDB);
-        if (j < 4) half_exp_slice(h1, j, st.scale_l2, ms);
+        if (BODY == BODY_ONLINE && j == 0) {
+            alpha1 = half_online_ref(h1, st.m_run, st.scale_l2, resc1);
+            ms = (st.m_run == kNegInf ? 0.0f : st.m_run) * st.scale_l2;
+        }
+        if (BODY == BODY_ONLINE ? (j >= 1 && j <= 4) : j < 4)
+            half_exp_slice(h1, BODY == BODY_ONLINE ? j - 1 : j, st.scale_l2, ms);
         __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int q = (BODY == BODY_ONLINE ? 2 * NDB - 1 : 4); q < 4; ++q) half_exp_slice(h1, q, st.scale_l2, ms);
     if (BODY == BODY_ONLINE && resc1) {
         st.l_run = (st.l_run + h0.rs) * alpha1;
         h0.rs = 0.0f;

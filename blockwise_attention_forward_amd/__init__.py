@@ -20,7 +20,7 @@ __all__ = [
     "BWA_TILE_SKIP", "BWA_TILE_FULL", "BWA_TILE_PARTIAL", "BwaError", "Mask", "BlockLists",
     "lib_path", "bwa_version", "bwa_status_string", "bwa_last_error", "bwa_attn_tile",
     "bwa_block_mask_size", "bwa_block_mask_build", "bwa_fixed_m_bound", "bwa_attn_fwd",
-    "bwa_attn_fwd_carry", "bwa_lse_merge",
+    "bwa_attn_fwd_carry", "bwa_attn_fwd_balanced", "bwa_attn_fwd_balanced_workspace", "bwa_lse_merge",
 ]
 
 BWA_F32, BWA_BF16 = 0, 1
@@ -77,6 +77,8 @@ def _load():
         "bwa_fixed_m_bound": (I32, [TP, TP, I32, P, I32, I64P, I64, F32, F32, P, P, P, P, P]),
         "bwa_attn_fwd": (I32, [TP, TP, TP, MP, BP, F32, I32, P, P, TP, P, P]),
         "bwa_attn_fwd_carry": (I32, [TP, TP, TP, MP, BP, F32, I32, P, P, TP, P, TP, P, P]),
+        "bwa_attn_fwd_balanced": (I32, [TP, TP, TP, MP, BP, F32, I32, P, P, I32, P, I64, TP, P, P]),
+        "bwa_attn_fwd_balanced_workspace": (I32, [I32, I64, I64, I64, I64, I64, I32, I64P, I64P, I32P]),
         "bwa_lse_merge": (I32, [I32, TP, ctypes.POINTER(ctypes.c_void_p), TP, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -282,6 +284,46 @@ def bwa_attn_fwd_carry(q, k, v, o_prev, lse_prev, mask=None, blocks=None, scale=
                                    bs, float(scale), int(mode), _ptr(m), _ptr(gate), ctypes.byref(pt),
                                    _ptr(lse_prev), ctypes.byref(ot), _ptr(lse), _stream(q.device)),
            "bwa_attn_fwd_carry")
+    return o, lse
+
+
+def bwa_attn_fwd_balanced_workspace(dtype, B, H, Lq, Lk, D, n_cus=0, plan=False):
+    """Workspace bytes of bwa_attn_fwd_balanced (dtype: BWA_BF16 or a torch
+    dtype); with plan=True, (bytes, cut_blocks, pieces)."""
+    if isinstance(dtype, torch.dtype):
+        dtype = BWA_BF16 if dtype == torch.bfloat16 else BWA_F32
+    n, cut, pieces = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+    _check(_lib.bwa_attn_fwd_balanced_workspace(int(dtype), int(B), int(H), int(Lq), int(Lk), int(D), int(n_cus),
+                                                ctypes.byref(n), ctypes.byref(cut), ctypes.byref(pieces)),
+           "bwa_attn_fwd_balanced_workspace")
+    return (n.value, cut.value, pieces.value) if plan else n.value
+
+
+def bwa_attn_fwd_balanced(q, k, v, mask=None, blocks=None, scale=None, mode=BWA_MODE_ONLINE, m=None, gate=None,
+                          n_cus=0, workspace=None, o=None, lse=None, out_dtype=None):
+    """bwa_attn_fwd with one workgroup per compute unit taking whole query
+    blocks and then pieces of the last ones from a queue (bf16 inputs).
+    workspace: a uint8 device tensor of at least
+    bwa_attn_fwd_balanced_workspace bytes (allocated here if None).
+    Returns (o, lse)."""
+    B, Lq, H, D = q.shape
+    if scale is None:
+        scale = D ** -0.5
+    if o is None:
+        o = torch.empty(B, Lq, H, D, dtype=out_dtype or q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, H, Lq, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = bwa_attn_fwd_balanced_workspace(_dtype_code(q), B, H, Lq, k.shape[1], D, n_cus)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
+    mk = Mask.of(mask, q.device)
+    qt, kt, vt, ot = _tensor(q), _tensor(k), _tensor(v), _tensor(o)
+    bs = ctypes.byref(blocks.struct) if blocks is not None else None
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(_lib.bwa_attn_fwd_balanced(ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt),
+                                      ctypes.byref(mk.struct), bs, float(scale), int(mode), _ptr(m), _ptr(gate),
+                                      int(n_cus), _ptr(workspace), nbytes, ctypes.byref(ot),
+                                      _ptr(lse), _stream(q.device)), "bwa_attn_fwd_balanced")
     return o, lse
 
 

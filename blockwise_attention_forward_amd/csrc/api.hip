@@ -224,10 +224,36 @@ int32_t bwa_fixed_m_bound(const bwa_tensor* q, const bwa_tensor* k_chunks, int32
     return hip_status(bwa::launch_fixed_m_bound(a, (hipStream_t)stream), "fixed_m_bound launch");
 }
 
+// Balanced launch request: workgroups (one per compute unit, resolved) and workspace.
+struct Balance {
+    int32_t n_cus;
+    void* ws;
+    int64_t ws_bytes;
+};
+
+static constexpr int32_t kMaxPlannedCus = 1 << 16;
+
+// Compute units of the current device (the balanced launch's default).
+static int32_t device_cus(int32_t* n) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail(BWA_ERR_HIP, "compute unit count: %s", hipGetErrorString(e));
+    return BWA_OK;
+}
+
+static int32_t resolve_cus(int32_t n_cus, int32_t* out) {
+    if (n_cus > kMaxPlannedCus) return fail(BWA_ERR_UNSUPPORTED, "n_cus %d > %d", n_cus, kMaxPlannedCus);
+    int32_t st;
+    if (n_cus <= 0 && (st = device_cus(&n_cus))) return st;
+    *out = n_cus;
+    return BWA_OK;
+}
+
 static int32_t attn_fwd_impl(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v, const bwa_mask* mask,
                              const bwa_blocks* blocks, float scale, int32_t mode, const float* m,
                              const uint8_t* gate, const bwa_tensor* o_prev, const float* lse_prev, bwa_tensor* o,
-                             float* lse, void* stream) {
+                             float* lse, void* stream, const Balance* bal = nullptr) {
     int32_t st;
     if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
         (st = check_tensor(o, "o")))
@@ -306,6 +332,20 @@ static int32_t attn_fwd_impl(const bwa_tensor* q, const bwa_tensor* k, const bwa
         a.op_sB = o_prev->sB; a.op_sL = o_prev->sL; a.op_sH = o_prev->sH;
         a.lse_prev = rows > 0 ? lse_prev : nullptr;
     }
+    if (bal) {
+        if (q->dtype != BWA_BF16) return fail(BWA_ERR_UNSUPPORTED, "the balanced launch computes bf16 inputs only");
+        const i64 units = B * H * a.n_qblocks;
+        const bwa::SplitPlan sp = bwa::split_plan(units, bal->n_cus, Lk);
+        const i64 need = bwa::split_workspace_bytes(sp, bq, (int)q->D);
+        if (units > 0) {
+            if (!bal->ws) return fail(BWA_ERR_NULL_ARG, "workspace is NULL");
+            if ((uintptr_t)bal->ws % 256) return fail(BWA_ERR_BAD_STRIDE, "workspace not 256-byte aligned");
+            if (bal->ws_bytes < need)
+                return fail(BWA_ERR_CAPACITY, "workspace of %lld bytes; %lld needed", (long long)bal->ws_bytes,
+                            (long long)need);
+            bwa::split_workspace_layout(a, bal->ws, sp, bq, (int)q->D);
+        }
+    }
     return hip_status(bwa::launch_attn_fwd(a, (hipStream_t)stream), "attn_fwd launch");
 }
 
@@ -321,6 +361,33 @@ int32_t bwa_attn_fwd_carry(const bwa_tensor* q, const bwa_tensor* k, const bwa_t
                            float* lse, void* stream) {
     if (!o_prev) return fail(BWA_ERR_NULL_ARG, "o_prev is NULL");
     return attn_fwd_impl(q, k, v, mask, blocks, scale, mode, m, gate, o_prev, lse_prev, o, lse, stream);
+}
+
+int32_t bwa_attn_fwd_balanced_workspace(int32_t dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                                        int32_t n_cus, int64_t* bytes, int64_t* cut_blocks, int32_t* pieces) {
+    if (!bytes) return fail(BWA_ERR_NULL_ARG, "bytes output is NULL");
+    if (B < 0 || H < 0 || Lq < 0 || Lk < 0) return fail(BWA_ERR_BAD_SHAPE, "negative size");
+    int32_t bq, bkv, st;
+    if ((st = bwa_attn_tile(dtype, D, &bq, &bkv))) return st;
+    if ((st = resolve_cus(n_cus, &n_cus))) return st;
+    const i64 units = B * H * ((Lq + bq - 1) / bq);
+    const bwa::SplitPlan sp = bwa::split_plan(units, n_cus, Lk);
+    *bytes = units > 0 ? bwa::split_workspace_bytes(sp, bq, (int)D) : 0;
+    if (cut_blocks) *cut_blocks = units > 0 ? sp.tail : 0;
+    if (pieces) *pieces = sp.s;
+    return ok();
+}
+
+int32_t bwa_attn_fwd_balanced(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v, const bwa_mask* mask,
+                              const bwa_blocks* blocks, float scale, int32_t mode, const float* m,
+                              const uint8_t* gate, int32_t n_cus, void* workspace, int64_t workspace_bytes,
+                              bwa_tensor* o, float* lse, void* stream) {
+    Balance bal;
+    int32_t st;
+    if ((st = resolve_cus(n_cus, &bal.n_cus))) return st;
+    bal.ws = workspace;
+    bal.ws_bytes = workspace_bytes;
+    return attn_fwd_impl(q, k, v, mask, blocks, scale, mode, m, gate, nullptr, nullptr, o, lse, stream, &bal);
 }
 
 int32_t bwa_lse_merge(int32_t n_parts, const bwa_tensor* o_parts, const float* const* lse_parts,

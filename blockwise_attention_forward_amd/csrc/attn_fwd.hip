@@ -39,6 +39,8 @@
 // Exponentials use the hardware base-2 exponential with log2(e) folded into
 // the scale; LSE is returned in natural-log units.
 
+#include <algorithm>
+
 #include "internal.h"
 
 namespace bwa {
@@ -117,7 +119,8 @@ template <int TILE>
 struct Cursor {
     int r = -1, j0 = 0, ke = 0, kind = 0;
     // Advance to the next tile; false when the walk is over.
-    __device__ inline bool next(const Walk& w) {
+    template <class W>
+    __device__ inline bool next(const W& w) {
         j0 += TILE;
         while (j0 >= ke) {
             if (++r >= w.nruns) return false;
@@ -129,6 +132,63 @@ struct Cursor {
     }
     __device__ inline bool masked(int Lk) const { return kind != BWA_TILE_FULL || j0 + TILE > Lk; }
 };
+
+// Tiles of a walk (the count the kernel's cursor visits).
+__device__ inline i64 walk_tiles(const Walk& w, int tile) {
+    i64 n = 0;
+    for (int r = 0; r < w.nruns; ++r) {
+        int kb, ke, kind;
+        w.get(r, kb, ke, kind);
+        if (ke > kb) n += (ke - kb + tile - 1) / tile;
+    }
+    return n;
+}
+
+// A walk cut down to its tiles [t0, t1): the runs from roff on, each run
+// clamped to key positions [cb, ce).  Runs are increasing and disjoint, so
+// the clamp only changes the first and the last; tiles keep the positions
+// they have in the whole walk.
+struct ClipWalk {
+    Walk w;
+    int nruns, Lk, roff, cb, ce;
+
+    __device__ inline void get(int r, int& kb, int& ke, int& kind) const {
+        w.get(r + roff, kb, ke, kind);
+        kb = max(kb, cb);
+        ke = min(ke, ce);
+    }
+};
+
+template <int TILE>
+__device__ inline ClipWalk clip_walk(const Walk& w, i64 t0, i64 t1) {
+    ClipWalk c;
+    c.w = w;
+    c.Lk = w.Lk;
+    c.roff = 0;
+    c.cb = -0x7fffffff;
+    c.ce = 0x7fffffff;
+    c.nruns = 0;
+    int first = -1;
+    i64 t = 0;
+    for (int r = 0; r < w.nruns && t0 < t1; ++r) {
+        int kb, ke, kind;
+        w.get(r, kb, ke, kind);
+        const i64 n = ke > kb ? (ke - kb + TILE - 1) / TILE : 0;
+        if (n == 0) continue;
+        if (first < 0 && t0 < t + n) {
+            first = r;
+            c.cb = kb + (int)(t0 - t) * TILE;
+        }
+        if (first >= 0 && t1 <= t + n) {
+            c.ce = kb + (int)(t1 - t) * TILE;
+            c.roff = first;
+            c.nruns = r - first + 1;
+            break;
+        }
+        t += n;
+    }
+    return c;
+}
 
 template <int NT>
 __device__ inline void block_reduce4(int& mn_lo, int& mx_hi, int& mx_lo, int& mn_hi, int* red) {
@@ -261,59 +321,79 @@ __device__ inline void fixed_update(f32x16 (&s)[NKB], float& l_run, float scale_
     l_run += rs;
 }
 
-// Epilogue: O = acc / l, LSE = ln-sum-exp; rows that saw nothing -> 0, -inf.
+// Epilogue of one query row (the lane pair l, l + 32 holds it): this call's
+// partial is O = acc / l and LSE = reference + ln l (natural-log units).  With
+// a previous partial of other key chunks (prev_o != nullptr) the two merge in
+// LSE space ("Fixed-m softmax for 2D-ring x Ulysses attention (WAN 2.2)",
+// Notes): lse = ln(e^lse + e^lse_prev), O = e^(lse-lse') O + e^(lse_prev-lse')
+// O_prev; a side whose LSE is -inf has weight 0 and its O row is not read.
+// o_row points at the row's first element (OUT decides fp32 or bf16); lse_at
+// is written by the lane with hb == 0.
 template <int D, int OUT, int BODY>
-__device__ inline void store_out(const AttnLaunch& p, f32x16 (&acc)[D / 32], float m_run, float l_run,
-                                 float m_fixed, i64 b, i64 h, i64 row) {
+__device__ inline void store_rows(const AttnLaunch& p, f32x16 (&acc)[D / 32], float m_run, float l_run,
+                                  float m_fixed, bool row_ok, void* o_row, float* lse_at, const float* prev_o,
+                                  const float* prev_lse) {
     const int hb = (threadIdx.x >> 5) & 1;
     const float l = pair_sum(l_run);
-    if (row >= p.Lq) return;
+    if (!row_ok) return;
     const bool any = l > 0.0f;
-    // This call's partial: O = acc / l, LSE = reference + ln l (natural-log units).
     float lse = any ? (BODY == BODY_FIXED ? m_fixed : m_run * p.scale) + __logf(l) : kNegInf;
-    float w_cur = any ? 1.0f / l : 0.0f, w_prev = 0.0f;
-    const i64 li = (b * p.H + h) * p.Lq + row;
-    if (p.lse_prev) {
-        // Carried partial of earlier key chunks ("Fixed-m softmax for 2D-ring x
-        // Ulysses attention (WAN 2.2)", Notes: hop partials combine in LSE
-        // space): lse = ln(e^lse + e^lse_prev), O = e^(lse_cur-lse) O_cur +
-        // e^(lse_prev-lse) O_prev.  A side whose LSE is -inf has weight 0.
-        const float lp = p.lse_prev[li];
+    const float w_own = any ? 1.0f / l : 0.0f;  // normalizes this call's partial
+    float w_cur = 1.0f, w_prev = 0.0f;
+    if (prev_o) {
+        const float lp = *prev_lse;
         const float mx = fmaxf(lse, lp);
         if (mx != kNegInf) {  // once per row: the accurate exp and log
             const float ec = any ? expf(lse - mx) : 0.0f;
             const float ep = lp != kNegInf ? expf(lp - mx) : 0.0f;
             const float tot = ec + ep;
-            w_cur *= ec / tot;
+            w_cur = ec / tot;
             w_prev = ep / tot;
             lse = mx + logf(tot);
         }
     }
-    const i64 base = b * p.o_sB + row * p.o_sL + h * p.o_sH;
-    const i64 pbase = b * p.op_sB + row * p.op_sL + h * p.op_sH;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int d = db * 32 + 8 * g + hb * 4;
-            float o0 = acc[db][4 * g] * w_cur, o1 = acc[db][4 * g + 1] * w_cur;
-            float o2 = acc[db][4 * g + 2] * w_cur, o3 = acc[db][4 * g + 3] * w_cur;
-            if (w_prev != 0.0f) {
-                const f32x4 pv = *(const f32x4*)(p.o_prev + pbase + d);
-                o0 += w_prev * pv[0];
-                o1 += w_prev * pv[1];
-                o2 += w_prev * pv[2];
-                o3 += w_prev * pv[3];
+            float o0 = acc[db][4 * g] * w_own, o1 = acc[db][4 * g + 1] * w_own;
+            float o2 = acc[db][4 * g + 2] * w_own, o3 = acc[db][4 * g + 3] * w_own;
+            if (prev_o) {
+                // Normalized sides, each product rounded, one add: the same
+                // bits whichever side is this call's (both sides of a split
+                // unit store their normalized partial as fl(acc * w_own)).
+#pragma clang fp contract(off)
+                f32x4 pv = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (w_prev != 0.0f) pv = *(const f32x4*)(prev_o + d);
+                o0 = o0 * w_cur + w_prev * pv[0];
+                o1 = o1 * w_cur + w_prev * pv[1];
+                o2 = o2 * w_cur + w_prev * pv[2];
+                o3 = o3 * w_cur + w_prev * pv[3];
             }
             if (OUT == BWA_F32) {
                 f32x4 v = {o0, o1, o2, o3};
-                *(f32x4*)((float*)p.o + base + d) = v;
+                *(f32x4*)((float*)o_row + d) = v;
             } else {
                 uint2 v = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-                *(uint2*)((__bf16*)p.o + base + d) = v;
+                *(uint2*)((__bf16*)o_row + d) = v;
             }
         }
-    if (hb == 0) p.lse[li] = lse;
+    if (hb == 0) *lse_at = lse;
+}
+
+// The call's own outputs, merged with the caller's carried partial if any.
+template <int D, int OUT, int BODY>
+__device__ inline void store_out(const AttnLaunch& p, f32x16 (&acc)[D / 32], float m_run, float l_run,
+                                 float m_fixed, i64 b, i64 h, i64 row) {
+    const bool row_ok = row < p.Lq;
+    const i64 r = row_ok ? row : 0;
+    const i64 li = (b * p.H + h) * p.Lq + r;
+    void* o_row = OUT == BWA_F32 ? (void*)((float*)p.o + b * p.o_sB + r * p.o_sL + h * p.o_sH)
+                                 : (void*)((__bf16*)p.o + b * p.o_sB + r * p.o_sL + h * p.o_sH);
+    const float* prev_o = p.lse_prev ? p.o_prev + b * p.op_sB + r * p.op_sL + h * p.op_sH : nullptr;
+    store_rows<D, OUT, BODY>(p, acc, m_run, l_run, m_fixed, row_ok, o_row, p.lse + li, prev_o,
+                             p.lse_prev ? p.lse_prev + li : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -601,9 +681,9 @@ struct Ring {
     uint8_t* v[C::NBUF];
 };
 
-template <int D, int NW, int BODY, int I>
+template <int D, int NW, int BODY, int I, class W>
 __device__ __attribute__((always_inline)) inline bool bf16_step(const AttnLaunch& p, Bf16State<D, NW>& st,
-                                                               const Walk& walk, const Ring<D, NW>& ring,
+                                                               const W& walk, const Ring<D, NW>& ring,
                                                                Cursor<64>& cur, Cursor<64>& ahead, bool& more,
                                                                int& n_after, const __bf16* kbase,
                                                                const __bf16* vbase, int kv_lim) {
@@ -628,9 +708,10 @@ __device__ __attribute__((always_inline)) inline bool bf16_step(const AttnLaunch
     return have;
 }
 
-template <int D, int NW, int BODY, int OUT>
-__device__ inline void bf16_run(const AttnLaunch& p, Bf16State<D, NW>& st, const Walk& walk,
-                                const Ring<D, NW>& ring, i64 b, i64 h, i64 row) {
+// Every tile of the walk, accumulated into st; the caller stores the result.
+template <int D, int NW, int BODY, class W>
+__device__ inline void bf16_walk(const AttnLaunch& p, Bf16State<D, NW>& st, const W& walk,
+                                 const Ring<D, NW>& ring, i64 b, i64 h) {
     using C = Bf16Cfg<D, NW>;
     constexpr int NB = C::NBUF;
     static_assert(NB == 2 || NB == 3, "ring of 2 or 3 buffers");
@@ -662,6 +743,12 @@ __device__ inline void bf16_run(const AttnLaunch& p, Bf16State<D, NW>& st, const
                                                   kv_lim);
         }
     }
+}
+
+template <int D, int NW, int BODY, int OUT>
+__device__ inline void bf16_run(const AttnLaunch& p, Bf16State<D, NW>& st, const Walk& walk,
+                                const Ring<D, NW>& ring, i64 b, i64 h, i64 row) {
+    bf16_walk<D, NW, BODY>(p, st, walk, ring, b, h);
     store_out<D, OUT, BODY>(p, st.acc, st.m_run, st.l_run, st.m_fixed, b, h, row);
 }
 
@@ -732,6 +819,214 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_bf16(const 
     } else {
         bf16_run<D, NW, MODE, OUT>(p, st, walk, ring, b, h, row);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Balanced launch.  The plain launch runs one workgroup per query block and
+// the device deals workgroups to its 8 XCDs round-robin, so each XCD gets an
+// equal, contiguous share of blocks (the remap above) and runs it in rounds
+// of one block per compute unit.  XCDs do not run at the same speed, and a
+// share that is not a multiple of the XCD's units leaves a last, partial
+// round, so units idle at the end.  Here one workgroup per compute unit
+// loops over queues, one per XCD, of the same shares (so blocks that share a
+// head's keys still run together on one XCD's L2): first the share's whole
+// blocks, then the blocks of its last partial round cut along their key
+// tiles into s pieces each (piece index first, so the pieces running at one
+// time stream the same key range).  A workgroup whose queue is empty takes
+// items from the next XCD's queue, so fast XCDs take over the slow ones'
+// work.  A piece stores its normalized partial and LSE in the workspace; a
+// second kernel merges the s partials of each cut block in LSE space, in
+// piece order ("Fixed-m softmax for 2D-ring x Ulysses attention (WAN 2.2)",
+// Notes: the combine of partials over disjoint key ranges).  Workgroups
+// never wait for each other, and the kernel boundary orders the partials
+// before the merge.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void zero_ints_kernel(int* p, i64 n) {
+    const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+// Query block u (launch order) skipped by this call (gate and mode).
+__device__ inline bool unit_skipped(const AttnLaunch& p, i64 bh) {
+    if (!p.gate || p.mode == BWA_MODE_GATED) return false;
+    return (p.gate[bh] != 0) != (p.mode == BWA_MODE_FIXED_M);
+}
+
+// One item: query block u whole (piece < 0: final output), or piece 'piece'
+// of cut block k (partial into the workspace).
+template <int D, int NW, int MODE, int OUT>
+__device__ inline void bal_item(const AttnLaunch& p, const Ring<D, NW>& ring, int* red, i64 u, int piece, i64 k) {
+    using C = Bf16Cfg<D, NW>;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int l32 = lane & 31, hb = lane >> 5;
+    const i64 bh = u / p.n_qblocks;
+    const i64 qb = p.n_qblocks - 1 - (u % p.n_qblocks);
+    const i64 b = bh / p.H, h = bh % p.H;
+    if (unit_skipped(p, bh)) return;
+    const bool fixed = MODE == MODE_GATED ? (p.gate && p.gate[bh] != 0) : MODE == BODY_FIXED;
+
+    Bf16State<D, NW> st;
+    const i64 row = qb * C::BQ + wave * 32 + l32;
+    const bool row_ok = row < p.Lq;
+    int lo = 0, hi = 0;
+    if (row_ok) {
+        if (p.have_blocks) {
+            const i64 lb = p.list_batch == 1 ? 0 : b;
+            lo = p.row_lo[lb * p.Lq + row];
+            hi = p.row_hi[lb * p.Lq + row];
+        } else {
+            row_interval(p.mask, b, row, lo, hi);
+        }
+    }
+    st.lo = lo;
+    st.hi = hi;
+    const __bf16* qp = (const __bf16*)p.q + b * p.q_sB + row * p.q_sL + h * p.q_sH;
+#pragma unroll
+    for (int ds = 0; ds < C::NDS; ++ds)
+        st.qf[ds] = row_ok ? *(const uint4*)(qp + ds * 16 + hb * 8) : uint4{0, 0, 0, 0};
+#pragma unroll
+    for (int d = 0; d < C::NDB; ++d) st.acc[d] = f32x16{};
+    st.m_run = kNegInf;
+    st.l_run = 0.0f;
+    st.m_fixed = 0.0f;
+    st.m_l2 = 0.0f;
+    if (fixed && row_ok) {
+        st.m_fixed = p.m[bh * p.Lq + row];
+        st.m_l2 = st.m_fixed * kLog2e;
+    }
+    st.scale_l2 = p.scale * kLog2e;
+    const bool ne = row_ok && lo < hi;
+    const Walk walk = make_walk<C::TILE, C::NT>(p, b, qb, ne ? lo : 0x7fffffff, ne ? hi : 0,
+                                                row_ok ? (ne ? lo : 0x7fffffff) : 0,
+                                                row_ok ? (ne ? hi : -1) : 0x7fffffff, red);
+    auto finish = [&](auto body_tag) {
+        constexpr int BODY = decltype(body_tag)::value;
+        const i64 n = walk_tiles(walk, C::TILE);
+        const int s = piece < 0 ? 1 : p.split_s;
+        const int c = piece < 0 ? 0 : piece;
+        bf16_walk<D, NW, BODY>(p, st, clip_walk<C::TILE>(walk, c * n / s, (c + 1) * n / s), ring, b, h);
+        if (piece < 0) {
+            store_out<D, OUT, BODY>(p, st.acc, st.m_run, st.l_run, st.m_fixed, b, h, row);
+        } else {
+            const i64 slot = k * s + piece;
+            const int rib = wave * 32 + l32;
+            store_rows<D, BWA_F32, BODY>(p, st.acc, st.m_run, st.l_run, st.m_fixed, row_ok,
+                                         p.split_o + (slot * C::BQ + rib) * D, p.split_lse + slot * C::BQ + rib,
+                                         nullptr, nullptr);
+        }
+    };
+    if (MODE == MODE_GATED ? fixed : MODE == BODY_FIXED) finish(std::integral_constant<int, BODY_FIXED>{});
+    else finish(std::integral_constant<int, BODY_ONLINE>{});
+}
+
+template <int D, int NW, int MODE, int OUT>
+__global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_bal(const AttnLaunch p) {
+    using C = Bf16Cfg<D, NW>;
+    __shared__ __attribute__((aligned(1024))) uint8_t k0[C::TILE_BYTES], v0[C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t k1[C::TILE_BYTES], v1[C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t k2[C::NBUF == 3 ? C::TILE_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t v2[C::NBUF == 3 ? C::TILE_BYTES : 16];
+    Ring<D, NW> ring;
+    ring.k[0] = k0; ring.v[0] = v0; ring.k[1] = k1; ring.v[1] = v1;
+    if (C::NBUF == 3) { ring.k[C::NBUF - 1] = k2; ring.v[C::NBUF - 1] = v2; }
+    __shared__ int red[4 * NW];
+    __shared__ i64 s_unit, s_k;
+    __shared__ int s_piece;
+
+    const i64 U = (i64)p.B * p.H * p.n_qblocks;
+    const int s = p.split_s;
+    int xq = blockIdx.x & 7;  // this workgroup's XCD: its own queue first
+    for (;;) {
+        // Every wave is done with the previous item's tile buffers and flags.
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            i64 unit = -1, k = 0;
+            int piece = -1;
+            // The next item of queue xq; an empty queue stays empty, so move
+            // on to the next one (taking work of another XCD) until all are.
+            for (int tries = 0; tries < 8; ++tries, xq = (xq + 1) & 7) {
+                const SplitShare sh = split_share(U, p.split_c, s, xq);
+                const i64 i = (i64)atomicAdd(p.split_next + xq, 1ull);
+                if (i < sh.d) {
+                    unit = sh.a + i;
+                    break;
+                }
+                if (i < sh.d + sh.t * s) {
+                    const i64 pc = i - sh.d, j = pc % sh.t;
+                    unit = sh.a + sh.d + j;
+                    piece = (int)(pc / sh.t);
+                    k = sh.k0 + j;
+                    break;
+                }
+            }
+            s_unit = unit;
+            s_piece = piece;
+            s_k = k;
+        }
+        __syncthreads();
+        const i64 unit = s_unit;
+        if (unit < 0) break;
+        bal_item<D, NW, MODE, OUT>(p, ring, red, unit, s_piece, s_k);
+    }
+}
+
+// Merge of the s piece partials of cut block k (one workgroup each) into the
+// output rows, in piece order.  Two threads per row, each over half of D.
+template <int D, int NW, int OUT>
+__global__ __launch_bounds__(NW * 64) void merge_pieces_kernel(const AttnLaunch p) {
+    using C = Bf16Cfg<D, NW>;
+    constexpr int TPR = NW * 64 / C::BQ;  // threads per row
+    constexpr int NV = D / TPR / 4;       // float4 per thread
+    const i64 U = (i64)p.B * p.H * p.n_qblocks;
+    const i64 k = blockIdx.x;
+    int x = 0;
+    SplitShare sh = split_share(U, p.split_c, p.split_s, 0);
+    while (k >= sh.k0 + sh.t) sh = split_share(U, p.split_c, p.split_s, ++x);
+    const i64 u = sh.a + sh.d + (k - sh.k0);
+    const i64 bh = u / p.n_qblocks;
+    if (unit_skipped(p, bh)) return;
+    const i64 qb = p.n_qblocks - 1 - (u % p.n_qblocks);
+    const i64 b = bh / p.H, h = bh % p.H;
+    const int s = p.split_s;
+    const int tid = threadIdx.x, rib = tid / TPR, part = tid % TPR;
+    const i64 row = qb * C::BQ + rib;
+    if (row >= p.Lq) return;
+    const float* lse_k = p.split_lse + k * s * C::BQ + rib;
+    const float* o_k = p.split_o + (k * s * C::BQ + rib) * D + part * (D / TPR);
+    float mx = kNegInf;
+    for (int c = 0; c < s; ++c) mx = fmaxf(mx, lse_k[c * C::BQ]);
+    f32x4 acc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float lse = kNegInf;
+    if (mx != kNegInf) {
+        float tot = 0.0f;
+        for (int c = 0; c < s; ++c) {
+            const float lc = lse_k[c * C::BQ];
+            if (lc != kNegInf) tot += expf(lc - mx);
+        }
+        for (int c = 0; c < s; ++c) {
+            const float lc = lse_k[c * C::BQ];
+            if (lc == kNegInf) continue;  // an empty piece's O rows are not read
+            const float w = expf(lc - mx) / tot;
+            const f32x4* oc = (const f32x4*)(o_k + (i64)c * C::BQ * D);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) acc[i] += w * oc[i];
+        }
+        lse = mx + logf(tot);
+    }
+    const i64 off = b * p.o_sB + row * p.o_sL + h * p.o_sH + part * (D / TPR);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        if (OUT == BWA_F32) {
+            *(f32x4*)((float*)p.o + off + 4 * i) = acc[i];
+        } else {
+            uint2 v = {pack_bf16x2(acc[i][0], acc[i][1]), pack_bf16x2(acc[i][2], acc[i][3])};
+            *(uint2*)((__bf16*)p.o + off + 4 * i) = v;
+        }
+    }
+    if (part == 0) p.lse[(b * p.H + h) * p.Lq + row] = lse;
 }
 
 // ---------------------------------------------------------------------------
@@ -834,6 +1129,16 @@ template <int D, int MODE, int OUT>
 hipError_t launch_one(const AttnLaunch& a, hipStream_t stream) {
     const i64 grid = a.n_qblocks * (i64)a.B * a.H;
     if (grid == 0) return hipSuccess;
+    if (a.split_next) {
+        constexpr int NW = kBf16Waves;
+        hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(256), 0, stream, (int*)a.split_next, (i64)16);
+        hipLaunchKernelGGL((attn_fwd_bf16_bal<D, NW, MODE, OUT>), dim3((unsigned)a.split_wg), dim3(NW * 64), 0,
+                           stream, a);
+        if (a.split_tail > 0 && a.split_s > 1)
+            hipLaunchKernelGGL((merge_pieces_kernel<D, NW, OUT>), dim3((unsigned)a.split_tail), dim3(NW * 64), 0,
+                               stream, a);
+        return hipGetLastError();
+    }
     if (a.in_dtype == BWA_BF16) {
         constexpr int NW = kBf16Waves;
         hipLaunchKernelGGL((attn_fwd_bf16<D, NW, MODE, OUT>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, a);
@@ -857,6 +1162,41 @@ hipError_t launch_d(const AttnLaunch& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+static i64 pad256(i64 x) { return (x + 255) / 256 * 256; }
+
+SplitPlan split_plan(i64 units, int n_cus, i64 lk) {
+    SplitPlan sp;
+    sp.wg = n_cus;
+    sp.c = std::max(1, n_cus / 8);
+    // Pieces of about a quarter of a block, at least 8 tiles each; the cut
+    // blocks are each XCD's last, partial round.
+    const i64 tiles = std::max<i64>(1, (lk + 63) / 64);
+    sp.s = (int)std::max<i64>(1, std::min<i64>(std::min<i64>(kMaxSplit, 4), tiles / 8));
+    const SplitShare last = split_share(units, sp.c, sp.s, 7);
+    sp.tail = last.k0 + last.t;
+    return sp;
+}
+
+i64 split_workspace_bytes(const SplitPlan& sp, int rows_per_block, int D) {
+    const i64 parts = sp.tail * sp.s * rows_per_block;
+    return 256 + pad256(parts * 4) + parts * D * 4;
+}
+
+void split_workspace_layout(AttnLaunch& a, void* ws, const SplitPlan& sp, int rows_per_block, int D) {
+    uint8_t* base = (uint8_t*)ws;
+    const i64 parts = sp.tail * sp.s * rows_per_block;
+    a.split_next = (unsigned long long*)base;
+    base += 256;
+    a.split_lse = (float*)base;
+    base += pad256(parts * 4);
+    a.split_o = (float*)base;
+    a.split_s = sp.s;
+    a.split_c = sp.c;
+    a.split_tail = sp.tail;
+    a.split_wg = sp.wg;
+    (void)D;
+}
 
 int attn_rows_per_block(int dtype, int D) { return dtype == BWA_BF16 ? 32 * kBf16Waves : 128; }
 

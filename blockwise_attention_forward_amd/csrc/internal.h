@@ -91,6 +91,14 @@ struct AttnLaunch {
     // carried partial of earlier key chunks (lse_prev != nullptr): merged in the epilogue
     const float* o_prev; i64 op_sB, op_sL, op_sH;
     const float* lse_prev;
+    // balanced launch (split_next != nullptr): split_wg persistent workgroups
+    // take whole query blocks and pieces of cut blocks from 8 queues (see
+    // SplitShare), counters split_next[0..7]
+    unsigned long long* split_next;
+    int split_s, split_c, split_wg;
+    i64 split_tail;
+    float* split_lse;       // [split_tail][split_s][rows per block] piece LSEs
+    float* split_o;         // [split_tail][split_s][rows per block][D] piece outputs (normalized)
     // run lists (have_blocks != 0)
     int have_blocks;
     const i64* row_ptr; const int* run_begin; const int* run_end; const uint8_t* run_kind;
@@ -100,6 +108,41 @@ struct AttnLaunch {
     MaskDev mask;
 };
 hipError_t launch_attn_fwd(const AttnLaunch& a, hipStream_t stream);
+
+// Shares of the balanced launch: `units` query blocks (launch order) dealt to
+// the 8 XCDs in contiguous shares, as the plain launch's remap deals them.
+// Of XCD x's u blocks, the first d = floor(u / c) * c run whole (c compute
+// units per XCD); the t = u - d of the last, partial round are cut into s
+// pieces each (none when s == 1).  k0 numbers the cut blocks over all XCDs.
+struct SplitShare {
+    i64 a, d, t, k0;  // first block, whole blocks, cut blocks, first cut index
+};
+__host__ __device__ inline SplitShare split_share(i64 units, int c, int s, int x) {
+    const i64 q = units >> 3, r = units & 7;
+    SplitShare sh{0, 0, 0, 0};
+    for (int i = 0; i <= x; ++i) {
+        const i64 u = q + (i < r ? 1 : 0);
+        const i64 d = s > 1 ? (u / c) * c : u;
+        if (i == x) {
+            sh.a = i * q + (i < r ? i : r);
+            sh.d = d;
+            sh.t = u - d;
+        } else {
+            sh.k0 += u - d;
+        }
+    }
+    return sh;
+}
+// Plan for `units` blocks on n_cus compute units with keys of length lk:
+// workgroups, compute units per XCD, pieces per cut block, cut blocks.
+struct SplitPlan {
+    int wg, c, s;
+    i64 tail;
+};
+constexpr int kMaxSplit = 16;  // pieces per cut block at most
+SplitPlan split_plan(i64 units, int n_cus, i64 lk);
+i64 split_workspace_bytes(const SplitPlan& sp, int rows_per_block, int D);
+void split_workspace_layout(AttnLaunch& a, void* ws, const SplitPlan& sp, int rows_per_block, int D);
 int attn_rows_per_block(int dtype, int D);
 
 struct BlocksLaunch {

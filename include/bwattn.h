@@ -265,6 +265,63 @@ int32_t bwa_attn_fwd_carry(const bwa_tensor* q, const bwa_tensor* k, const bwa_t
                            bwa_tensor* o, float* lse, void* stream);
 
 /*
+ * bwa_attn_fwd with the work balanced over the compute units.  Computes the
+ * same O and LSE as bwa_attn_fwd (within rounding: see below).  The plain
+ * launch runs one workgroup per (b, h, query block); the device deals
+ * workgroups round-robin to its 8 XCDs, so each XCD runs an equal,
+ * contiguous share of the blocks in launch order (head-major, the last query
+ * block of a head first), in rounds of one block per compute unit.  XCDs do
+ * not run at the same speed, and a share that is not a multiple of the
+ * XCD's units leaves a last, partial round, so units idle at the end.  Here
+ * n_cus workgroups (one per compute unit) loop over 8 queues holding the
+ * same shares: first a share's whole rounds of blocks, then the blocks of
+ * its last partial round, each cut along its key tiles into `pieces` equal
+ * pieces; a workgroup whose queue is empty takes items from another XCD's.
+ * The pieces' partials (fp32, in the workspace) are merged in LSE space
+ * ([FIXEDM Notes]: the combine of partials over disjoint key ranges) by a
+ * second kernel, in piece order.  No workgroup waits for another.
+ *   - q, k, v must be BWA_BF16; every other argument, the outputs, gate and
+ *     mode behave as in bwa_attn_fwd (blocks may be NULL).
+ *   - n_cus: workgroups to launch (>= 1), normally the device's compute-unit
+ *     count, which <= 0 selects.  Any value gives a correct result.
+ *   - workspace: device memory of at least the bytes
+ *     bwa_attn_fwd_balanced_workspace reports for the same dtype, B, H, Lq,
+ *     Lk, D and n_cus, 256-byte aligned, owned by the caller.  The call
+ *     clears what it uses; calls that share a workspace must be ordered
+ *     (same stream), since a running call owns it.
+ *   - Rounding: whole blocks give bwa_attn_fwd's bits.  A cut block's rows
+ *     combine `pieces` partials, so they can differ from bwa_attn_fwd in the
+ *     last bits (in the online mode each piece also rounds its
+ *     probabilities to bf16 against its own running max); the result does
+ *     not depend on the order in which workgroups take items, so it is
+ *     deterministic for given sizes and n_cus.
+ * Errors as for bwa_attn_fwd, plus BWA_ERR_NULL_ARG (workspace NULL),
+ * BWA_ERR_UNSUPPORTED (fp32 inputs; n_cus > 65536), BWA_ERR_BAD_STRIDE
+ * (workspace alignment), BWA_ERR_CAPACITY (workspace too small).
+ */
+int32_t bwa_attn_fwd_balanced(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
+                              const bwa_mask* mask, const bwa_blocks* blocks, float scale,
+                              int32_t mode, const float* m, const uint8_t* gate,
+                              int32_t n_cus, void* workspace, int64_t workspace_bytes,
+                              bwa_tensor* o, float* lse, void* stream);
+
+/*
+ * Plan of bwa_attn_fwd_balanced for q of dtype/B/H/Lq/D, keys of length Lk
+ * and n_cus (<= 0: the current device's compute-unit count, which this call
+ * then queries).  Host outputs: *bytes, the workspace size (required);
+ * *cut_blocks, how many query blocks are cut, and *pieces, into how many
+ * pieces each (both optional, may be NULL).  With U blocks dealt to 8 shares
+ * of floor(U/8) or floor(U/8) + 1 (the first U mod 8 shares) and
+ * c = max(1, n_cus / 8), a share of u blocks cuts its last u mod c;
+ * pieces = min(4, floor(ceil(Lk / 64) / 8)), and nothing is cut when that is
+ * below 2.
+ * The workspace holds 256 bytes of queue counters plus
+ * cut_blocks * pieces * rows-per-block * (D + 1) * 4 bytes of partials.
+ */
+int32_t bwa_attn_fwd_balanced_workspace(int32_t dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                                        int32_t n_cus, int64_t* bytes, int64_t* cut_blocks, int32_t* pieces);
+
+/*
  * Log-sum-exp merge of attention partials over disjoint key chunks
  * [FIXEDM Notes: the fallback merge in LSE space, invariant to the overshoot]:
  *   lse[b,h,i] = ln sum_t exp(lse_t[b,h,i])            (-inf if all are -inf)

@@ -215,3 +215,57 @@ def test_attn_tile():
     assert bw.bwa_attn_tile(1, 128)[1] == 64 and bw.bwa_attn_tile(1, 128)[0] % 128 == 0 and bw.bwa_attn_tile(0, 128) == (128, 64)
     with pytest.raises(bw.BwaError):
         bw.bwa_attn_tile(1, 80)
+
+
+def test_balanced_workspace_size():
+    n, cut, pieces = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+    f = L.bwa_attn_fwd_balanced_workspace
+    # 8 query blocks of 256 rows, one per XCD share, on 64 workgroups (8 per
+    # XCD): each share's block is a partial round, cut in 2 pieces of a
+    # 16-tile walk; each piece keeps 256 rows x (D + 1) fp32 after the
+    # 256-byte queue counters
+    assert f(1, 1, 2, 1000, 1000, 128, 64, ctypes.byref(n), ctypes.byref(cut), ctypes.byref(pieces)) == 0
+    assert (cut.value, pieces.value) == (8, 2)
+    assert n.value == 256 + 8 * 2 * 256 * 4 + 8 * 2 * 256 * 128 * 4
+    # 64 blocks, 8 per share, on 48 workgroups (6 per XCD): 2 per share cut in 4
+    assert f(1, 2, 4, 2048, 4096, 64, 48, ctypes.byref(n), ctypes.byref(cut), ctypes.byref(pieces)) == 0
+    assert (cut.value, pieces.value) == (16, 4) and n.value == 256 + 16 * 4 * 256 * 4 + 16 * 4 * 256 * 64 * 4
+    # whole rounds only (one workgroup per XCD), or keys too short to cut: only the counters
+    assert f(1, 1, 2, 1000, 1000, 128, 8, ctypes.byref(n), ctypes.byref(cut), None) == 0
+    assert n.value == 256 and cut.value == 0
+    assert f(1, 1, 2, 1000, 400, 128, 64, ctypes.byref(n), ctypes.byref(cut), None) == 0
+    assert n.value == 256 and cut.value == 0
+    assert f(1, 1, 2, 1000, 1000, 128, 7, None, None, None) == 1
+    assert f(1, 1, 2, 1000, 1000, 96, 7, ctypes.byref(n), None, None) == 6
+    assert f(7, 1, 2, 1000, 1000, 128, 7, ctypes.byref(n), None, None) == 4
+    assert f(1, -1, 2, 1000, 1000, 128, 7, ctypes.byref(n), None, None) == 2
+    assert f(1, 1, 2, 1000, 1000, 128, (1 << 16) + 1, ctypes.byref(n), None, None) == 6
+
+
+def _bal_blocks(L=256, bq=256):
+    nqb = (L + bq - 1) // bq
+    return bw._Blocks(bq, 64, L, L, 1, nqb, 4 * nqb, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+
+
+def _bal(q, k, v, o, blocks, ws=0x100000, ws_bytes=1 << 30, n_cus=4):
+    # 2 query blocks on 4 workgroups: the workspace holds the queue counter
+    bs = ctypes.byref(blocks) if blocks is not None else None
+    return L.bwa_attn_fwd_balanced(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(_mask()), bs,
+                                   0.1, 0, None, None, n_cus, ws, ws_bytes, ctypes.byref(o), 0x20000, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ws=None), 1),                         # workspace is required
+    (dict(ws=0x100010), 3),                     # 256-byte alignment
+    (dict(ws_bytes=100), 7),                    # smaller than the queue counter
+    (dict(n_cus=(1 << 16) + 1), 6),
+])
+def test_balanced_argument_errors(kw, code):
+    assert _bal(_t(), _t(), _t(), _t(), _bal_blocks(), **kw) == code
+    assert bw.bwa_last_error() != ""
+
+
+def test_balanced_needs_bf16_inputs():
+    f32 = dict(dtype=0)
+    assert _bal(_t(**f32), _t(**f32), _t(**f32), _t(**f32), bw._Blocks(128, 64, 256, 256, 1, 2, 8, 0x1000,
+                0x1000, 0x1000, 0x1000, 0x1000, 0x1000)) == 6

@@ -1,6 +1,7 @@
 """Benchmark of the blockwise attention forward hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dit_share]
+                    [--launch auto|plain|balanced]
 
 Prints ONE JSON line.  A step is one pass of the whole hot path over one
 batch of synthetic input already resident in HBM.  The default workload is
@@ -18,6 +19,10 @@ value      = counted attention FLOPs per step / step time (TFLOP/s), FLOPs
 roofline   = the dominant kernel (the gated attention launch of one hop):
              algorithmic FLOPs per launch / its mean launch time (HIP events on
              the launch stream), against the bf16 dense matrix-core peak.
+launch     = plain (one workgroup per query block) or balanced (one
+             workgroup per compute unit over per-XCD queues, the last
+             partial round of blocks cut along the keys and merged by a
+             second kernel); auto takes balanced from 4 rounds of blocks up.
 cpu_baseline = the fp64 oracle timed on the host on a bounded sample of the
              same workload (rank 0, N = 1 only).
 measured_ceilings = what this device sustains, beside the published peaks: a
@@ -108,7 +113,24 @@ def _traffic(kernel_key):
     return rec.get("bytes_per_launch")
 
 
-def setup_dit_share(torch, bw, synth):
+def _launcher(torch, bw, launch, q, lk, units):
+    """The attention entry point for this workload: plain or balanced (with
+    its workspace allocated once), and a description for the JSON line."""
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if launch == "auto":
+        launch = "balanced" if units >= 4 * n_cus else "plain"
+    if launch == "plain":
+        return bw.bwa_attn_fwd, {"launch": "plain", "units": units}
+    B, Lq, H, D = q.shape
+    nbytes, cut, pieces = bw.bwa_attn_fwd_balanced_workspace(q.dtype, B, H, Lq, lk, D, plan=True)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+
+    def call(q, k, v, mask=None, blocks=None, **kw):
+        return bw.bwa_attn_fwd_balanced(q, k, v, mask, blocks=blocks, workspace=ws, **kw)
+    return call, {"launch": "balanced", "units": units, "workgroups": n_cus, "cut_units": cut, "pieces": pieces}
+
+
+def setup_dit_share(torch, bw, synth, launch="auto"):
     d = synth.make_dit_share("cuda")
     q, ks, vs = d["q"], d["k_chunks"], d["v_chunks"]
     B, Lq, H, D = q.shape
@@ -127,6 +149,7 @@ def setup_dit_share(torch, bw, synth):
     torch.cuda.synchronize()
     flops_hop = _counted_flops(count_lists, D, H, Lq, Lc)
     gate_host = None
+    attn, launch_info = _launcher(torch, bw, launch, q, Lc, B * H * ((Lq + bq - 1) // bq))
 
     def step(timer=None):
         for t, m in enumerate(masks):
@@ -137,8 +160,8 @@ def setup_dit_share(torch, bw, synth):
             timer.stop(tb)
         for t in range(len(ks)):
             tok = timer.start("hop") if timer else None
-            bw.bwa_attn_fwd(q, ks[t], vs[t], m=mm, mask=masks[t], blocks=blocks[t], scale=scale,
-                            mode=bw.BWA_MODE_GATED, gate=gate, o=o_parts[t], lse=l_parts[t])
+            attn(q, ks[t], vs[t], m=mm, mask=masks[t], blocks=blocks[t], scale=scale,
+                 mode=bw.BWA_MODE_GATED, gate=gate, o=o_parts[t], lse=l_parts[t])
             if timer:
                 timer.stop(tok)
         tm = timer.start("merge") if timer else None
@@ -169,14 +192,14 @@ def setup_dit_share(torch, bw, synth):
 
     def online_hop(timer):
         tok = timer.start("online_hop")
-        bw.bwa_attn_fwd(q, ks[0], vs[0], mask=masks[0], blocks=blocks[0], scale=scale,
-                        mode=bw.BWA_MODE_ONLINE, o=o_parts[0], lse=l_parts[0])
+        attn(q, ks[0], vs[0], mask=masks[0], blocks=blocks[0], scale=scale,
+             mode=bw.BWA_MODE_ONLINE, o=o_parts[0], lse=l_parts[0])
         timer.stop(tok)
         # every head through the branch-free fixed-m body (timing only: the
         # sink head's output from this launch is not used)
         tok = timer.start("fixed_hop")
-        bw.bwa_attn_fwd(q, ks[0], vs[0], mask=masks[0], blocks=blocks[0], scale=scale, m=bound_out[2],
-                        mode=bw.BWA_MODE_FIXED_M, o=o_parts[0], lse=l_parts[0])
+        attn(q, ks[0], vs[0], mask=masks[0], blocks=blocks[0], scale=scale, m=bound_out[2],
+             mode=bw.BWA_MODE_FIXED_M, o=o_parts[0], lse=l_parts[0])
         timer.stop(tok)
 
     step()
@@ -189,7 +212,7 @@ def setup_dit_share(torch, bw, synth):
                  "fixed-m (gate 106.5) with one sink head on online fallback in one gated launch per hop, "
                  "LSE merge to bf16",
         B=B, H=H, D=D, Lq=Lq, Lk_per_hop=Lc, hops=len(ks), heads_fixed_m=n_fixed,
-        sink_head=d["sink_head"])
+        sink_head=d["sink_head"], **launch_info)
     flops_step = flops_hop * len(ks)
     bytes_merge = (len(ks) * (B * Lq * H * D * 4 + B * H * Lq * 4) + B * Lq * H * D * 2 + B * H * Lq * 4)
     bytes_bound = (B * Lq * H * D * 2 + sum(B * k.shape[1] * H * D * 2 for k in ks) + B * H * Lq * 4 * 3)
@@ -211,10 +234,10 @@ def setup_dit_share(torch, bw, synth):
 
     return dict(step=step, step_carry=step_carry, online_hop=online_hop, flops_step=flops_step, flops_dominant=flops_hop,
                 dominant="hop", info=info, bytes_merge=bytes_merge, bytes_bound=bytes_bound,
-                sample_oracle=sample_oracle, hops=len(ks))
+                sample_oracle=sample_oracle, hops=len(ks), launch=launch_info["launch"])
 
 
-def setup_single(torch, bw, synth, name):
+def setup_single(torch, bw, synth, name, launch="auto"):
     """One attention call of a masked workload (run lists + attention)."""
     if name == "varlen":
         d = synth.make_varlen("cuda")
@@ -240,11 +263,12 @@ def setup_single(torch, bw, synth, name):
     lse = torch.empty(B, H, Lq, device="cuda")
     torch.cuda.synchronize()
     flops = _counted_flops(count_lists, D, H, Lq, Lk)
+    attn, launch_info = _launcher(torch, bw, launch, q, Lk, B * H * ((Lq + bq - 1) // bq))
 
     def step(timer=None):
         bw.bwa_block_mask_build(mask, B, Lq, Lk, bq, 128, out=blocks)
         tok = timer.start("hop") if timer else None
-        bw.bwa_attn_fwd(q, k, v, mask, blocks=blocks, scale=scale, o=o, lse=lse)
+        attn(q, k, v, mask, blocks=blocks, scale=scale, o=o, lse=lse)
         if timer:
             timer.stop(tok)
 
@@ -260,7 +284,7 @@ def setup_single(torch, bw, synth, name):
         fl = 4.0 * D * float(sum(max(0, int(hi[r]) - int(lo[r])) for r in rows))
         return fl, dt, f"head 0, {len(rows)} seeded query rows against their visible keys, fp64"
 
-    info = dict(workload=desc, B=B, H=H, D=D, Lq=Lq, Lk=Lk)
+    info = dict(workload=desc, B=B, H=H, D=D, Lq=Lq, Lk=Lk, **launch_info)
     return dict(step=step, flops_step=flops, flops_dominant=flops, dominant="hop", info=info,
                 sample_oracle=sample_oracle)
 
@@ -327,6 +351,8 @@ def main():
     ap.add_argument("--workload", default="dit_share",
                     choices=["dit_share", "varlen", "window", "long_causal", "long_causal_packed"],
                     help="dit_share (default) is the measured configuration; the others time one masked call")
+    ap.add_argument("--launch", default="auto", choices=["auto", "plain", "balanced"],
+                    help="attention launch; auto: balanced from 4 rounds of query blocks per compute unit up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 3 plain elementwise copies of MIB MiB (scale for HBM byte counters)")
@@ -353,7 +379,7 @@ def main():
         del src, dst
     if args.workload != "dit_share":
         return run_single(args, torch, bw, synth)
-    W = setup_dit_share(torch, bw, synth)
+    W = setup_dit_share(torch, bw, synth, args.launch)
     timer = Timer(torch)
     for _ in range(args.warmup):
         W["step"]()
@@ -426,7 +452,7 @@ def main():
         "ms_per_kv_hop": round(ms_hop, 4),
         "online_only_ms_per_kv_hop": round(ms_online_hop, 4),
         "fixed_m_all_heads_ms_per_kv_hop": round(ms_fixed_hop, 4),
-        "carried_hops": {"ms_per_step": round(ms_step_carry, 4),
+        "carried_hops": {"launch": "plain", "ms_per_step": round(ms_step_carry, 4),
                          "TFLOPs": round(W["flops_step"] / (ms_step_carry * 1e-3) / 1e12, 2),
                          "ms_hop0": round(t3.mean_ms("hop0"), 4),
                          "ms_carry_hop": round(t3.mean_ms("hop_carry"), 4)},
@@ -439,7 +465,8 @@ def main():
         "measured_ceilings": meas,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": _traffic("attn_fwd_bf16_gated")},
+                     "traffic": _traffic("attn_fwd_bf16_bal_gated" if W["launch"] == "balanced"
+                                         else "attn_fwd_bf16_gated")},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
@@ -447,7 +474,7 @@ def main():
 
 def run_single(args, torch, bw, synth):
     """A masked workload: one attention call per step (bf16 in and out)."""
-    W = setup_single(torch, bw, synth, args.workload)
+    W = setup_single(torch, bw, synth, args.workload, args.launch)
     timer = Timer(torch)
     for _ in range(args.warmup):
         W["step"]()

@@ -932,21 +932,22 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_bal(const AttnLaunch
     if (C::NBUF == 3) { ring.k[C::NBUF - 1] = k2; ring.v[C::NBUF - 1] = v2; }
     __shared__ int red[4 * NW];
     __shared__ i64 s_unit, s_k;
-    __shared__ int s_piece;
+    __shared__ int s_piece, s_xq;
 
-    const i64 U = (i64)p.B * p.H * p.n_qblocks;
-    const int s = p.split_s;
-    int xq = blockIdx.x & 7;  // this workgroup's XCD: its own queue first
+    if (threadIdx.x == 0) s_xq = blockIdx.x & 7;  // this workgroup's XCD: its own queue first
     for (;;) {
         // Every wave is done with the previous item's tile buffers and flags.
         __syncthreads();
         if (threadIdx.x == 0) {
+            const i64 U = (i64)p.B * p.H * p.n_qblocks;
+            const int s = p.split_s, c = p.split_c;
+            int xq = s_xq;
             i64 unit = -1, k = 0;
             int piece = -1;
             // The next item of queue xq; an empty queue stays empty, so move
             // on to the next one (taking work of another XCD) until all are.
             for (int tries = 0; tries < 8; ++tries, xq = (xq + 1) & 7) {
-                const SplitShare sh = split_share(U, p.split_c, s, xq);
+                const SplitShare sh = split_share(U, c, s, xq);
                 const i64 i = (i64)atomicAdd(p.split_next + xq, 1ull);
                 if (i < sh.d) {
                     unit = sh.a + i;
@@ -960,6 +961,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_bal(const AttnLaunch
                     break;
                 }
             }
+            s_xq = xq;
             s_unit = unit;
             s_piece = piece;
             s_k = k;

@@ -5,7 +5,8 @@ Workloads (synthetic stand-ins for the pages' models and data, see synth):
   * varlen   H3 packed request, cu_seqlens [0, 33002, 33024], 24 heads
   * window   causal bands W in {512, 1024, 2048} on 4096^2, 4096x8192, 8192^2
   * dit      one rank's share of ring2 x uly2 video-DiT attention (2 KV hops,
-             fixed-m with a sink head on online fallback, LSE merge)
+             fixed-m with a sink head on online fallback, LSE merge), with the
+             plain and the balanced launch (the bench's)
   * long     1,048,576-token causal attention, single segment and packed
 
 Large outputs are checked on a seeded sample of 512 query rows per head
@@ -122,17 +123,59 @@ def dit():
     return synth.make_dit_share(DEV)
 
 
-def _hops(d, mode, m=None, gate=None):
+def _hops(d, mode, m=None, gate=None, balanced=False, parts_out=None):
     q = d["q"]
     B, Lq, H, D = q.shape
     bq, _ = bw.bwa_attn_tile(BF16, D)
+    attn = bw.bwa_attn_fwd_balanced if balanced else bw.bwa_attn_fwd
     parts = []
     for k, v, off in zip(d["k_chunks"], d["v_chunks"], d["kv_offsets"]):
         mask = {"kv_offset": off}
         blocks = bw.bwa_block_mask_build(mask, B, Lq, k.shape[1], bq, 128)
-        parts.append(bw.bwa_attn_fwd(q, k, v, mask, blocks=blocks, scale=d["scale"], mode=mode, m=m, gate=gate,
-                                     out_dtype=torch.float32))
+        parts.append(attn(q, k, v, mask, blocks=blocks, scale=d["scale"], mode=mode, m=m, gate=gate,
+                          out_dtype=torch.float32))
+    if parts_out is not None:
+        parts_out.extend(parts)
     return bw.bwa_lse_merge([p[0] for p in parts], [p[1] for p in parts], out_dtype=BF16)
+
+
+def _cut_blocks(B, H, Lq, Lk, D):
+    """(b, h, first row, end row) of the query blocks the balanced launch cuts
+    on this device: per XCD share, the blocks past its last whole round."""
+    nbytes, cut, pieces = bw.bwa_attn_fwd_balanced_workspace(BF16, B, H, Lq, Lk, D, plan=True)
+    bq, _ = bw.bwa_attn_tile(BF16, D)
+    nqb = (Lq + bq - 1) // bq
+    U = B * H * nqb
+    c = max(1, torch.cuda.get_device_properties(0).multi_processor_count // 8)
+    q_, r_ = divmod(U, 8)
+    out = []
+    for x in range(8):
+        u = q_ + (1 if x < r_ else 0)
+        a = x * q_ + min(x, r_)
+        d = (u // c) * c if pieces > 1 else u
+        for unit in range(a + d, a + u):
+            bh, qb = unit // nqb, nqb - 1 - unit % nqb
+            out.append((bh // H, bh % H, qb * bq, min(Lq, (qb + 1) * bq)))
+    assert len(out) == cut
+    return out
+
+
+def _check_balanced_vs_plain(o_b, l_b, o_p, l_p, cut):
+    """Rows of whole blocks: the plain launch's bits.  Rows of cut blocks: one
+    LSE-space combine more, with probabilities rounded to bf16 against each
+    piece's own running max in the online body: bf16 rounding level of P."""
+    cut_rows = torch.zeros(l_p.shape, dtype=torch.bool, device=DEV)  # [B, H, L]
+    for b, h, r0, r1 in cut:
+        cut_rows[b, h, r0:r1] = True
+    assert cut_rows.any() and not cut_rows.all()
+    assert torch.equal(l_b[~cut_rows], l_p[~cut_rows])
+    oc = cut_rows.permute(0, 2, 1)
+    assert torch.equal(o_b[~oc], o_p[~oc])
+    fin = torch.isfinite(l_p) & cut_rows
+    assert torch.equal(torch.isneginf(l_b), torch.isneginf(l_p))
+    assert bool(((l_b[fin] - l_p[fin]).abs() <= 1e-5 + 1e-6 * l_p[fin].abs()).all())
+    err = (o_b[oc].float() - o_p[oc].float()).abs()
+    assert err.max().item() <= 4e-3 and err.mean().item() <= 3e-4, (err.max().item(), err.mean().item())
 
 
 def _dit_oracle(d, rows):
@@ -170,6 +213,43 @@ def test_dit_gated_and_online_hops(dit):
     o_ref, l_ref = _dit_oracle(dit, rows)
     assert_close(*gpu_rows(o_g, l_g, rows), o_ref, l_ref, BF16, "dit gated")
     assert_close(*gpu_rows(o_o, l_o, rows), o_ref, l_ref, BF16, "dit online")
+
+
+def test_dit_balanced_hops(dit):
+    # The bench's launch: each hop through the balanced launch (per-XCD queues,
+    # cut blocks of each XCD's last partial round), then the merge.  Sampled
+    # rows cover the cut blocks; whole blocks match the plain launch bit for bit.
+    q = dit["q"]
+    B, Lq, H, D = q.shape
+    Lc = dit["k_chunks"][0].shape[1]
+    kmax, mmax, m, gate = bw.bwa_fixed_m_bound(q, dit["k_chunks"], dit["scale"], 106.5)
+    cut = _cut_blocks(B, H, Lq, Lc, D)
+    parts_b, parts_p = [], []
+    o, l = _hops(dit, bw.BWA_MODE_GATED, m=m, gate=gate, balanced=True, parts_out=parts_b)
+    _hops(dit, bw.BWA_MODE_GATED, m=m, gate=gate, parts_out=parts_p)
+    for (ob, lb), (op, lp) in zip(parts_b, parts_p):
+        _check_balanced_vs_plain(ob, lb, op, lp, cut)
+    must = [0, Lq - 1] + sorted({r0 for _, _, r0, _ in cut} | {r1 - 1 for _, _, _, r1 in cut})[:24]
+    rows = synth.sample_rows(Lq, 512, seed=27, must=must)
+    o_ref, l_ref = _dit_oracle(dit, rows)
+    assert_close(*gpu_rows(o, l, rows), o_ref, l_ref, BF16, "dit balanced hops")
+
+
+def test_varlen_balanced():
+    w = synth.make_varlen(DEV)
+    q, k, v, mask, scale = w["q"], w["k"], w["v"], w["mask"], w["scale"]
+    B, L, H, D = q.shape
+    bq, _ = bw.bwa_attn_tile(BF16, D)
+    blocks = bw.bwa_block_mask_build(mask, 1, L, L, bq, 128)
+    cut = _cut_blocks(B, H, L, L, D)
+    o, l = bw.bwa_attn_fwd_balanced(q, k, v, mask, blocks=blocks, scale=scale)
+    o_p, l_p = bw.bwa_attn_fwd(q, k, v, mask, blocks=blocks, scale=scale)
+    _check_balanced_vs_plain(o, l, o_p, l_p, cut)
+    assert torch.all(o[:, 33002:] == 0) and torch.all(torch.isneginf(l[:, :, 33002:]))
+    must = [0, 33001, 33002, 33023] + sorted({r0 for _, _, r0, _ in cut} | {r1 - 1 for _, _, _, r1 in cut})[:24]
+    rows = synth.sample_rows(L, 512, seed=28, must=must)
+    o_ref, l_ref = oracle_attention(q, k, v, mask, scale, rows)
+    assert_close(*gpu_rows(o, l, rows), o_ref, l_ref, BF16, "varlen balanced")
 
 
 def _hops_carry(d, mode, m=None, gate=None):

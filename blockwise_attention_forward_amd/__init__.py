@@ -46,9 +46,10 @@ class _Tensor(ctypes.Structure):
 class _Mask(ctypes.Structure):
     _fields_ = [("causal", ctypes.c_int32), ("window", ctypes.c_int32), ("kv_offset", ctypes.c_int64),
                 ("q_valid", ctypes.c_int64), ("kv_valid", ctypes.c_int64),
-                ("num_segments", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("num_segments", ctypes.c_int32), ("dilation", ctypes.c_int32),
                 ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_kv", ctypes.c_void_p),
-                ("segment_ids_q", ctypes.c_void_p), ("segment_ids_kv", ctypes.c_void_p)]
+                ("segment_ids_q", ctypes.c_void_p), ("segment_ids_kv", ctypes.c_void_p),
+                ("prefix", ctypes.c_int64), ("documents", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class _Blocks(ctypes.Structure):
@@ -146,12 +147,14 @@ class Mask:
 
     Keyword names: causal, window, kv_offset, q_valid, kv_valid,
     cu_seqlens_q, cu_seqlens_kv (host sequences or tensors), segment_ids_q,
-    segment_ids_kv ([B, L] or [L] host/device integer arrays).  The device
-    copies are made once here and kept alive by this object.
+    segment_ids_kv ([B, L] or [L] host/device integer arrays), prefix,
+    dilation, documents.  The device copies are made once here and kept
+    alive by this object.
     """
 
     def __init__(self, device="cuda", causal=False, window=0, kv_offset=0, q_valid=-1, kv_valid=-1,
-                 cu_seqlens_q=None, cu_seqlens_kv=None, segment_ids_q=None, segment_ids_kv=None):
+                 cu_seqlens_q=None, cu_seqlens_kv=None, segment_ids_q=None, segment_ids_kv=None,
+                 prefix=0, dilation=0, documents=False):
         def dev(x):
             if x is None:
                 return None
@@ -161,8 +164,8 @@ class Mask:
         nseg = 0 if cq is None else int(cq.numel()) - 1
         self.struct = _Mask(int(bool(causal)), int(window), int(kv_offset),
                             -1 if q_valid is None else int(q_valid),
-                            -1 if kv_valid is None else int(kv_valid), nseg, 0,
-                            _ptr(cq), _ptr(ck), _ptr(iq), _ptr(ik))
+                            -1 if kv_valid is None else int(kv_valid), nseg, int(dilation or 0),
+                            _ptr(cq), _ptr(ck), _ptr(iq), _ptr(ik), int(prefix or 0), int(bool(documents)), 0)
 
     @classmethod
     def of(cls, mask, device="cuda"):

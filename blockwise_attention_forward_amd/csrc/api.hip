@@ -63,8 +63,15 @@ int32_t resolve_mask(const bwa_mask* m, i64 B, i64 lq, i64 lk, bwa::MaskDev& out
     if (!m) return fail(BWA_ERR_NULL_ARG, "mask is NULL");
     if (m->causal != 0 && m->causal != 1) return fail(BWA_ERR_BAD_MASK, "causal must be 0 or 1");
     if (m->window < 0) return fail(BWA_ERR_BAD_MASK, "window must be >= 0");
-    if (m->window > 0 && !m->causal)
-        return fail(BWA_ERR_BAD_MASK, "a sliding window needs causal = 1");
+    if (m->dilation < 0) return fail(BWA_ERR_BAD_MASK, "dilation must be >= 0");
+    if (m->dilation > 1 && (!m->causal || m->window <= 0))
+        return fail(BWA_ERR_BAD_MASK, "a dilated band needs causal = 1 and a window");
+    if (m->prefix < 0) return fail(BWA_ERR_BAD_MASK, "prefix must be >= 0");
+    if (m->prefix > 0 && (!m->causal || m->window > 0))
+        return fail(BWA_ERR_BAD_MASK, "a prefix needs causal = 1 and no window");
+    if (m->prefix > kMaxLen) return fail(BWA_ERR_BAD_MASK, "prefix out of range");
+    if (m->documents != 0 && m->documents != 1) return fail(BWA_ERR_BAD_MASK, "documents must be 0 or 1");
+    if (m->documents && !m->segment_ids_q) return fail(BWA_ERR_BAD_MASK, "documents needs segment ids");
     if (m->q_valid > lq) return fail(BWA_ERR_BAD_MASK, "q_valid %lld > Lq %lld", (long long)m->q_valid, (long long)lq);
     if (m->kv_valid > lk) return fail(BWA_ERR_BAD_MASK, "kv_valid %lld > Lk %lld", (long long)m->kv_valid, (long long)lk);
     if (m->kv_offset > kMaxLen || m->kv_offset < -kMaxLen)
@@ -85,7 +92,11 @@ int32_t resolve_mask(const bwa_mask* m, i64 B, i64 lq, i64 lk, bwa::MaskDev& out
     out.kv_valid = m->kv_valid < 0 ? lk : m->kv_valid;
     out.causal = m->causal;
     out.window = m->window;
-    out.seg_mode = cu ? 1 : (ids ? 2 : 0);
+    out.dilation = m->dilation > 1 ? m->dilation : 1;
+    out.prefix = m->prefix;
+    out.seg_mode = cu ? 1 : (ids ? (m->documents ? 3 : 2) : 0);
+    if (out.seg_mode == 3 || out.dilation > 1)
+        return fail(BWA_ERR_UNSUPPORTED, "document ids and dilated bands are not built yet");
     out.num_segments = cu ? m->num_segments : 0;
     out.cu_q = m->cu_seqlens_q;
     out.cu_kv = m->cu_seqlens_kv ? m->cu_seqlens_kv : m->cu_seqlens_q;
@@ -192,6 +203,7 @@ int32_t bwa_fixed_m_bound(const bwa_tensor* q, const bwa_tensor* k_chunks, int32
     if (BH > 0 && (!kmax_out || !mmax_out || !gate_out || (q->L > 0 && !m_out)))
         return fail(BWA_ERR_NULL_ARG, "bound outputs must be non-NULL");
     bwa::BoundLaunch a;
+    a.Hk = n_chunks > 0 ? (int)k_chunks[0].H : (int)q->H;
     a.q = {q->ptr, q->L, q->sB, q->sL, q->sH, q_valid < 0 ? q->L : q_valid};
     for (int c = 0; c < n_chunks; ++c) {
         const bwa_tensor* k = &k_chunks[c];
@@ -199,8 +211,11 @@ int32_t bwa_fixed_m_bound(const bwa_tensor* q, const bwa_tensor* k_chunks, int32
         snprintf(name, sizeof(name), "k_chunks[%d]", c);
         st = check_tensor(k, name);
         if (st) return st;
-        if (k->dtype != q->dtype || k->B != q->B || k->H != q->H || k->D != q->D)
-            return fail(BWA_ERR_BAD_SHAPE, "%s: dtype/B/H/D differ from q", name);
+        if (k->dtype != q->dtype || k->B != q->B || k->D != q->D || k->H != a.Hk)
+            return fail(BWA_ERR_BAD_SHAPE, "%s: dtype/B/D differ from q, or heads from k_chunks[0]", name);
+        if (q->H > 0 && (k->H <= 0 || q->H % k->H))
+            return fail(BWA_ERR_BAD_SHAPE, "%s: %lld key heads do not divide %lld query heads", name,
+                        (long long)k->H, (long long)q->H);
         i64 valid = k->L;
         if (kv_valid && kv_valid[c] >= 0) {
             if (kv_valid[c] > k->L) return fail(BWA_ERR_BAD_SHAPE, "%s: kv_valid > L", name);
@@ -262,8 +277,11 @@ static int32_t attn_fwd_impl(const bwa_tensor* q, const bwa_tensor* k, const bwa
         return fail(BWA_ERR_BAD_DTYPE, "q, k and v must share a dtype");
     if (o->dtype != BWA_F32 && o->dtype != q->dtype)
         return fail(BWA_ERR_BAD_DTYPE, "o must be fp32 or q's dtype");
-    if (k->B != q->B || v->B != q->B || k->H != q->H || v->H != q->H || k->D != q->D || v->D != q->D)
-        return fail(BWA_ERR_BAD_SHAPE, "q, k, v disagree on B, H or D");
+    if (k->B != q->B || v->B != q->B || k->D != q->D || v->D != q->D || v->H != k->H)
+        return fail(BWA_ERR_BAD_SHAPE, "q, k, v disagree on B or D, or k and v on H");
+    if (q->H > 0 && (k->H <= 0 || q->H % k->H))
+        return fail(BWA_ERR_BAD_SHAPE, "%lld key/value heads do not divide %lld query heads", (long long)k->H,
+                    (long long)q->H);
     if (k->L != v->L) return fail(BWA_ERR_BAD_SHAPE, "k and v lengths differ");
     if (o->B != q->B || o->L != q->L || o->H != q->H || o->D != q->D)
         return fail(BWA_ERR_BAD_SHAPE, "o must have q's shape");
@@ -311,6 +329,7 @@ static int32_t attn_fwd_impl(const bwa_tensor* q, const bwa_tensor* k, const bwa
     a.o = o->ptr; a.o_sB = o->sB; a.o_sL = o->sL; a.o_sH = o->sH;
     a.lse = lse;
     a.B = (int)B; a.H = (int)H; a.D = (int)q->D;
+    a.kv_group = H > 0 ? (int)(H / k->H) : 1;
     a.Lq = Lq; a.Lk = Lk;
     a.in_dtype = q->dtype;
     a.out_dtype = o->dtype;

@@ -716,8 +716,9 @@ __device__ inline void bf16_walk(const AttnLaunch& p, Bf16State<D, NW>& st, cons
     constexpr int NB = C::NBUF;
     static_assert(NB == 2 || NB == 3, "ring of 2 or 3 buffers");
     static_assert(2 * C::RUNS_PER_WAVE * (NB - 2) <= 12, "wait_vm covers at most 12 outstanding copies");
-    const __bf16* kbase = (const __bf16*)p.k + b * p.k_sB + h * p.k_sH;
-    const __bf16* vbase = (const __bf16*)p.v + b * p.v_sB + h * p.v_sH;
+    const i64 hk = (int)h / p.kv_group;  // key/value head of query head h
+    const __bf16* kbase = (const __bf16*)p.k + b * p.k_sB + hk * p.k_sH;
+    const __bf16* vbase = (const __bf16*)p.v + b * p.v_sB + hk * p.v_sH;
     const int kv_lim = (int)p.mask.kv_valid;
     // Copies run NB - 1 tiles ahead of the compute.
     Cursor<C::TILE> cur, ahead;
@@ -1044,8 +1045,9 @@ __device__ inline void f32_run(const AttnLaunch& p, const Walk& walk, float* ks,
 #pragma unroll
     for (int d = 0; d < NDB; ++d) acc[d] = f32x16{};
     float m_run = kNegInf, l_run = 0.0f;
-    const float* kbase = (const float*)p.k + b * p.k_sB + h * p.k_sH;
-    const float* vbase = (const float*)p.v + b * p.v_sB + h * p.v_sH;
+    const i64 hk = (int)h / p.kv_group;  // key/value head of query head h
+    const float* kbase = (const float*)p.k + b * p.k_sB + hk * p.k_sH;
+    const float* vbase = (const float*)p.v + b * p.v_sB + hk * p.v_sH;
     const int kv_lim = (int)p.mask.kv_valid;
     Cursor<TILE> cur;
     while (cur.next(walk)) {

@@ -59,18 +59,20 @@ __global__ __launch_bounds__(256) void norms_kernel(const NormTasks nt) {
     int t = 0;
     while (t <= a.n_chunks && task >= nt.task_off[t + 1]) ++t;
     const BoundTensor& T = (t == 0) ? a.q : a.k[t - 1];
-    const i64 rows = (i64)a.B * T.L * a.H;
+    const int TH = (t == 0) ? a.H : a.Hk;  // heads of this tensor
+    const int g = a.H / a.Hk;              // query heads per key head
+    const i64 rows = (i64)a.B * T.L * TH;
     const i64 r_begin = (task - nt.task_off[t]) * kRowsPerTask;
     const int n_rows = (int)min<i64>(kRowsPerTask, rows - r_begin);
     // Start of the stretch in (b, l, h); rows inside it are offsets of at most
     // kRowsPerTask from here, so 32-bit division finds each row's indices.
-    const unsigned H = (unsigned)a.H, L = (unsigned)T.L;
+    const unsigned H = (unsigned)TH, L = (unsigned)T.L;
     const i64 tok0 = r_begin / H;
     const unsigned h0 = (unsigned)(r_begin - tok0 * H);
     const i64 b0 = tok0 / L;
     const unsigned l0 = (unsigned)(tok0 - b0 * L);
     const bool one_batch = (i64)l0 + (h0 + (unsigned)n_rows - 1) / H < (i64)L;
-    const bool in_lds = a.H <= kMaxHeadsLds && one_batch;
+    const bool in_lds = TH <= kMaxHeadsLds && one_batch;
     const int tid = threadIdx.x, sub = tid % TPR;
     for (int i = tid; i < kMaxHeadsLds; i += 256) hmax[i] = 0u;
     __syncthreads();
@@ -118,20 +120,28 @@ __global__ __launch_bounds__(256) void norms_kernel(const NormTasks nt) {
                 const float nrm = __builtin_sqrtf(ss);
                 if (t == 0) a.m_out[(b * a.H + h) * T.L + l] = nrm;
                 if (l < T.valid) {
-                    if (in_lds) atomicMax(&hmax[h], __float_as_uint(nrm));
-                    else atomicMax((unsigned int*)((t == 0) ? &a.mmax_out[b * a.H + h] : &a.kmax_out[b * a.H + h]),
-                                   __float_as_uint(nrm));
+                    if (in_lds) {
+                        atomicMax(&hmax[h], __float_as_uint(nrm));
+                    } else if (t == 0) {
+                        atomicMax((unsigned int*)&a.mmax_out[b * a.H + h], __float_as_uint(nrm));
+                    } else {  // every query head of key head h
+                        for (int r = 0; r < g; ++r)
+                            atomicMax((unsigned int*)&a.kmax_out[b * a.H + h * g + r], __float_as_uint(nrm));
+                    }
                 }
             }
         }
     }
     __syncthreads();
     if (in_lds) {
-        for (int h = tid; h < a.H; h += 256) {
+        for (int h = tid; h < TH; h += 256) {
             const unsigned v = hmax[h];
             if (v == 0u) continue;
-            float* dst = (t == 0) ? &a.mmax_out[b0 * a.H + h] : &a.kmax_out[b0 * a.H + h];
-            atomicMax((unsigned int*)dst, v);
+            if (t == 0) {
+                atomicMax((unsigned int*)&a.mmax_out[b0 * a.H + h], v);
+            } else {  // every query head of key head h
+                for (int r = 0; r < g; ++r) atomicMax((unsigned int*)&a.kmax_out[b0 * a.H + h * g + r], v);
+            }
         }
     }
 }
@@ -163,13 +173,14 @@ void launch_norms(const NormTasks& nt, i64 tasks, hipStream_t stream) {
 hipError_t launch_fixed_m_bound(const BoundLaunch& a, hipStream_t stream) {
     const int BH = a.B * a.H;
     if (BH == 0) return hipSuccess;
+    const i64 BHk = (i64)a.B * a.Hk;
     hipLaunchKernelGGL(init_kernel, dim3((BH + 255) / 256), dim3(256), 0, stream, a);
     NormTasks nt;
     nt.a = a;
     nt.task_off[0] = 0;
     nt.task_off[1] = ((i64)BH * a.q.L + kRowsPerTask - 1) / kRowsPerTask;
     for (int c = 0; c < a.n_chunks; ++c)
-        nt.task_off[c + 2] = nt.task_off[c + 1] + ((i64)BH * a.k[c].L + kRowsPerTask - 1) / kRowsPerTask;
+        nt.task_off[c + 2] = nt.task_off[c + 1] + (BHk * a.k[c].L + kRowsPerTask - 1) / kRowsPerTask;
     for (int c = a.n_chunks + 2; c < kMaxChunks + 2; ++c) nt.task_off[c] = nt.task_off[a.n_chunks + 1];
     const i64 tasks = nt.task_off[a.n_chunks + 1];
     if (tasks >= ((i64)1 << 24)) return hipErrorInvalidConfiguration;  // 256 work-items each, < 2^32 in all

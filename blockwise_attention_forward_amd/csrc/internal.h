@@ -19,7 +19,9 @@ struct MaskDev {
     i64 q_valid, kv_valid;
     int causal;
     int window;
-    int seg_mode;  // 0 none, 1 cu_seqlens, 2 per-token segment ids
+    int dilation;  // 1 = none
+    i64 prefix;    // 0 = none
+    int seg_mode;  // 0 none, 1 cu_seqlens, 2 per-token segment ids (non-decreasing), 3 document ids (any order)
     int num_segments;
     const int* cu_q;
     const int* cu_kv;
@@ -27,12 +29,14 @@ struct MaskDev {
     const int* ids_kv;  // [B][lk]
 };
 
-// Keys visible to query row i of batch element b form one interval [lo, hi):
-// every term of the mask bounds it from below or above (padding, segment,
-// causal and window terms of the visibility rule in bwattn.h).  Rows that see
-// nothing return (0, 0).  Segment lookups are binary searches over the
-// cumulative lengths or the (non-decreasing) per-token ids; nothing is
-// tabulated per token.
+// Keys visible to query row i of batch element b lie in one interval
+// [lo, hi): every term of the mask bounds them from below or above (padding,
+// segment, causal, prefix and window terms of the visibility rule in
+// bwattn.h).  Except for dilated bands and document ids, every key of the
+// interval is visible.  Rows that see nothing return (0, 0).  Segment
+// lookups are binary searches over the cumulative lengths or the
+// (non-decreasing) per-token ids; nothing is tabulated per token.  Document
+// ids (any order) bound nothing here: their keys are tested one by one.
 __device__ inline void row_interval(const MaskDev& m, i64 b, i64 i, int& out_lo, int& out_hi) {
     i64 lo = 0, hi = m.kv_valid;
     bool ok = (i >= 0) && (i < m.q_valid);
@@ -66,8 +70,11 @@ __device__ inline void row_interval(const MaskDev& m, i64 b, i64 i, int& out_lo,
         lo = max(lo, first);
         hi = min(hi, a);
     }
-    if (m.causal) hi = min(hi, i - m.kv_offset + 1);
-    if (m.window > 0) lo = max(lo, i - m.kv_offset - (i64)m.window + 1);
+    if (m.causal) hi = min(hi, max(i - m.kv_offset + 1, m.prefix - m.kv_offset));
+    if (m.window > 0) {
+        lo = max(lo, i - m.kv_offset - (i64)m.window + 1);
+        if (!m.causal) hi = min(hi, i - m.kv_offset + (i64)m.window);
+    }
     lo = max(lo, (i64)0);
     if (!ok || lo >= hi) { lo = 0; hi = 0; }
     out_lo = (int)lo;
@@ -82,6 +89,7 @@ struct AttnLaunch {
     void* o; i64 o_sB, o_sL, o_sH;
     float* lse;
     int B, H, D;
+    int kv_group;  // query heads per key/value head (h reads key/value head h / kv_group)
     i64 Lq, Lk;
     int in_dtype, out_dtype;
     float scale;
@@ -162,6 +170,7 @@ struct BoundLaunch {
     BoundTensor k[kMaxChunks];
     int n_chunks;
     int B, H, D, dtype;
+    int Hk;  // key heads (H a multiple of Hk: query head h reads key head h / (H / Hk))
     const float* kmax_in;
     int n_kmax_in;
     float scale, tau;

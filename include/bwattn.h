@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define BWATTN_VERSION 1
+#define BWATTN_VERSION 2
 
 /* Status codes. */
 enum {
@@ -84,36 +84,50 @@ typedef struct bwa_tensor {
 
 /*
  * Mask description.  Query row i sits at position i and key j at position
- * j + kv_offset.  Key j is visible to row i iff all of:
+ * j + kv_offset; write d = i - (j + kv_offset).  Key j is visible to row i
+ * iff all of:
  *   j < kv_valid and i < q_valid         -- padding at the end of the global
  *                                           sequence [ULYRING]; alignment rows
  *                                           are zeroed [H3 Modifications]
- *   seg_q(i) == seg_kv(j)                -- packing / varlen [SPLASH; H3]
- *   causal     => j + kv_offset <= i
- *   window > 0 => i - (j + kv_offset) < window   (requires causal)
- * A row with no visible key gets O = 0 and LSE = -inf.
+ *   seg_q(i) == seg_kv(j)                -- packing / varlen [SPLASH; H3];
+ *                                           documents [DKORDER masks]
+ *   causal, no prefix => d >= 0
+ *   causal, prefix P  => d >= 0 or j + kv_offset < P   (prefix-LM: the first
+ *                                           P positions are seen by every row)
+ *   window W > 0      => d < W when causal (a band of W keys ending at the
+ *                        row), |d| < W when not (a two-sided band)
+ *   dilation g >= 2   => d mod g == 0 (a dilated band; needs causal and W)
+ * A row with no visible key gets O = 0 and LSE = -inf.  (The [DKORDER]
+ * tables name sliding_window, prefix_lm, dilated_sliding_window and
+ * document masks without defining them; these are the plainest readings.)
  *
  * Segments come either from cumulative lengths (cu_seqlens_q/kv, shared by
  * every batch element; segment s covers [cu[s], cu[s+1]); positions covered
- * by no segment see nothing) or from per-token segment ids ([B][L],
- * non-decreasing along L, equal ids see each other).  Leave both NULL for an
- * unsegmented mask.  Segments are turned into per-row key intervals before
- * any attention tile runs, so no per-token table is ever held on chip and the
- * sequence length is bounded by memory only; one segment covering every
- * token gives exactly the unsegmented result [SPLASH description].
+ * by no segment see nothing) or from per-token segment ids ([B][L]; equal
+ * ids see each other).  With documents == 0 the ids must be non-decreasing
+ * along L (contiguous segments), and segments become per-row key intervals
+ * before any attention tile runs, so no per-token table is held on chip and
+ * the sequence length is bounded by memory only; one segment covering every
+ * token gives exactly the unsegmented result [SPLASH description].  With
+ * documents == 1 the ids may come in any order (a document's tokens need not
+ * be contiguous): tiles that mix documents compare ids key by key.  Leave
+ * both NULL for an unsegmented mask.
  */
 typedef struct bwa_mask {
     int32_t causal;                 /* 0 or 1 */
-    int32_t window;                 /* 0 = no window; > 0 needs causal */
+    int32_t window;                 /* 0 = no window; see above */
     int64_t kv_offset;              /* key j is at position j + kv_offset (ring hop, bottom-right) */
     int64_t q_valid;                /* rows >= q_valid see nothing; < 0 means Lq */
     int64_t kv_valid;               /* keys >= kv_valid are invisible; < 0 means Lk */
     int32_t num_segments;           /* segments in cu_seqlens (0 when not used) */
-    int32_t reserved;
+    int32_t dilation;               /* 0 or 1 = none; >= 2 needs causal and window */
     const int32_t* cu_seqlens_q;    /* device [num_segments + 1], non-decreasing */
     const int32_t* cu_seqlens_kv;   /* device [num_segments + 1]; NULL = cu_seqlens_q */
-    const int32_t* segment_ids_q;   /* device [B][Lq] non-decreasing, or NULL */
+    const int32_t* segment_ids_q;   /* device [B][Lq], or NULL */
     const int32_t* segment_ids_kv;  /* device [B][Lk]; NULL = segment_ids_q (needs Lq == Lk) */
+    int64_t prefix;                 /* 0 = none; > 0 needs causal and no window */
+    int32_t documents;              /* 0: ids non-decreasing; 1: ids in any order */
+    int32_t reserved;
 } bwa_mask;
 
 /*

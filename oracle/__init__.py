@@ -29,6 +29,8 @@ module docstrings where they are used.
 
 from .attention import (  # noqa: F401
     visibility,
+    contiguous,
+    kv_head,
     row_intervals_bruteforce,
     row_intervals,
     attention,

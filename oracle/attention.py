@@ -8,10 +8,12 @@ A mask is a plain dict with the keys below (missing keys take the default):
 
 ``causal`` (False), ``window`` (0), ``kv_offset`` (0), ``q_valid`` (Lq),
 ``kv_valid`` (Lk), ``cu_seqlens_q`` / ``cu_seqlens_kv`` (None),
-``segment_ids_q`` / ``segment_ids_kv`` (None; 1-D, one batch).
+``segment_ids_q`` / ``segment_ids_kv`` (None; 1-D, one batch), ``prefix``
+(0), ``dilation`` (0), ``documents`` (False).
 
 Query row ``i`` sits at position ``i``; key ``j`` sits at position
-``j + kv_offset``.  Key ``j`` is visible to row ``i`` iff all of:
+``j + kv_offset``; write ``d = i - (j + kv_offset)``.  Key ``j`` is visible
+to row ``i`` iff all of:
 
 1. ``j < kv_valid`` and ``i < q_valid`` -- padding sits only at the end of the
    global sequence and the mask is taken from positions, not tiled per shard
@@ -23,11 +25,20 @@ Query row ``i`` sits at position ``i``; key ``j`` sits at position
    covered by no segment sees nothing) or from per-token segment ids
    ("Let splash attention exceed 524,288 tokens when packing is off",
    description; sglang pull request 47566, Motivation).
-3. ``causal`` => ``j + kv_offset <= i``.
-4. ``window > 0`` => ``i - (j + kv_offset) < window`` (the band holds
-   ``window`` keys counting the query's own position; the flash-attention
-   page names ``sliding_window:512`` without fixing the bound, and this is
-   the plainest reading).
+3. ``causal`` => ``d >= 0``, or, with ``prefix = P > 0``, ``d >= 0`` or
+   ``j + kv_offset < P`` (prefix-LM: the first ``P`` positions are seen by
+   every row).
+4. ``window > 0`` => ``d < window`` when causal (the band holds ``window``
+   keys counting the query's own position), ``|d| < window`` when not (a
+   two-sided band).
+5. ``dilation = g >= 2`` (with causal and a window) => ``d mod g == 0``.
+
+The flash-attention page ("Add more optimal dk order optional arg", the
+mask tables) names ``sliding_window:512``, ``prefix_lm``,
+``dilated_sliding_window`` and ``document`` masks without defining them;
+the terms above are the plainest readings.  With ``documents`` the
+per-token ids of term 2 may come in any order (a document's tokens need
+not be contiguous); without it they are non-decreasing.
 
 Attention output for a row with at least one visible key is the plain softmax
 average ``O_i = sum_j p_ij v_j / sum_j p_ij`` with ``p_ij = exp(s_ij - M_i)``,
@@ -80,12 +91,24 @@ def visibility(rows, Lk, mask, Lq=None):
         sq = np.asarray(ids_q, dtype=np.int64)[rows][:, None]
         sk = np.asarray(ids_k, dtype=np.int64)[:Lk][None, :]
         vis &= sq == sk
-    if _get(mask, "causal", False):
-        vis &= (j + off) <= i
+    d = i - (j + off)
+    causal = bool(_get(mask, "causal", False))
+    if causal:
+        prefix = int(_get(mask, "prefix", 0))
+        vis &= (d >= 0) | ((j + off) < prefix)
     w = int(_get(mask, "window", 0))
     if w > 0:
-        vis &= (i - (j + off)) < w
+        vis &= (d < w) if causal else (np.abs(d) < w)
+    g = int(_get(mask, "dilation", 0))
+    if g >= 2:
+        vis &= (d % g) == 0
     return vis
+
+
+def contiguous(mask):
+    """True when every row's visible keys form one interval (all masks but
+    dilated bands and document ids)."""
+    return int(_get(mask, "dilation", 0)) < 2 and not _get(mask, "documents", False)
 
 
 def row_intervals_bruteforce(Lq, Lk, mask):
@@ -103,8 +126,8 @@ def row_intervals_bruteforce(Lq, Lk, mask):
         last = Lk - 1 - np.argmax(vis[:, ::-1], axis=1)
         lo[rows] = np.where(anyv, first, 0)
         hi[rows] = np.where(anyv, last + 1, 0)
-        # Every mask described above leaves a contiguous visible set per row.
-        assert np.all(vis.sum(axis=1) == np.where(anyv, last + 1 - first, 0))
+        if contiguous(mask):
+            assert np.all(vis.sum(axis=1) == np.where(anyv, last + 1 - first, 0))
     return lo, hi
 
 
@@ -114,8 +137,10 @@ def row_intervals(Lq, Lk, mask):
     An independent second derivation for sequences too long for the element
     predicate: each term of the mask bounds the visible keys of a row from
     below or above.  Segment ids must be non-decreasing (contiguous
-    segments).  Rows that see nothing get ``(0, 0)``.
+    segments), and the mask contiguous (no dilation, no document ids).  Rows
+    that see nothing get ``(0, 0)``.
     """
+    assert contiguous(mask), "row_intervals needs a contiguous mask"
     i = np.arange(Lq, dtype=np.int64)
     q_valid = int(_get(mask, "q_valid", Lq))
     kv_valid = int(_get(mask, "kv_valid", Lk))
@@ -137,11 +162,17 @@ def row_intervals(Lq, Lk, mask):
         mine = np.asarray(ids_q, dtype=np.int64)[:Lq]
         lo = np.maximum(lo, np.searchsorted(ids_k, mine, side="left"))
         hi = np.minimum(hi, np.searchsorted(ids_k, mine, side="right"))
-    if _get(mask, "causal", False):
-        hi = np.minimum(hi, i - off + 1)
+    causal = bool(_get(mask, "causal", False))
+    if causal:
+        # the causal part [0, i - off] and the prefix part [0, P - off) are
+        # both prefixes of the key axis: their union ends at the larger end
+        prefix = int(_get(mask, "prefix", 0))
+        hi = np.minimum(hi, np.maximum(i - off + 1, prefix - off))
     w = int(_get(mask, "window", 0))
     if w > 0:
         lo = np.maximum(lo, i - off - w + 1)
+        if not causal:
+            hi = np.minimum(hi, i - off + w)
     lo = np.maximum(lo, 0)
     empty = (lo >= hi) | (i >= q_valid)
     return np.where(empty, 0, lo), np.where(empty, 0, hi)
@@ -263,3 +294,14 @@ def fixed_m_bound(q, k_chunks, scale, tau, q_valid=None, kv_valid=None,
     mmax = float(m[:q_valid].max()) if q_valid > 0 else 0.0
     gate = bool(np.float32(mmax) <= np.float32(tau))
     return kmax, m, mmax, gate
+
+
+def kv_head(h, H, H_kv):
+    """Key/value head read by query head ``h`` when ``H`` query heads share
+    ``H_kv`` key/value heads in contiguous groups (grouped-query attention;
+    ``H_kv = 1`` is multi-query, ``H_kv = H`` one head each).  The
+    flash-attention page's benchmark rows carry a ``kv_mode`` column (``mha``
+    in every row); grouping consecutive query heads is the plainest reading
+    of the other modes."""
+    assert H_kv >= 1 and H % H_kv == 0
+    return h // (H // H_kv)

@@ -53,7 +53,7 @@ def block_kinds_intervals(lo, hi, Lq, Lk, bq, bkv, qblocks=None):
     """Kind of every tile from per-row visible intervals ``[lo_i, hi_i)``.
 
     Uses only that each row's visible keys are one contiguous interval (true
-    for every mask in this package): a tile is visited iff some row interval
+    for every mask here but dilated bands and document ids): a tile is visited iff some row interval
     meets its key range, and FULL iff every row interval covers it.
     ``qblocks`` restricts the output to the listed query blocks.
     """

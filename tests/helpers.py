@@ -38,6 +38,7 @@ def oracle_attention(q, k, v, mask, scale, rows=None, heads=None):
     Converts one (batch, head) at a time to fp64, so long sequences fit.
     """
     B, Lq, H, D = q.shape
+    Hk = k.shape[2]  # key/value heads (grouped-query attention when fewer than H)
     heads = list(range(H)) if heads is None else list(heads)
     rows = np.arange(Lq) if rows is None else np.asarray(rows)
     O = np.zeros((B, len(rows), len(heads), D))
@@ -45,7 +46,8 @@ def oracle_attention(q, k, v, mask, scale, rows=None, heads=None):
     for b in range(B):
         m = mask_for_batch(mask, b)
         for n, h in enumerate(heads):
-            o, l = oracle.attention_rows(np64(q[b, :, h]), np64(k[b, :, h]), np64(v[b, :, h]), m, scale, rows)
+            hk = oracle.kv_head(h, H, Hk)
+            o, l = oracle.attention_rows(np64(q[b, :, h]), np64(k[b, :, hk]), np64(v[b, :, hk]), m, scale, rows)
             O[b, :, n] = o
             L[b, n] = l
     return O, L

@@ -66,6 +66,7 @@ def test_struct_layout_matches_header():
 int main(void) {
   printf("%zu %zu %zu %zu\n", sizeof(bwa_tensor), offsetof(bwa_tensor, B), offsetof(bwa_tensor, sH), sizeof(bwa_mask));
   printf("%zu %zu %zu %zu\n", offsetof(bwa_mask, num_segments), offsetof(bwa_mask, segment_ids_kv), sizeof(bwa_blocks), offsetof(bwa_blocks, row_hi));
+  printf("%zu %zu %zu\n", offsetof(bwa_mask, dilation), offsetof(bwa_mask, prefix), offsetof(bwa_mask, documents));
   return 0;
 }
 """
@@ -77,12 +78,13 @@ int main(void) {
     got = list(map(int, out))
     want = [ctypes.sizeof(bw._Tensor), bw._Tensor.B.offset, bw._Tensor.sH.offset, ctypes.sizeof(bw._Mask),
             bw._Mask.num_segments.offset, bw._Mask.segment_ids_kv.offset, ctypes.sizeof(bw._Blocks),
-            bw._Blocks.row_hi.offset]
+            bw._Blocks.row_hi.offset, bw._Mask.dilation.offset, bw._Mask.prefix.offset,
+            bw._Mask.documents.offset]
     assert got == want
 
 
 def test_version_and_status_strings():
-    assert bw.bwa_version() == 1
+    assert bw.bwa_version() == 2
     for code in range(9):
         assert bw.bwa_status_string(code) != "unknown status"
     assert bw.bwa_status_string(99) == "unknown status"
@@ -117,7 +119,8 @@ def _attn(q, k, v, o, mask=None, mode=0, m=None, lse=0x20000):
     (dict(k=dict(dtype=7)), 4),
     (dict(o=dict(L=255)), 2),
     (dict(v=dict(L=100)), 2),
-    (dict(k=dict(H=3), v=dict(H=3)), 2),
+    (dict(k=dict(H=3), v=dict(H=3)), 2),       # 3 key heads do not divide 2 query heads
+    (dict(k=dict(H=1), v=dict(H=2)), 2),       # k and v heads differ
 ])
 def test_attn_fwd_argument_errors(case, code):
     args = {n: _t(**case.get(n, {})) for n in ("q", "k", "v", "o")}
@@ -126,8 +129,15 @@ def test_attn_fwd_argument_errors(case, code):
 
 
 @pytest.mark.parametrize("mask,code", [
-    (dict(window=128), 5),                    # window needs causal
     (dict(causal=2), 5),
+    (dict(dilation=2, window=64), 5),         # a dilated band needs causal
+    (dict(dilation=2, causal=1), 5),          # ... and a window
+    (dict(dilation=-1), 5),
+    (dict(prefix=64), 5),                     # a prefix needs causal
+    (dict(prefix=64, causal=1, window=32), 5),  # ... and no window
+    (dict(prefix=-1, causal=1), 5),
+    (dict(documents=1), 5),                   # documents needs segment ids
+    (dict(documents=2, segment_ids_q=0x40000), 5),
     (dict(q_valid=300), 5),                   # > Lq
     (dict(kv_valid=300), 5),
     (dict(num_segments=2), 5),                # segments without cu_seqlens
@@ -157,6 +167,23 @@ def test_attn_fwd_carry_argument_errors(o_prev, o, lse_prev, code):
     op = _t(**o_prev) if o_prev is not None else None
     assert _carry(_t(), _t(), _t(), _t(**o), op, lse_prev=lse_prev) == code
     assert bw.bwa_last_error() != ""
+
+
+def test_gqa_head_checks():
+    # 8 query heads on 2 key/value heads pass the shape checks: each call
+    # below fails at a later argument check (nothing is launched)
+    q, kv = _t(H=8), _t(H=2)
+    assert _attn(q, kv, _t(H=2), _t(H=8), mask=_mask(causal=2)) == 5
+    assert "causal" in bw.bwa_last_error()
+    assert _attn(q, _t(H=3), _t(H=3), _t(H=8)) == 2
+    ks = (bw._Tensor * 2)(_t(H=2), _t(H=2, dtype=0))
+    assert L.bwa_fixed_m_bound(ctypes.byref(_t(H=8)), ks, 2, None, 0, None, -1, 0.1, 106.5, 0x1000, 0x1000,
+                               0x1000, 0x1000, None) == 2
+    assert "k_chunks[1]" in bw.bwa_last_error()
+    ks3 = (bw._Tensor * 1)(_t(H=3))
+    assert L.bwa_fixed_m_bound(ctypes.byref(_t(H=8)), ks3, 1, None, 0, None, -1, 0.1, 106.5, 0x1000, 0x1000,
+                               0x1000, 0x1000, None) == 2
+    assert "do not divide" in bw.bwa_last_error()
 
 
 def test_fixed_m_needs_m_and_lse():

@@ -55,6 +55,10 @@ MASKS = [
     {"cu_seqlens_q": [0, 70, 200, 333], "cu_seqlens_kv": [0, 70, 200, 333]},
     {"cu_seqlens_q": [0, 150, 333], "cu_seqlens_kv": [0, 150, 333], "causal": True, "q_valid": 300},
     {"cu_seqlens_q": [5, 100, 300], "cu_seqlens_kv": [0, 60, 333], "causal": True, "window": 50},
+    {"causal": True, "prefix": 100},                      # prefix-LM
+    {"causal": True, "prefix": 300, "kv_offset": 40, "q_valid": 320},
+    {"window": 60},                                       # two-sided band
+    {"window": 50, "kv_offset": -40, "kv_valid": 310},
 ]
 
 
@@ -129,6 +133,38 @@ def test_block_lists_bit_exact(mi, bq, bkv):
     lo, hi = oracle.row_intervals_bruteforce(Lq, Lk, mask)
     assert np.array_equal(bl.row_lo[:Lq].cpu().numpy(), lo)
     assert np.array_equal(bl.row_hi[:Lq].cpu().numpy(), hi)
+
+
+@pytest.mark.parametrize("Hk", [1, 2, 6])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_grouped_query_heads(Hk, dtype):
+    # 6 query heads on Hk key/value heads (multi-query at 1, one each at 6),
+    # plain and balanced launch, fixed-m bound per key head
+    B, H, Lq, Lk, D = 2, 6, 333, 401, 128
+    scale = 1 / math.sqrt(D)
+    q = _rand((B, Lq, H, D), 60, dtype)
+    k = _rand((B, Lk, Hk, D), 61, dtype)
+    v = _rand((B, Lk, Hk, D), 62, dtype)
+    mask = {"causal": True, "kv_offset": 68}
+    o_ref, l_ref = oracle_attention(q, k, v, mask, scale)
+    o, l = bw.bwa_attn_fwd(q, k, v, mask, scale=scale, out_dtype=torch.float32)
+    assert_close(o, l, o_ref, l_ref, dtype, f"gqa Hk={Hk}")
+    if dtype == torch.bfloat16:
+        bq, _ = bw.bwa_attn_tile(dtype, D)
+        blocks = bw.bwa_block_mask_build(mask, B, Lq, Lk, bq, 64)
+        ob, lb = bw.bwa_attn_fwd_balanced(q, k, v, mask, blocks=blocks, scale=scale, n_cus=16,
+                                          out_dtype=torch.float32)
+        assert_close(ob, lb, o_ref, l_ref, dtype, f"gqa balanced Hk={Hk}")
+    kmax, mmax, m, gate = bw.bwa_fixed_m_bound(q, [k], scale, 106.5)
+    for b in range(B):
+        for h in range(H):
+            km, mr, mm, gh = oracle.fixed_m_bound(np64(q[b, :, h]), [np64(k[b, :, oracle.kv_head(h, H, Hk)])],
+                                                  scale, 106.5)
+            np.testing.assert_allclose(kmax[b, h].item(), km, rtol=1e-6)
+            np.testing.assert_allclose(np64(m[b, h]), mr, rtol=2e-6)
+            assert bool(gate[b, h].item()) == gh
+    o2, l2 = bw.bwa_attn_fwd(q, k, v, mask, scale=scale, mode=bw.BWA_MODE_FIXED_M, m=m, out_dtype=torch.float32)
+    assert_close(o2, l2, o_ref, l_ref, dtype, f"gqa fixed-m Hk={Hk}")
 
 
 def test_fixed_m_bound_and_gate():

@@ -49,9 +49,14 @@ def _visible_py(i, j, Lq, Lk, m):
         if m["segment_ids_q"][i] != m["segment_ids_kv"][j]:
             return False
     pos_k = j + m.get("kv_offset", 0)
-    if m.get("causal") and pos_k > i:
+    if m.get("causal") and pos_k > i and not pos_k < m.get("prefix", 0):
         return False
-    if m.get("window", 0) > 0 and i - pos_k >= m["window"]:
+    if m.get("window", 0) > 0:
+        if m.get("causal") and i - pos_k >= m["window"]:
+            return False
+        if not m.get("causal") and abs(i - pos_k) >= m["window"]:
+            return False
+    if m.get("dilation", 0) >= 2 and (i - pos_k) % m["dilation"] != 0:
         return False
     return True
 
@@ -92,6 +97,19 @@ MASKS = [
     {"cu_seqlens_q": [0, 12, 31], "cu_seqlens_kv": [0, 5, 24], "causal": True},
     {"cu_seqlens_q": [3, 15, 31], "cu_seqlens_kv": [0, 14, 29], "q_valid": 25},
     {"causal": True, "window": 6, "cu_seqlens_q": [0, 10, 31], "cu_seqlens_kv": [0, 10, 31]},
+    {"causal": True, "prefix": 6},
+    {"causal": True, "prefix": 12, "kv_offset": 3},
+    {"causal": True, "prefix": 8, "cu_seqlens_q": [0, 10, 31], "cu_seqlens_kv": [0, 10, 29]},
+    {"window": 4},
+    {"window": 3, "kv_offset": -5},
+    {"causal": True, "window": 9, "dilation": 3},
+    {"causal": True, "window": 12, "dilation": 2, "kv_offset": 2},
+    {"segment_ids_q": [3, 1, 3, 2, 1, 1, 3, 2, 2, 0, 3, 1, 1, 2, 3, 0, 0, 3, 1, 2, 3, 1, 2, 2, 3, 0, 1, 1, 3, 2, 1],
+     "segment_ids_kv": [1, 3, 2, 2, 0, 1, 3, 3, 1, 2, 0, 1, 3, 2, 2, 1, 0, 3, 1, 1, 2, 3, 0, 2, 1, 3, 3, 2, 1],
+     "documents": True},
+    {"segment_ids_q": [0, 1, 0, 1, 2, 2, 0, 1, 0, 2, 1, 1, 0, 0, 2, 1, 2, 0, 1, 0, 2, 2, 1, 0, 1, 0, 2, 1, 0, 1, 2],
+     "segment_ids_kv": [0, 1, 0, 1, 2, 2, 0, 1, 0, 2, 1, 1, 0, 0, 2, 1, 2, 0, 1, 0, 2, 2, 1, 0, 1, 0, 2, 1, 0],
+     "documents": True, "causal": True},
 ]
 
 
@@ -304,6 +322,57 @@ def test_fixed_m_gate_sink_padding_and_promotion():
     assert oracle.fixed_m_bound(q, [k], scale, float(np.float32(mm_t)))[3]
 
 
+def test_new_masks_reduce_to_known_ones():
+    # closed forms of the prefix, two-sided, dilated and document terms
+    L, D = 40, 6
+    q, k, v = _qkv(L, L, D, seed=31)
+    dense = oracle.attention(q, k, v, {}, 0.4)
+    causal = oracle.attention(q, k, v, {"causal": True}, 0.4)
+    # a prefix covering every key is the dense mask; an empty prefix is causal
+    for a, b in ((oracle.attention(q, k, v, {"causal": True, "prefix": L}, 0.4), dense),
+                 (oracle.attention(q, k, v, {"causal": True, "prefix": 0}, 0.4), causal),
+                 # a two-sided band wider than the sequence is the dense mask
+                 (oracle.attention(q, k, v, {"window": L}, 0.4), dense)):
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # the prefix rows: row i < P sees exactly the first P keys (dense on them)
+    P = 15
+    o_p, l_p = oracle.attention(q, k, v, {"causal": True, "prefix": P}, 0.4)
+    o_d, l_d = oracle.attention(q[:P], k[:P], v[:P], {}, 0.4)
+    np.testing.assert_allclose(o_p[:P], o_d, rtol=1e-14, atol=1e-15)
+    # a band of W <= g keys dilated by g: only d = 0, each row its own value
+    o_g, _ = oracle.attention(q, k, v, {"causal": True, "window": 3, "dilation": 3}, 0.4)
+    np.testing.assert_allclose(o_g, v, rtol=1e-14, atol=1e-15)
+    # dilation g over a band of W: exactly the keys i, i-g, ..., i-g*floor((W-1)/g)
+    vis = oracle.visibility(np.arange(L), L, {"causal": True, "window": 10, "dilation": 4}, L)
+    for i in range(L):
+        assert np.flatnonzero(vis[i]).tolist() == [j for j in (i - 8, i - 4, i) if j >= 0]
+    # contiguous non-decreasing ids: the document path equals the segment path
+    ids = np.array([0] * 7 + [1] * 13 + [3] * 20)
+    for causal_ in (False, True):
+        m = {"segment_ids_q": ids, "segment_ids_kv": ids, "causal": causal_}
+        a = oracle.attention(q, k, v, m, 0.4)
+        b = oracle.attention(q, k, v, dict(m, documents=True), 0.4)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # documents: one permutation of tokens, ids and rows permutes the output
+    r = np.random.Generator(np.random.PCG64(32))
+    doc = r.integers(0, 4, size=L)
+    perm = r.permutation(L)
+    o1, l1 = oracle.attention(q, k, v, {"segment_ids_q": doc, "segment_ids_kv": doc, "documents": True}, 0.4)
+    o2, l2 = oracle.attention(q[perm], k[perm], v[perm],
+                              {"segment_ids_q": doc[perm], "segment_ids_kv": doc[perm], "documents": True}, 0.4)
+    np.testing.assert_allclose(o2, o1[perm], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l2, l1[perm], rtol=1e-12, atol=1e-13)
+
+
+def test_kv_head_groups():
+    assert [oracle.kv_head(h, 8, 8) for h in range(8)] == list(range(8))
+    assert [oracle.kv_head(h, 8, 1) for h in range(8)] == [0] * 8
+    assert [oracle.kv_head(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+    assert [oracle.kv_head(h, 6, 3) for h in range(6)] == [0, 0, 1, 1, 2, 2]
+    with pytest.raises(AssertionError):
+        oracle.kv_head(0, 6, 4)
+
+
 # ---------------------------------------------------------------- row intervals
 def _random_masks(n, L, seed):
     r = np.random.Generator(np.random.PCG64(seed))
@@ -312,8 +381,13 @@ def _random_masks(n, L, seed):
         m = {}
         if r.random() < 0.6:
             m["causal"] = True
-            if r.random() < 0.6:
+            u = r.random()
+            if u < 0.5:
                 m["window"] = int(r.integers(1, L // 2))
+            elif u < 0.7:
+                m["prefix"] = int(r.integers(1, L))
+        elif r.random() < 0.4:
+            m["window"] = int(r.integers(1, L // 2))  # two-sided band
         m["kv_offset"] = int(r.integers(-L // 3, L // 3)) if r.random() < 0.4 else 0
         if r.random() < 0.3:
             m["q_valid"] = int(r.integers(0, L + 1))

@@ -250,6 +250,9 @@ def setup_single(torch, bw, synth, name, launch="auto"):
         d = synth.make_long_causal("cuda", packed=name.endswith("packed"))
         desc = ("long_causal: B=1 H=8 D=128 bf16, Lq=Lk=1,048,576 causal"
                 + (", packed segments of U[4096, 131072] tokens" if name.endswith("packed") else ""))
+    elif name in synth.PAGE_MASKS:
+        d = synth.make_page_mask(name, 8192, 8192, "cuda")
+        desc = f"{name}: B=1 H=16 D=128 bf16, Lq=Lk=8192 ({synth.WORKLOADS['page_masks']})"
     else:
         raise ValueError(name)
     q, k, v, scale = d["q"], d["k"], d["v"], d["scale"]
@@ -276,12 +279,15 @@ def setup_single(torch, bw, synth, name, launch="auto"):
         import oracle
         rows = synth.sample_rows(Lq, 64, seed=11, must=[0, Lq - 1])
         m = dict(d["mask"])
+        for key in ("segment_ids_q", "segment_ids_kv"):  # batch element 0
+            if m.get(key) is not None and getattr(m[key], "ndim", 1) == 2:
+                m[key] = m[key][0]
         qh, kh, vh = (x[0, :, 0].double().cpu().numpy() for x in (q, k, v))
         t0 = time.perf_counter()
         oracle.attention_rows(qh, kh, vh, m, scale, rows)
         dt = time.perf_counter() - t0
-        lo, hi = oracle.row_intervals(Lq, Lk, m)
-        fl = 4.0 * D * float(sum(max(0, int(hi[r]) - int(lo[r])) for r in rows))
+        visible = sum(int(oracle.visibility([r], Lk, m, Lq).sum()) for r in rows)
+        fl = 4.0 * D * float(visible)
         return fl, dt, f"head 0, {len(rows)} seeded query rows against their visible keys, fp64"
 
     info = dict(workload=desc, B=B, H=H, D=D, Lq=Lq, Lk=Lk, **launch_info)
@@ -349,7 +355,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dit_share",
-                    choices=["dit_share", "varlen", "window", "long_causal", "long_causal_packed"],
+                    choices=["dit_share", "varlen", "window", "long_causal", "long_causal_packed",
+                             "prefix_lm", "dilated_sliding_window", "document", "two_sided_window"],
                     help="dit_share (default) is the measured configuration; the others time one masked call")
     ap.add_argument("--launch", default="auto", choices=["auto", "plain", "balanced"],
                     help="attention launch; auto: balanced from 4 rounds of query blocks per compute unit up")

@@ -95,8 +95,6 @@ int32_t resolve_mask(const bwa_mask* m, i64 B, i64 lq, i64 lk, bwa::MaskDev& out
     out.dilation = m->dilation > 1 ? m->dilation : 1;
     out.prefix = m->prefix;
     out.seg_mode = cu ? 1 : (ids ? (m->documents ? 3 : 2) : 0);
-    if (out.seg_mode == 3 || out.dilation > 1)
-        return fail(BWA_ERR_UNSUPPORTED, "document ids and dilated bands are not built yet");
     out.num_segments = cu ? m->num_segments : 0;
     out.cu_q = m->cu_seqlens_q;
     out.cu_kv = m->cu_seqlens_kv ? m->cu_seqlens_kv : m->cu_seqlens_q;
@@ -149,10 +147,14 @@ int32_t bwa_block_mask_size(const bwa_mask* mask, int64_t B, int64_t lq, int64_t
     int32_t st = resolve_mask(mask, B, lq, lk, md);
     if (st) return st;
     const i64 nqb = (lq + bq - 1) / bq, nkb = (lk + bkv - 1) / bkv;
-    const i64 per = md.seg_mode ? std::min<i64>(nkb, (i64)bq + 2) : std::min<i64>(nkb, 3);
+    // runs per query block: at most 3 for one interval per row, bq + 2 for
+    // segments (a run pair per segment the block meets), and for dilated
+    // bands and document ids (exact classification) any number up to nkb
+    const bool exact = md.dilation > 1 || md.seg_mode == 3;
+    const i64 per = exact ? nkb : (md.seg_mode ? std::min<i64>(nkb, (i64)bq + 2) : std::min<i64>(nkb, 3));
     *n_qblocks = nqb;
     *capacity = std::max<i64>(nqb * per, 1);
-    *list_batch = md.seg_mode == 2 ? B : 1;
+    *list_batch = md.seg_mode >= 2 ? B : 1;
     return ok();
 }
 
@@ -304,7 +306,7 @@ static int32_t attn_fwd_impl(const bwa_tensor* q, const bwa_tensor* k, const bwa
         if (blocks->lq != Lq || blocks->lk != Lk || blocks->n_qblocks != (Lq + bq - 1) / bq)
             return fail(BWA_ERR_BAD_SHAPE, "blocks describe a different problem size");
         if (blocks->batch != 1 && blocks->batch != B) return fail(BWA_ERR_BAD_SHAPE, "blocks batch must be 1 or B");
-        if (a.mask.seg_mode == 2 && blocks->batch != B)
+        if (a.mask.seg_mode >= 2 && blocks->batch != B)
             return fail(BWA_ERR_BAD_SHAPE, "per-token segment ids need one list copy per batch element");
         if (!blocks->row_ptr || !blocks->run_begin || !blocks->run_end || !blocks->run_kind ||
             (Lq > 0 && (!blocks->row_lo || !blocks->row_hi)))
@@ -353,6 +355,8 @@ static int32_t attn_fwd_impl(const bwa_tensor* q, const bwa_tensor* k, const bwa
     }
     if (bal) {
         if (q->dtype != BWA_BF16) return fail(BWA_ERR_UNSUPPORTED, "the balanced launch computes bf16 inputs only");
+        if (a.mask.dilation > 1 || a.mask.seg_mode == 3)
+            return fail(BWA_ERR_UNSUPPORTED, "the balanced launch takes no dilated bands or document ids");
         const i64 units = B * H * a.n_qblocks;
         const bwa::SplitPlan sp = bwa::split_plan(units, bal->n_cus, Lk);
         const i64 need = bwa::split_workspace_bytes(sp, bq, (int)q->D);

@@ -245,7 +245,10 @@ __device__ inline Walk make_walk(const AttnLaunch& p, i64 b, i64 qb, int mn_lo, 
     w.nruns = 3;
     if (mx_hi == 0) { w.nruns = 0; return w; }  // no row of this block sees anything
     const int t0 = (mn_lo / TILE) * TILE, t1 = mx_hi;
-    const bool all_rows = mx_lo != 0x7fffffff && mn_hi >= 0;
+    // Dilated bands and document ids hide keys inside the intervals: no tile
+    // is known to be full.
+    const bool exact_only = p.mask.dilation > 1 || p.mask.seg_mode == 3;
+    const bool all_rows = !exact_only && mx_lo != 0x7fffffff && mn_hi >= 0;
     const int f0 = all_rows ? ((mx_lo + TILE - 1) / TILE) * TILE : 0;
     const int f1 = all_rows ? (mn_hi / TILE) * TILE : 0;
     if (!all_rows || f0 >= f1) {
@@ -272,6 +275,57 @@ __device__ inline void apply_mask(f32x16 (&s)[NKB], int j0, int lo, int hi) {
             const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
             s[kb][r] = ((unsigned)(off - lo_rel) < span) ? s[kb][r] : kNegInf;
         }
+}
+
+// Dilated bands and document ids: keys inside a row's interval that the
+// element rule still hides (only tiles listed or walked as PARTIAL).  A key j
+// of the interval is visible iff j = row position (mod g) and, with
+// document ids, the key's id equals the row's.
+struct XMask {
+    int g;           // dilation (1 = none)
+    unsigned pat;    // bits 0, g, 2g, ... below 32
+    const int* kid;  // document ids of this batch element's keys, or nullptr
+    int lk;
+};
+
+__device__ inline XMask make_xmask(const AttnLaunch& p, i64 b) {
+    XMask x;
+    x.g = p.mask.dilation;
+    x.pat = 0u;
+    for (int o = 0; o < 32; o += x.g) x.pat |= 1u << o;
+    x.kid = p.mask.seg_mode == 3 ? p.mask.ids_kv + b * p.mask.lk : nullptr;
+    x.lk = (int)p.mask.lk;
+    return x;
+}
+
+// The row's terms: its position mod g, and its document id.
+__device__ inline void xmask_row(const AttnLaunch& p, i64 b, i64 row, bool row_ok, int& xres, int& xdoc) {
+    const int g = p.mask.dilation;
+    const i64 pos = row - p.mask.kv_offset;
+    xres = (int)(((pos % g) + g) % g);
+    xdoc = (row_ok && p.mask.seg_mode == 3) ? p.mask.ids_q[b * p.mask.lq + row] : 0;
+}
+
+// Hide the keys of one 32-key block (first key jb) in the accumulator layout
+// (lane: one query row, keys jb + hb*4 + 8*(r/4) + r%4) that the row cannot see.
+__device__ inline void xmask32(f32x16& s, int jb, int xres, int xdoc, const XMask& xm) {
+    const int hb = (threadIdx.x >> 5) & 1;
+    const int jl = jb + hb * 4;  // the key of r = 0
+    unsigned bits = 0xffffffffu;
+    if (xm.g > 1) {
+        const int m = ((xres - jl % xm.g) % xm.g + xm.g) % xm.g;  // offsets with the row's residue: m, m+g, ...
+        bits = m < 32 ? (xm.pat << m) : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int o = 8 * (r >> 2) + (r & 3);
+        bool ok = (bits >> o) & 1u;
+        if (xm.kid) {
+            const int j = jl + o;
+            ok = ok && j < xm.lk && xm.kid[j] == xdoc;
+        }
+        s[r] = ok ? s[r] : kNegInf;
+    }
 }
 
 template <int NKB, int NDB>
@@ -442,6 +496,7 @@ struct Bf16State {
     f32x16 acc[C::NDB];
     float m_run, l_run, m_fixed, m_l2, scale_l2;
     int lo, hi;
+    int xres, xdoc;  // dilated bands / document ids (the XM kernels only)
 };
 
 // Swizzles of the 16-byte chunk index c of row r.  A 256-byte bank window
@@ -543,9 +598,9 @@ __device__ inline float half_online_ref(const Half& x, float& m_run, float scale
     return alpha;
 }
 
-template <int D, int NW, int BODY>
+template <int D, int NW, int BODY, bool XM>
 __device__ inline void bf16_compute_tile(const uint8_t* kl, const uint8_t* vl, Bf16State<D, NW>& st, int j0,
-                                         bool masked) {
+                                         bool masked, const XMask& xm) {
     using C = Bf16Cfg<D, NW>;
     constexpr int NDS = C::NDS, NDB = C::NDB;
     const int lane = threadIdx.x & 63, l32 = lane & 31, hb = lane >> 5;
@@ -600,7 +655,10 @@ __device__ inline void bf16_compute_tile(const uint8_t* kl, const uint8_t* vl, B
     float ms = st.m_l2;  // fixed-m reference (scaled)
     bool resc = false;
     float alpha = 1.0f;
-    if (masked) half_mask(h0, j0, 0, st.lo, st.hi);
+    if (masked) {
+        half_mask(h0, j0, 0, st.lo, st.hi);
+        if (XM) xmask32(h0.s, j0, st.xres, st.xdoc, xm);
+    }
     uint4 vf[4 * NDB];
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
@@ -626,7 +684,10 @@ __device__ inline void bf16_compute_tile(const uint8_t* kl, const uint8_t* vl, B
     }
     // C: O^T += V^T P^T for keys 0..31 under the softmax of half 1 (its
     // online reference settled under the first step, as above).
-    if (masked) half_mask(h1, j0, 1, st.lo, st.hi);
+    if (masked) {
+        half_mask(h1, j0, 1, st.lo, st.hi);
+        if (XM) xmask32(h1.s, j0 + 32, st.xres, st.xdoc, xm);
+    }
     bool resc1 = false;
     float alpha1 = 1.0f;
 #pragma unroll
@@ -681,12 +742,12 @@ struct Ring {
     uint8_t* v[C::NBUF];
 };
 
-template <int D, int NW, int BODY, int I, class W>
+template <int D, int NW, int BODY, bool XM, int I, class W>
 __device__ __attribute__((always_inline)) inline bool bf16_step(const AttnLaunch& p, Bf16State<D, NW>& st,
                                                                const W& walk, const Ring<D, NW>& ring,
                                                                Cursor<64>& cur, Cursor<64>& ahead, bool& more,
                                                                int& n_after, const __bf16* kbase,
-                                                               const __bf16* vbase, int kv_lim) {
+                                                               const __bf16* vbase, int kv_lim, const XMask& xm) {
     using C = Bf16Cfg<D, NW>;
     constexpr int NB = C::NBUF;
     constexpr int LOADS = 2 * C::RUNS_PER_WAVE;
@@ -702,14 +763,14 @@ __device__ __attribute__((always_inline)) inline bool bf16_step(const AttnLaunch
         bf16_issue_tile<D, NW>(p, kbase, vbase, ahead.j0, kv_lim, ring.k[J], ring.v[J]);
         ++n_after;
     }
-    bf16_compute_tile<D, NW, BODY>(ring.k[I], ring.v[I], st, j0, masked);
+    bf16_compute_tile<D, NW, BODY, XM>(ring.k[I], ring.v[I], st, j0, masked, xm);
     const bool have = cur.next(walk);
     if (have) --n_after;
     return have;
 }
 
 // Every tile of the walk, accumulated into st; the caller stores the result.
-template <int D, int NW, int BODY, class W>
+template <int D, int NW, int BODY, bool XM, class W>
 __device__ inline void bf16_walk(const AttnLaunch& p, Bf16State<D, NW>& st, const W& walk,
                                  const Ring<D, NW>& ring, i64 b, i64 h) {
     using C = Bf16Cfg<D, NW>;
@@ -720,6 +781,8 @@ __device__ inline void bf16_walk(const AttnLaunch& p, Bf16State<D, NW>& st, cons
     const __bf16* kbase = (const __bf16*)p.k + b * p.k_sB + hk * p.k_sH;
     const __bf16* vbase = (const __bf16*)p.v + b * p.v_sB + hk * p.v_sH;
     const int kv_lim = (int)p.mask.kv_valid;
+    XMask xm{1, 0u, nullptr, 0};
+    if (XM) xm = make_xmask(p, b);
     // Copies run NB - 1 tiles ahead of the compute.
     Cursor<C::TILE> cur, ahead;
     bool have = cur.next(walk);
@@ -735,25 +798,27 @@ __device__ inline void bf16_walk(const AttnLaunch& p, Bf16State<D, NW>& st, cons
         }
     }
     while (have) {
-        have = bf16_step<D, NW, BODY, 0>(p, st, walk, ring, cur, ahead, more, n_after, kbase, vbase, kv_lim);
+        have = bf16_step<D, NW, BODY, XM, 0>(p, st, walk, ring, cur, ahead, more, n_after, kbase, vbase, kv_lim,
+                                             xm);
         if (!have) break;
-        have = bf16_step<D, NW, BODY, 1>(p, st, walk, ring, cur, ahead, more, n_after, kbase, vbase, kv_lim);
+        have = bf16_step<D, NW, BODY, XM, 1>(p, st, walk, ring, cur, ahead, more, n_after, kbase, vbase, kv_lim,
+                                             xm);
         if (NB == 3) {
             if (!have) break;
-            have = bf16_step<D, NW, BODY, NB - 1>(p, st, walk, ring, cur, ahead, more, n_after, kbase, vbase,
-                                                  kv_lim);
+            have = bf16_step<D, NW, BODY, XM, NB - 1>(p, st, walk, ring, cur, ahead, more, n_after, kbase, vbase,
+                                                      kv_lim, xm);
         }
     }
 }
 
-template <int D, int NW, int BODY, int OUT>
+template <int D, int NW, int BODY, int OUT, bool XM>
 __device__ inline void bf16_run(const AttnLaunch& p, Bf16State<D, NW>& st, const Walk& walk,
                                 const Ring<D, NW>& ring, i64 b, i64 h, i64 row) {
-    bf16_walk<D, NW, BODY>(p, st, walk, ring, b, h);
+    bf16_walk<D, NW, BODY, XM>(p, st, walk, ring, b, h);
     store_out<D, OUT, BODY>(p, st.acc, st.m_run, st.l_run, st.m_fixed, b, h, row);
 }
 
-template <int D, int NW, int MODE, int OUT>
+template <int D, int NW, int MODE, int OUT, bool XM>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_bf16(const AttnLaunch p) {
     using C = Bf16Cfg<D, NW>;
     __shared__ __attribute__((aligned(1024))) uint8_t k0[C::TILE_BYTES], v0[C::TILE_BYTES];
@@ -809,16 +874,19 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_bf16(const 
         st.m_l2 = st.m_fixed * kLog2e;
     }
     st.scale_l2 = p.scale * kLog2e;
+    st.xres = 0;
+    st.xdoc = 0;
+    if (XM) xmask_row(p, b, row, row_ok, st.xres, st.xdoc);
 
     const bool ne = row_ok && lo < hi;
     const Walk walk = make_walk<C::TILE, C::NT>(p, b, qb, ne ? lo : 0x7fffffff, ne ? hi : 0,
                                                 row_ok ? (ne ? lo : 0x7fffffff) : 0,
                                                 row_ok ? (ne ? hi : -1) : 0x7fffffff, red);
     if (MODE == MODE_GATED) {
-        if (fixed) bf16_run<D, NW, BODY_FIXED, OUT>(p, st, walk, ring, b, h, row);
-        else bf16_run<D, NW, BODY_ONLINE, OUT>(p, st, walk, ring, b, h, row);
+        if (fixed) bf16_run<D, NW, BODY_FIXED, OUT, XM>(p, st, walk, ring, b, h, row);
+        else bf16_run<D, NW, BODY_ONLINE, OUT, XM>(p, st, walk, ring, b, h, row);
     } else {
-        bf16_run<D, NW, MODE, OUT>(p, st, walk, ring, b, h, row);
+        bf16_run<D, NW, MODE, OUT, XM>(p, st, walk, ring, b, h, row);
     }
 }
 
@@ -906,7 +974,7 @@ __device__ inline void bal_item(const AttnLaunch& p, const Ring<D, NW>& ring, in
         const i64 n = walk_tiles(walk, C::TILE);
         const int s = piece < 0 ? 1 : p.split_s;
         const int c = piece < 0 ? 0 : piece;
-        bf16_walk<D, NW, BODY>(p, st, clip_walk<C::TILE>(walk, c * n / s, (c + 1) * n / s), ring, b, h);
+        bf16_walk<D, NW, BODY, false>(p, st, clip_walk<C::TILE>(walk, c * n / s, (c + 1) * n / s), ring, b, h);
         if (piece < 0) {
             store_out<D, OUT, BODY>(p, st.acc, st.m_run, st.l_run, st.m_fixed, b, h, row);
         } else {
@@ -1035,7 +1103,7 @@ __global__ __launch_bounds__(NW * 64) void merge_pieces_kernel(const AttnLaunch 
 // ---------------------------------------------------------------------------
 // fp32 kernel: 32-key tiles, 32x32x2 fp32 MFMA, no reduced-precision step.
 // ---------------------------------------------------------------------------
-template <int D, int BODY, int OUT>
+template <int D, int BODY, int OUT, bool XM>
 __device__ inline void f32_run(const AttnLaunch& p, const Walk& walk, float* ks, float* vs, const float (&qf)[D / 2],
                                int lo, int hi, float m_fixed, i64 b, i64 h, i64 row) {
     constexpr int TILE = 32, NDB = D / 32, LD = D + 1;
@@ -1049,6 +1117,12 @@ __device__ inline void f32_run(const AttnLaunch& p, const Walk& walk, float* ks,
     const float* kbase = (const float*)p.k + b * p.k_sB + hk * p.k_sH;
     const float* vbase = (const float*)p.v + b * p.v_sB + hk * p.v_sH;
     const int kv_lim = (int)p.mask.kv_valid;
+    XMask xm{1, 0u, nullptr, 0};
+    int xres = 0, xdoc = 0;
+    if (XM) {
+        xm = make_xmask(p, b);
+        xmask_row(p, b, row, row < p.Lq, xres, xdoc);
+    }
     Cursor<TILE> cur;
     while (cur.next(walk)) {
         const int j0 = cur.j0;
@@ -1072,7 +1146,10 @@ __device__ inline void f32_run(const AttnLaunch& p, const Walk& walk, float* ks,
 #pragma unroll
         for (int ds = 0; ds < D / 2; ++ds)
             s[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[l32 * LD + ds * 2 + hb], qf[ds], s[0], 0, 0, 0);
-        if (cur.masked(walk.Lk)) apply_mask<1>(s, j0, lo, hi);
+        if (cur.masked(walk.Lk)) {
+            apply_mask<1>(s, j0, lo, hi);
+            if (XM) xmask32(s[0], j0, xres, xdoc, xm);
+        }
         if (BODY == BODY_FIXED) fixed_update<1>(s, l_run, scale_l2, m_l2);
         else online_update<1, NDB>(s, acc, m_run, l_run, scale_l2);
 #pragma unroll
@@ -1086,7 +1163,7 @@ __device__ inline void f32_run(const AttnLaunch& p, const Walk& walk, float* ks,
     store_out<D, OUT, BODY>(p, acc, m_run, l_run, m_fixed, b, h, row);
 }
 
-template <int D, int MODE, int OUT>
+template <int D, int MODE, int OUT, bool XM>
 __global__ __launch_bounds__(256, 1) void attn_fwd_f32(const AttnLaunch p) {
     constexpr int TILE = 32, LD = D + 1;
     __shared__ float ks[TILE * LD];
@@ -1125,8 +1202,8 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_f32(const AttnLaunch p) {
     const Walk walk = make_walk<TILE, 256>(p, b, qb, ne ? lo : 0x7fffffff, ne ? hi : 0,
                                            row_ok ? (ne ? lo : 0x7fffffff) : 0,
                                            row_ok ? (ne ? hi : -1) : 0x7fffffff, red);
-    if (fixed) f32_run<D, BODY_FIXED, OUT>(p, walk, ks, vs, qf, lo, hi, m_fixed, b, h, row);
-    else f32_run<D, BODY_ONLINE, OUT>(p, walk, ks, vs, qf, lo, hi, m_fixed, b, h, row);
+    if (fixed) f32_run<D, BODY_FIXED, OUT, XM>(p, walk, ks, vs, qf, lo, hi, m_fixed, b, h, row);
+    else f32_run<D, BODY_ONLINE, OUT, XM>(p, walk, ks, vs, qf, lo, hi, m_fixed, b, h, row);
 }
 
 template <int D, int MODE, int OUT>
@@ -1143,11 +1220,19 @@ hipError_t launch_one(const AttnLaunch& a, hipStream_t stream) {
                                stream, a);
         return hipGetLastError();
     }
+    // Dilated bands and document ids take the kernels with the element test.
+    const bool xm = a.mask.dilation > 1 || a.mask.seg_mode == 3;
     if (a.in_dtype == BWA_BF16) {
         constexpr int NW = kBf16Waves;
-        hipLaunchKernelGGL((attn_fwd_bf16<D, NW, MODE, OUT>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, a);
+        if (xm)
+            hipLaunchKernelGGL((attn_fwd_bf16<D, NW, MODE, OUT, true>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((attn_fwd_bf16<D, NW, MODE, OUT, false>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                               stream, a);
     } else {
-        hipLaunchKernelGGL((attn_fwd_f32<D, MODE, OUT>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+        if (xm) hipLaunchKernelGGL((attn_fwd_f32<D, MODE, OUT, true>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((attn_fwd_f32<D, MODE, OUT, false>), dim3((unsigned)grid), dim3(256), 0, stream, a);
     }
     return hipGetLastError();
 }

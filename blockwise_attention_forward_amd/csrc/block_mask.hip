@@ -130,6 +130,117 @@ __global__ __launch_bounds__(256) void runs_kernel(const BlocksLaunch a) {
     if (!FILL && lane == 0) rp[qb + 1] = n;
 }
 
+// Masks whose visible keys are not one interval per row (dilated bands,
+// document ids in any order): every key block that meets the union of the
+// block's row intervals is classified from the element rule, so the lists
+// stay exact.  A row sees a key of the block iff one of its interval's keys
+// there passes the dilation test (j = row position mod g) and has the row's
+// document id; the block is FULL iff every row of the block sees every key
+// of it.  One wavefront per (copy, query block) as above.
+template <bool FILL>
+__global__ __launch_bounds__(256) void runs_exact_kernel(const BlocksLaunch a) {
+    const i64 wg = (i64)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const i64 nqb = a.n_qblocks;
+    if (wg >= a.copies * nqb) return;
+    const int lane = threadIdx.x & 63;
+    const i64 copy = wg / nqb, qb = wg % nqb;
+    const MaskDev& m = a.mask;
+    const i64 lq = m.lq, lk = m.lk;
+    const int g = m.dilation;
+    const bool docs = m.seg_mode == 3;
+    const int* kid = docs ? m.ids_kv + copy * lk : nullptr;
+    const int per_lane = a.bq / 64;
+    int rlo[kMaxRowsPerLane], rhi[kMaxRowsPerLane], rres[kMaxRowsPerLane], rdoc[kMaxRowsPerLane];
+    bool rex[kMaxRowsPerLane];
+    int mn_lo = 0x7fffffff, mx_hi = 0;
+#pragma unroll
+    for (int t = 0; t < kMaxRowsPerLane; ++t) {
+        const i64 r = qb * a.bq + lane + 64 * t;
+        rex[t] = t < per_lane && r < lq;
+        rlo[t] = rex[t] ? a.row_lo[copy * lq + r] : 0;
+        rhi[t] = rex[t] ? a.row_hi[copy * lq + r] : 0;
+        // the residue mod g of the keys this row can see: (r - kv_offset) mod g
+        const i64 pos = r - m.kv_offset;
+        rres[t] = (int)(((pos % g) + g) % g);
+        rdoc[t] = (rex[t] && docs) ? m.ids_q[copy * lq + r] : 0;
+        if (rex[t] && rlo[t] < rhi[t]) { mn_lo = min(mn_lo, rlo[t]); mx_hi = max(mx_hi, rhi[t]); }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        mn_lo = min(mn_lo, __shfl_xor(mn_lo, o));
+        mx_hi = max(mx_hi, __shfl_xor(mx_hi, o));
+    }
+    i64* rp = a.row_ptr + copy * (nqb + 1);
+    const i64 out = FILL ? rp[qb] : 0;
+    i64 n = 0;
+    int cur_kind = 0, cur_b = 0, cur_e = 0;
+    auto emit = [&]() {
+        if (FILL && lane == 0) {
+            const i64 slot = out + n;
+            if (slot < a.capacity) {
+                a.run_begin[copy * a.capacity + slot] = cur_b;
+                a.run_end[copy * a.capacity + slot] = cur_e;
+                a.run_kind[copy * a.capacity + slot] = (uint8_t)cur_kind;
+            }
+        }
+        ++n;
+    };
+    if (mx_hi > 0) {
+        const int kb_lo = mn_lo / a.bkv;
+        const int kb_hi = (int)((mx_hi + (i64)a.bkv - 1) / a.bkv);
+        for (int kb = kb_lo; kb < kb_hi; ++kb) {
+            const int j0 = kb * a.bkv, j1 = (int)min((i64)j0 + a.bkv, lk);
+            // document ids of the block's keys: their range, for quick tests
+            int dmin = 0x7fffffff, dmax = (int)0x80000000;
+            if (docs) {
+                for (int j = j0 + lane; j < j1; j += 64) {
+                    dmin = min(dmin, kid[j]);
+                    dmax = max(dmax, kid[j]);
+                }
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) {
+                    dmin = min(dmin, __shfl_xor(dmin, o));
+                    dmax = max(dmax, __shfl_xor(dmax, o));
+                }
+            }
+            bool sees = false, misses = false;  // some row sees a key / some row misses a key
+#pragma unroll
+            for (int t = 0; t < kMaxRowsPerLane; ++t) {
+                if (!rex[t]) continue;
+                const int lo = max(rlo[t], j0), hi = min(rhi[t], j1);
+                bool vis = false;
+                if (lo < hi && (!docs || (rdoc[t] >= dmin && rdoc[t] <= dmax))) {
+                    // first key >= lo with the row's residue, then every g-th
+                    int j = lo + ((rres[t] - lo % g) % g + g) % g;
+                    if (!docs) {
+                        vis = j < hi;
+                    } else {
+                        for (; j < hi && !vis; j += g) vis = kid[j] == rdoc[t];
+                    }
+                }
+                sees |= vis;
+                // FULL needs every key of the block: all in the interval, all
+                // with the residue (one key when g > 1), all with the row's id
+                const bool full = rlo[t] <= j0 && rhi[t] >= j1 && (g == 1 || (j1 - j0 == 1 && j0 % g == rres[t])) &&
+                                  (!docs || (dmin == rdoc[t] && dmax == rdoc[t]));
+                misses |= !full;
+            }
+            const int kind = __ballot(sees) == 0 ? BWA_TILE_SKIP
+                             : (__ballot(misses) == 0 ? BWA_TILE_FULL : BWA_TILE_PARTIAL);
+            if (kind == BWA_TILE_SKIP) {
+                if (cur_kind) { emit(); cur_kind = 0; }
+            } else if (cur_kind == kind && cur_e == kb) {
+                cur_e = kb + 1;
+            } else {
+                if (cur_kind) emit();
+                cur_kind = kind; cur_b = kb; cur_e = kb + 1;
+            }
+        }
+        if (cur_kind) emit();
+    }
+    if (!FILL && lane == 0) rp[qb + 1] = n;
+}
+
 // In-place inclusive scan of row_ptr[1..nqb] (counts) -> CSR offsets;
 // row_ptr[0] = 0.  One workgroup per list copy.
 __global__ __launch_bounds__(1024) void scan_kernel(const BlocksLaunch a) {
@@ -162,10 +273,17 @@ hipError_t launch_block_mask_build(const BlocksLaunch& a, hipStream_t stream) {
         hipLaunchKernelGGL(rows_kernel, dim3((unsigned)((nrows + 255) / 256)), dim3(256), 0, stream, a);
     const i64 waves = a.copies * a.n_qblocks;
     const unsigned grid = (unsigned)((waves + 3) / 4);
-    if (waves > 0) hipLaunchKernelGGL(runs_kernel<false>, dim3(grid), dim3(256), 0, stream, a);
+    const bool exact = a.mask.dilation > 1 || a.mask.seg_mode == 3;
+    if (waves > 0) {
+        if (exact) hipLaunchKernelGGL(runs_exact_kernel<false>, dim3(grid), dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL(runs_kernel<false>, dim3(grid), dim3(256), 0, stream, a);
+    }
     if (a.copies > 0)
         hipLaunchKernelGGL(scan_kernel, dim3((unsigned)a.copies), dim3(1024), 0, stream, a);
-    if (waves > 0) hipLaunchKernelGGL(runs_kernel<true>, dim3(grid), dim3(256), 0, stream, a);
+    if (waves > 0) {
+        if (exact) hipLaunchKernelGGL(runs_exact_kernel<true>, dim3(grid), dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL(runs_kernel<true>, dim3(grid), dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

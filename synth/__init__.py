@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 __all__ = [
-    "WORKLOADS", "normal", "make_tiny", "make_varlen", "make_window",
+    "WORKLOADS", "normal", "make_tiny", "make_varlen", "make_window", "make_page_mask", "PAGE_MASKS",
     "make_dit_share", "make_long_causal", "long_causal_segments",
     "sample_rows", "rope_3axis",
 ]
@@ -34,7 +34,15 @@ WORKLOADS = {
                  "latent tokens), 3-axis RoPE on q/k, per-head k scale U[0.5, 2], optional sink head",
     "long_causal": "B=1 H=8 D=128 bf16, Lq=Lk=1,048,576 causal; single segment or packed "
                    "segments of U[4096, 131072] tokens",
+    "page_masks": "B=1 H=16 D=128 bf16, Lq x Lk in {4096x4096, 4096x8192, 8192x8192}: prefix_lm "
+                  "(prefix: the positions of the first Lq/4 queries), dilated_sliding_window (W 1024, dilation 4), document (64-token "
+                  "chunks dealt to 8 documents at random), two-sided band (W 1024)",
 }
+
+# The flash-attention block-sparse tables ("Add more optimal dk order optional
+# arg") time these masks at these shapes without giving their parameters;
+# the parameters here are this package's choice.
+PAGE_MASKS = ("prefix_lm", "dilated_sliding_window", "document", "two_sided_window")
 
 
 def _gen(seed, device):
@@ -91,6 +99,34 @@ def make_window(Lq, Lk, window, device="cpu", seed=1002, H=16, D=128):
     k = normal((1, Lk, H, D), seed + 1, device)
     v = normal((1, Lk, H, D), seed + 2, device)
     mask = dict(causal=True, window=int(window), kv_offset=int(Lq - Lk))
+    return dict(q=q, k=k, v=v, mask=mask, scale=1.0 / math.sqrt(D))
+
+
+def make_page_mask(kind, Lq, Lk, device="cpu", seed=1006, H=16, D=128):
+    """One of the named masks of the flash-attention tables at ``Lq x Lk``.
+
+    Causal masks are bottom-right aligned (``kv_offset = Lq - Lk``).
+    ``document`` deals 64-token chunks of both sequences to 8 documents at
+    random (a document's tokens are not contiguous); the ids are [1, L].
+    """
+    q = normal((1, Lq, H, D), seed, device)
+    k = normal((1, Lk, H, D), seed + 1, device)
+    v = normal((1, Lk, H, D), seed + 2, device)
+    off = int(Lq - Lk)
+    if kind == "prefix_lm":
+        mask = dict(causal=True, kv_offset=off, prefix=Lq // 4)  # positions of the first quarter of the queries
+    elif kind == "dilated_sliding_window":
+        mask = dict(causal=True, kv_offset=off, window=1024, dilation=4)
+    elif kind == "document":
+        rng = np.random.Generator(np.random.PCG64(seed + 3))
+        ids_q = np.repeat(rng.integers(0, 8, size=(Lq + 63) // 64), 64)[:Lq]
+        ids_k = np.repeat(rng.integers(0, 8, size=(Lk + 63) // 64), 64)[:Lk]
+        mask = dict(segment_ids_q=ids_q[None].astype(np.int32), segment_ids_kv=ids_k[None].astype(np.int32),
+                    documents=True)
+    elif kind == "two_sided_window":
+        mask = dict(window=1024, kv_offset=off)
+    else:
+        raise ValueError(kind)
     return dict(q=q, k=k, v=v, mask=mask, scale=1.0 / math.sqrt(D))
 
 

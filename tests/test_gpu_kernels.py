@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from helpers import assert_close, np64, oracle_attention
+from helpers import assert_close, mask_for_batch, np64, oracle_attention
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +42,9 @@ def test_tiny_fp32_dense_and_chunk_merge():
     assert_close(om, lm, o_ref, l_ref, torch.float32, "tiny fp32 merged")
 
 
+# document ids in any order, one row per batch element (two elements)
+_DOCS = np.random.Generator(np.random.PCG64(404)).integers(0, 4, size=(2, 333)).astype(np.int32)
+
 MASKS = [
     {},
     {"causal": True},
@@ -59,7 +62,22 @@ MASKS = [
     {"causal": True, "prefix": 300, "kv_offset": 40, "q_valid": 320},
     {"window": 60},                                       # two-sided band
     {"window": 50, "kv_offset": -40, "kv_valid": 310},
+    {"causal": True, "window": 90, "dilation": 3},        # dilated band
+    {"causal": True, "window": 200, "dilation": 70, "kv_offset": 20},
+    {"segment_ids_q": _DOCS, "segment_ids_kv": _DOCS, "documents": True},
+    {"segment_ids_q": _DOCS, "segment_ids_kv": _DOCS, "documents": True, "causal": True, "q_valid": 300},
 ]
+
+
+def _contiguous_part(mask):
+    """The terms of a mask that bound each row's keys to one interval: what
+    the library's per-row intervals hold (dilation and document ids drop)."""
+    m = dict(mask)
+    m.pop("dilation", None)
+    if m.pop("documents", False):
+        m.pop("segment_ids_q", None)
+        m.pop("segment_ids_kv", None)
+    return m
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
@@ -127,10 +145,11 @@ def test_block_lists_bit_exact(mi, bq, bkv):
     Lq = Lk = 333
     bl = bw.bwa_block_mask_build(mask, 1, Lq, Lk, bq, bkv)
     rp, b, e, k = bl.host()
-    want = oracle.block_lists(mask, Lq, Lk, bq, bkv)
+    m0 = mask_for_batch(mask, 0)
+    want = oracle.block_lists(m0, Lq, Lk, bq, bkv)
     assert np.array_equal(rp, want[0]) and np.array_equal(b, want[1])
     assert np.array_equal(e, want[2]) and np.array_equal(k, want[3])
-    lo, hi = oracle.row_intervals_bruteforce(Lq, Lk, mask)
+    lo, hi = oracle.row_intervals_bruteforce(Lq, Lk, _contiguous_part(m0))
     assert np.array_equal(bl.row_lo[:Lq].cpu().numpy(), lo)
     assert np.array_equal(bl.row_hi[:Lq].cpu().numpy(), hi)
 
@@ -165,6 +184,24 @@ def test_grouped_query_heads(Hk, dtype):
             assert bool(gate[b, h].item()) == gh
     o2, l2 = bw.bwa_attn_fwd(q, k, v, mask, scale=scale, mode=bw.BWA_MODE_FIXED_M, m=m, out_dtype=torch.float32)
     assert_close(o2, l2, o_ref, l_ref, dtype, f"gqa fixed-m Hk={Hk}")
+
+
+def test_document_lists_per_batch_and_balanced_refusal():
+    # document ids differ per batch element: one list copy each; the balanced
+    # launch does not take element-test masks
+    B, H, L, D = 2, 2, 333, 128
+    mask = {"segment_ids_q": _DOCS, "segment_ids_kv": _DOCS, "documents": True, "causal": True}
+    bq, _ = bw.bwa_attn_tile(torch.bfloat16, D)
+    bl = bw.bwa_block_mask_build(mask, B, L, L, bq, 64)
+    assert bl.struct.batch == B
+    for b in range(B):
+        rp, be, en, kd = bl.host(b)
+        want = oracle.block_lists(mask_for_batch(mask, b), L, L, bq, 64)
+        assert all(np.array_equal(x, y) for x, y in zip((rp, be, en, kd), want))
+    q, k, v = (_rand((B, L, H, D), 70 + s, torch.bfloat16) for s in range(3))
+    with pytest.raises(bw.BwaError) as e:
+        bw.bwa_attn_fwd_balanced(q, k, v, mask, blocks=bl, n_cus=16)
+    assert e.value.status == 6
 
 
 def test_fixed_m_bound_and_gate():

@@ -8,6 +8,8 @@ Workloads (synthetic stand-ins for the pages' models and data, see synth):
              fixed-m with a sink head on online fallback, LSE merge), with the
              plain and the balanced launch (the bench's)
   * long     1,048,576-token causal attention, single segment and packed
+  * page     the flash-attention tables' named masks (prefix_lm, dilated
+             sliding window, document) and a two-sided band at their shapes
 
 Large outputs are checked on a seeded sample of 512 query rows per head
 (always holding the first and last valid rows, segment-boundary rows and an
@@ -23,7 +25,7 @@ import torch
 
 import oracle
 import synth
-from helpers import assert_close, gpu_rows, np64, oracle_attention
+from helpers import assert_close, gpu_rows, mask_for_batch, np64, oracle_attention
 
 pytestmark = pytest.mark.gpu
 
@@ -118,6 +120,29 @@ def test_sliding_window(Lq, Lk, W):
 
 
 # ------------------------------------------------------------------- dit share
+# ------------------------------------------------------------- page masks
+@pytest.mark.parametrize("kind", synth.PAGE_MASKS)
+@pytest.mark.parametrize("Lq,Lk", [(4096, 4096), (4096, 8192), (8192, 8192)])
+def test_page_masks(kind, Lq, Lk):
+    # the flash-attention tables' prefix_lm, dilated_sliding_window and
+    # document masks (and a two-sided band) at their shapes: run lists exact,
+    # sampled rows against the oracle, run lists and inline walk bit-equal
+    w = synth.make_page_mask(kind, Lq, Lk, DEV)
+    q, k, v, mask, scale = w["q"], w["k"], w["v"], w["mask"], w["scale"]
+    m0 = mask_for_batch(mask, 0)
+    bq, _ = bw.bwa_attn_tile(BF16, 128)
+    blocks = bw.bwa_block_mask_build(mask, 1, Lq, Lk, bq, 128)
+    rp, be, en, kd = blocks.host()
+    want = oracle.block_lists(m0, Lq, Lk, bq, 128)
+    assert all(np.array_equal(x, y) for x, y in zip((rp, be, en, kd), want))
+    o, l = bw.bwa_attn_fwd(q, k, v, mask, blocks=blocks, scale=scale)
+    o2, l2 = bw.bwa_attn_fwd(q, k, v, mask, scale=scale)
+    assert torch.equal(o, o2) and torch.equal(l, l2)
+    rows = synth.sample_rows(Lq, 256, seed=29, must=[0, 1, 63, 64, Lq // 4 - 1, Lq // 4, Lq - 1])
+    o_ref, l_ref = oracle_attention(q, k, v, m0, scale, rows)
+    assert_close(*gpu_rows(o, l, rows), o_ref, l_ref, BF16, f"{kind} {Lq}x{Lk}")
+
+
 @pytest.fixture(scope="module")
 def dit():
     return synth.make_dit_share(DEV)

@@ -120,14 +120,21 @@ def _launcher(torch, bw, launch, q, lk, units):
     if launch == "auto":
         launch = "balanced" if units >= 4 * n_cus else "plain"
     if launch == "plain":
-        return bw.bwa_attn_fwd, {"launch": "plain", "units": units}
+        def carry(q, k, v, o_prev, lse_prev, mask=None, blocks=None, **kw):
+            return bw.bwa_attn_fwd_carry(q, k, v, o_prev, lse_prev, mask, blocks=blocks, **kw)
+        return bw.bwa_attn_fwd, carry, {"launch": "plain", "units": units}
     B, Lq, H, D = q.shape
     nbytes, cut, pieces = bw.bwa_attn_fwd_balanced_workspace(q.dtype, B, H, Lq, lk, D, plan=True)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
 
     def call(q, k, v, mask=None, blocks=None, **kw):
         return bw.bwa_attn_fwd_balanced(q, k, v, mask, blocks=blocks, workspace=ws, **kw)
-    return call, {"launch": "balanced", "units": units, "workgroups": n_cus, "cut_units": cut, "pieces": pieces}
+
+    def carry(q, k, v, o_prev, lse_prev, mask=None, blocks=None, **kw):
+        return bw.bwa_attn_fwd_balanced(q, k, v, mask, blocks=blocks, workspace=ws, o_prev=o_prev,
+                                        lse_prev=lse_prev, **kw)
+    return call, carry, {"launch": "balanced", "units": units, "workgroups": n_cus, "cut_units": cut,
+                         "pieces": pieces}
 
 
 def setup_dit_share(torch, bw, synth, launch="auto"):
@@ -149,7 +156,7 @@ def setup_dit_share(torch, bw, synth, launch="auto"):
     torch.cuda.synchronize()
     flops_hop = _counted_flops(count_lists, D, H, Lq, Lc)
     gate_host = None
-    attn, launch_info = _launcher(torch, bw, launch, q, Lc, B * H * ((Lq + bq - 1) // bq))
+    attn, attn_carry, launch_info = _launcher(torch, bw, launch, q, Lc, B * H * ((Lq + bq - 1) // bq))
 
     def step(timer=None):
         for t, m in enumerate(masks):
@@ -177,16 +184,16 @@ def setup_dit_share(torch, bw, synth, launch="auto"):
             bw.bwa_block_mask_build(m, B, Lq, Lc, bq, 128, out=blocks[t])
         kmax, mmax, mm, gate = bw.bwa_fixed_m_bound(q, ks, scale, tau, out=bound_out)
         tok = timer.start("hop0") if timer else None
-        bw.bwa_attn_fwd(q, ks[0], vs[0], m=mm, mask=masks[0], blocks=blocks[0], scale=scale,
-                        mode=bw.BWA_MODE_GATED, gate=gate, o=o_parts[0], lse=l_parts[0])
+        attn(q, ks[0], vs[0], m=mm, mask=masks[0], blocks=blocks[0], scale=scale,
+             mode=bw.BWA_MODE_GATED, gate=gate, o=o_parts[0], lse=l_parts[0])
         if timer:
             timer.stop(tok)
         for t in range(1, len(ks)):
             last = t == len(ks) - 1
             tok = timer.start("hop_carry") if timer else None
-            bw.bwa_attn_fwd_carry(q, ks[t], vs[t], o_parts[0], l_parts[0], m=mm, mask=masks[t], blocks=blocks[t],
-                                  scale=scale, mode=bw.BWA_MODE_GATED, gate=gate,
-                                  o=o_out if last else o_parts[0], lse=l_out if last else l_parts[0])
+            attn_carry(q, ks[t], vs[t], o_parts[0], l_parts[0], m=mm, mask=masks[t], blocks=blocks[t],
+                       scale=scale, mode=bw.BWA_MODE_GATED, gate=gate,
+                       o=o_out if last else o_parts[0], lse=l_out if last else l_parts[0])
             if timer:
                 timer.stop(tok)
 
@@ -266,7 +273,7 @@ def setup_single(torch, bw, synth, name, launch="auto"):
     lse = torch.empty(B, H, Lq, device="cuda")
     torch.cuda.synchronize()
     flops = _counted_flops(count_lists, D, H, Lq, Lk)
-    attn, launch_info = _launcher(torch, bw, launch, q, Lk, B * H * ((Lq + bq - 1) // bq))
+    attn, _, launch_info = _launcher(torch, bw, launch, q, Lk, B * H * ((Lq + bq - 1) // bq))
 
     def step(timer=None):
         bw.bwa_block_mask_build(mask, B, Lq, Lk, bq, 128, out=blocks)
@@ -459,7 +466,7 @@ def main():
         "ms_per_kv_hop": round(ms_hop, 4),
         "online_only_ms_per_kv_hop": round(ms_online_hop, 4),
         "fixed_m_all_heads_ms_per_kv_hop": round(ms_fixed_hop, 4),
-        "carried_hops": {"launch": "plain", "ms_per_step": round(ms_step_carry, 4),
+        "carried_hops": {"launch": W["launch"], "ms_per_step": round(ms_step_carry, 4),
                          "TFLOPs": round(W["flops_step"] / (ms_step_carry * 1e-3) / 1e12, 2),
                          "ms_hop0": round(t3.mean_ms("hop0"), 4),
                          "ms_carry_hop": round(t3.mean_ms("hop_carry"), 4)},

@@ -21,6 +21,7 @@ __all__ = [
     "lib_path", "bwa_version", "bwa_status_string", "bwa_last_error", "bwa_attn_tile",
     "bwa_block_mask_size", "bwa_block_mask_build", "bwa_fixed_m_bound", "bwa_attn_fwd",
     "bwa_attn_fwd_carry", "bwa_attn_fwd_balanced", "bwa_attn_fwd_balanced_workspace", "bwa_lse_merge",
+    "bwa_attn_fwd_balanced_carry",
 ]
 
 BWA_F32, BWA_BF16 = 0, 1
@@ -79,6 +80,7 @@ def _load():
         "bwa_attn_fwd": (I32, [TP, TP, TP, MP, BP, F32, I32, P, P, TP, P, P]),
         "bwa_attn_fwd_carry": (I32, [TP, TP, TP, MP, BP, F32, I32, P, P, TP, P, TP, P, P]),
         "bwa_attn_fwd_balanced": (I32, [TP, TP, TP, MP, BP, F32, I32, P, P, I32, P, I64, TP, P, P]),
+        "bwa_attn_fwd_balanced_carry": (I32, [TP, TP, TP, MP, BP, F32, I32, P, P, TP, P, I32, P, I64, TP, P, P]),
         "bwa_attn_fwd_balanced_workspace": (I32, [I32, I64, I64, I64, I64, I64, I32, I64P, I64P, I32P]),
         "bwa_lse_merge": (I32, [I32, TP, ctypes.POINTER(ctypes.c_void_p), TP, P, P]),
     }
@@ -303,12 +305,13 @@ def bwa_attn_fwd_balanced_workspace(dtype, B, H, Lq, Lk, D, n_cus=0, plan=False)
 
 
 def bwa_attn_fwd_balanced(q, k, v, mask=None, blocks=None, scale=None, mode=BWA_MODE_ONLINE, m=None, gate=None,
-                          n_cus=0, workspace=None, o=None, lse=None, out_dtype=None):
+                          n_cus=0, workspace=None, o=None, lse=None, out_dtype=None, o_prev=None, lse_prev=None):
     """bwa_attn_fwd with one workgroup per compute unit taking whole query
     blocks and then pieces of the last ones from a queue (bf16 inputs).
     workspace: a uint8 device tensor of at least
-    bwa_attn_fwd_balanced_workspace bytes (allocated here if None).
-    Returns (o, lse)."""
+    bwa_attn_fwd_balanced_workspace bytes (allocated here if None).  With
+    o_prev / lse_prev, the carried partial is merged as in
+    bwa_attn_fwd_carry (bwa_attn_fwd_balanced_carry).  Returns (o, lse)."""
     B, Lq, H, D = q.shape
     if scale is None:
         scale = D ** -0.5
@@ -323,6 +326,14 @@ def bwa_attn_fwd_balanced(q, k, v, mask=None, blocks=None, scale=None, mode=BWA_
     qt, kt, vt, ot = _tensor(q), _tensor(k), _tensor(v), _tensor(o)
     bs = ctypes.byref(blocks.struct) if blocks is not None else None
     nbytes = workspace.numel() if workspace is not None else 0
+    if o_prev is not None:
+        pt = _tensor(o_prev)
+        _check(_lib.bwa_attn_fwd_balanced_carry(ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt),
+                                                ctypes.byref(mk.struct), bs, float(scale), int(mode), _ptr(m),
+                                                _ptr(gate), ctypes.byref(pt), _ptr(lse_prev), int(n_cus),
+                                                _ptr(workspace), nbytes, ctypes.byref(ot), _ptr(lse),
+                                                _stream(q.device)), "bwa_attn_fwd_balanced_carry")
+        return o, lse
     _check(_lib.bwa_attn_fwd_balanced(ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt),
                                       ctypes.byref(mk.struct), bs, float(scale), int(mode), _ptr(m), _ptr(gate),
                                       int(n_cus), _ptr(workspace), nbytes, ctypes.byref(ot),

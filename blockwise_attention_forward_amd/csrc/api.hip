@@ -413,6 +413,20 @@ int32_t bwa_attn_fwd_balanced(const bwa_tensor* q, const bwa_tensor* k, const bw
     return attn_fwd_impl(q, k, v, mask, blocks, scale, mode, m, gate, nullptr, nullptr, o, lse, stream, &bal);
 }
 
+int32_t bwa_attn_fwd_balanced_carry(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
+                                    const bwa_mask* mask, const bwa_blocks* blocks, float scale, int32_t mode,
+                                    const float* m, const uint8_t* gate, const bwa_tensor* o_prev,
+                                    const float* lse_prev, int32_t n_cus, void* workspace, int64_t workspace_bytes,
+                                    bwa_tensor* o, float* lse, void* stream) {
+    if (!o_prev) return fail(BWA_ERR_NULL_ARG, "o_prev is NULL");
+    Balance bal;
+    int32_t st;
+    if ((st = resolve_cus(n_cus, &bal.n_cus))) return st;
+    bal.ws = workspace;
+    bal.ws_bytes = workspace_bytes;
+    return attn_fwd_impl(q, k, v, mask, blocks, scale, mode, m, gate, o_prev, lse_prev, o, lse, stream, &bal);
+}
+
 int32_t bwa_lse_merge(int32_t n_parts, const bwa_tensor* o_parts, const float* const* lse_parts,
                       bwa_tensor* o_out, float* lse_out, void* stream) {
     if (n_parts < 1 || n_parts > bwa::kMaxParts)

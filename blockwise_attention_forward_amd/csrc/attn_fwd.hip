@@ -1065,23 +1065,33 @@ __global__ __launch_bounds__(NW * 64) void merge_pieces_kernel(const AttnLaunch 
     if (row >= p.Lq) return;
     const float* lse_k = p.split_lse + k * s * C::BQ + rib;
     const float* o_k = p.split_o + (k * s * C::BQ + rib) * D + part * (D / TPR);
+    // A carried partial of other key chunks (lse_prev != nullptr) is part s.
+    // o may be o_prev itself: each thread reads its part of the row before it
+    // writes it, and the two threads of a row are adjacent lanes of one wave.
+    const i64 li = (b * p.H + h) * p.Lq + row;
+    const int n_parts = p.lse_prev ? s + 1 : s;
+    auto part_lse = [&](int c) { return c < s ? lse_k[c * C::BQ] : p.lse_prev[li]; };
+    auto part_o = [&](int c) {
+        return c < s ? (const f32x4*)(o_k + (i64)c * C::BQ * D)
+                     : (const f32x4*)(p.o_prev + b * p.op_sB + row * p.op_sL + h * p.op_sH + part * (D / TPR));
+    };
     float mx = kNegInf;
-    for (int c = 0; c < s; ++c) mx = fmaxf(mx, lse_k[c * C::BQ]);
+    for (int c = 0; c < n_parts; ++c) mx = fmaxf(mx, part_lse(c));
     f32x4 acc[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float lse = kNegInf;
     if (mx != kNegInf) {
         float tot = 0.0f;
-        for (int c = 0; c < s; ++c) {
-            const float lc = lse_k[c * C::BQ];
+        for (int c = 0; c < n_parts; ++c) {
+            const float lc = part_lse(c);
             if (lc != kNegInf) tot += expf(lc - mx);
         }
-        for (int c = 0; c < s; ++c) {
-            const float lc = lse_k[c * C::BQ];
-            if (lc == kNegInf) continue;  // an empty piece's O rows are not read
+        for (int c = 0; c < n_parts; ++c) {
+            const float lc = part_lse(c);
+            if (lc == kNegInf) continue;  // an empty part's O rows are not read
             const float w = expf(lc - mx) / tot;
-            const f32x4* oc = (const f32x4*)(o_k + (i64)c * C::BQ * D);
+            const f32x4* oc = part_o(c);
 #pragma unroll
             for (int i = 0; i < NV; ++i) acc[i] += w * oc[i];
         }
@@ -1097,7 +1107,7 @@ __global__ __launch_bounds__(NW * 64) void merge_pieces_kernel(const AttnLaunch 
             *(uint2*)((__bf16*)p.o + off + 4 * i) = v;
         }
     }
-    if (part == 0) p.lse[(b * p.H + h) * p.Lq + row] = lse;
+    if (part == 0) p.lse[li] = lse;
 }
 
 // ---------------------------------------------------------------------------

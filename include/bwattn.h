@@ -320,6 +320,19 @@ int32_t bwa_attn_fwd_balanced(const bwa_tensor* q, const bwa_tensor* k, const bw
                               bwa_tensor* o, float* lse, void* stream);
 
 /*
+ * bwa_attn_fwd_balanced with a carried partial, merged as in
+ * bwa_attn_fwd_carry [FIXEDM Notes]: whole blocks merge it in their epilogue,
+ * cut blocks as one more part of the piece merge.  Arguments, aliasing rules
+ * and errors as for bwa_attn_fwd_carry and bwa_attn_fwd_balanced.
+ */
+int32_t bwa_attn_fwd_balanced_carry(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
+                                    const bwa_mask* mask, const bwa_blocks* blocks, float scale,
+                                    int32_t mode, const float* m, const uint8_t* gate,
+                                    const bwa_tensor* o_prev, const float* lse_prev,
+                                    int32_t n_cus, void* workspace, int64_t workspace_bytes,
+                                    bwa_tensor* o, float* lse, void* stream);
+
+/*
  * Plan of bwa_attn_fwd_balanced for q of dtype/B/H/Lq/D, keys of length Lk
  * and n_cus (<= 0: the current device's compute-unit count, which this call
  * then queries).  Host outputs: *bytes, the workspace size (required);

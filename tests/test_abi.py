@@ -296,3 +296,9 @@ def test_balanced_needs_bf16_inputs():
     f32 = dict(dtype=0)
     assert _bal(_t(**f32), _t(**f32), _t(**f32), _t(**f32), bw._Blocks(128, 64, 256, 256, 1, 2, 8, 0x1000,
                 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)) == 6
+
+
+def test_balanced_carry_needs_o_prev():
+    assert L.bwa_attn_fwd_balanced_carry(ctypes.byref(_t()), ctypes.byref(_t()), ctypes.byref(_t()),
+                                         ctypes.byref(_mask()), None, 0.1, 0, None, None, None, 0x30000, 4,
+                                         0x100000, 1 << 30, ctypes.byref(_t()), 0x20000, None) == 1

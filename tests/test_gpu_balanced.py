@@ -237,3 +237,43 @@ def test_balanced_workspace_reuse_and_sizes():
     with pytest.raises(bw.BwaError) as e:
         bw.bwa_attn_fwd_balanced(q, k, v, mask, blocks=blocks, scale=scale, n_cus=n_cus, workspace=ws[:need - 1])
     assert e.value.status == 7
+
+
+@pytest.mark.parametrize("mode", ["online", "fixed", "gated"])
+def test_balanced_carry_two_chunks(mode):
+    # Two key chunks of one causal sequence; hop 1 through the balanced launch
+    # merges the fp32 partial of hop 0 (whole blocks in their epilogue, cut
+    # blocks in the piece merge).
+    B, H, Lq, L0, L1, D = 2, 3, 1100, 400, 1100, 128
+    scale = 1 / math.sqrt(D)
+    q = _rand((B, Lq, H, D), 800)
+    k = _rand((B, L0 + L1, H, D), 801)
+    v = _rand((B, L0 + L1, H, D), 802)
+    k[1, 5, 2] *= 30  # head 2 of batch 1 fails the gate
+    ks, vs = [k[:, :L0], k[:, L0:]], [v[:, :L0], v[:, L0:]]
+    masks = [{"causal": True, "kv_offset": 0, "q_valid": 1050}, {"causal": True, "kv_offset": L0, "q_valid": 1050}]
+    kmax, mmax, m, gate = bw.bwa_fixed_m_bound(q, ks, scale, 106.5, q_valid=1050)
+    args = {"online": dict(mode=bw.BWA_MODE_ONLINE),
+            "fixed": dict(mode=bw.BWA_MODE_FIXED_M, m=m),
+            "gated": dict(mode=bw.BWA_MODE_GATED, m=m, gate=gate)}[mode]
+    o_ref, l_ref = oracle_attention(q, k, v, {"causal": True, "q_valid": 1050}, scale)
+    heads = [0, 1, 2] if mode != "fixed" else [0, 1]  # fixed-m is exact only for heads that pass the gate
+    o0, l0 = bw.bwa_attn_fwd(q, ks[0], vs[0], masks[0], scale=scale, out_dtype=torch.float32, **args)
+    blocks = _blocks(masks[1], B, Lq, L1, D)
+    n_cus = 24  # 30 blocks in XCD shares of 4 or 3 on 3 units each: 6 cut in 2, the rest whole
+    nbytes, cut, pieces = _plan(B, H, Lq, L1, D, n_cus)
+    assert (cut, pieces) == (6, 2)
+    ob, lb = bw.bwa_attn_fwd_balanced(q, ks[1], vs[1], masks[1], blocks=blocks, scale=scale, n_cus=n_cus,
+                                      o_prev=o0, lse_prev=l0, out_dtype=torch.float32, **args)
+    assert_close(ob[:, :, heads], lb[:, heads], o_ref[:, :, heads], l_ref[:, heads], torch.bfloat16,
+                 f"balanced carry {mode}")
+    op, lp = bw.bwa_attn_fwd_carry(q, ks[1], vs[1], o0, l0, masks[1], blocks=blocks, scale=scale,
+                                   out_dtype=torch.float32, **args)
+    tail, n_cut = _tail_rows(B, H, Lq, D, n_cus, pieces)
+    assert n_cut == cut
+    _check_vs_plain(ob, lb, op, lp, tail, f"balanced carry vs plain carry {mode}")
+    # in place: the carried partial is overwritten by the merged result
+    oi, li = o0.clone(), l0.clone()
+    bw.bwa_attn_fwd_balanced(q, ks[1], vs[1], masks[1], blocks=blocks, scale=scale, n_cus=n_cus,
+                             o_prev=oi, lse_prev=li, o=oi, lse=li, **args)
+    assert torch.equal(oi, ob) and torch.equal(li, lb)

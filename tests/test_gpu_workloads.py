@@ -277,7 +277,7 @@ def test_varlen_balanced():
     assert_close(*gpu_rows(o, l, rows), o_ref, l_ref, BF16, "varlen balanced")
 
 
-def _hops_carry(d, mode, m=None, gate=None):
+def _hops_carry(d, mode, m=None, gate=None, balanced=False):
     """The hops chained by the carried partial: hop 0 writes fp32, the last hop the bf16 result."""
     q = d["q"]
     B, Lq, H, D = q.shape
@@ -289,7 +289,10 @@ def _hops_carry(d, mode, m=None, gate=None):
         blocks = bw.bwa_block_mask_build(mask, B, Lq, k.shape[1], bq, 128)
         kw = dict(mask=mask, blocks=blocks, scale=d["scale"], mode=mode, m=m, gate=gate,
                   out_dtype=BF16 if t == n - 1 else torch.float32)
-        if t == 0:
+        if balanced:
+            carry = {} if t == 0 else dict(o_prev=o, lse_prev=lse)
+            o, lse = bw.bwa_attn_fwd_balanced(q, k, v, **kw, **carry)
+        elif t == 0:
             o, lse = bw.bwa_attn_fwd(q, k, v, **kw)
         else:
             o, lse = bw.bwa_attn_fwd_carry(q, k, v, o, lse, **kw)
@@ -309,6 +312,24 @@ def test_dit_hops_chained_by_carry(dit):
     o_m, l_m = _hops(dit, bw.BWA_MODE_GATED, m=m, gate=gate)
     assert (l - l_m).abs().max().item() <= 1e-5
     assert (o.float() - o_m.float()).abs().max().item() <= 2 ** -7
+
+
+def test_dit_balanced_hops_chained_by_carry(dit):
+    # the bench's carried-hops step with its launch (balanced)
+    q = dit["q"]
+    Lq = q.shape[1]
+    kmax, mmax, m, gate = bw.bwa_fixed_m_bound(q, dit["k_chunks"], dit["scale"], 106.5)
+    o, l = _hops_carry(dit, bw.BWA_MODE_GATED, m=m, gate=gate, balanced=True)
+    assert o.dtype == BF16
+    B, _, H, D = q.shape
+    cut = _cut_blocks(B, H, Lq, dit["k_chunks"][0].shape[1], D)
+    must = [0, Lq - 1] + sorted({r0 for _, _, r0, _ in cut})[:24]
+    rows = synth.sample_rows(Lq, 512, seed=30, must=must)
+    o_ref, l_ref = _dit_oracle(dit, rows)
+    assert_close(*gpu_rows(o, l, rows), o_ref, l_ref, BF16, "dit balanced carried hops")
+    o_p, l_p = _hops_carry(dit, bw.BWA_MODE_GATED, m=m, gate=gate)
+    assert (l - l_p).abs().max().item() <= 1e-5
+    assert (o.float() - o_p.float()).abs().max().item() <= 2 ** -7
 
 
 def test_dit_all_heads_eligible():

@@ -20,7 +20,9 @@ Sources (web pages; cited by title and section):
 * maxdiffusion pull request 404 (ulysses_ring review): padding sits at the end
   of the global sequence; masks come from global positions.
 * "Add more optimal dk order optional arg" (flash-attention pull request
-  2512): "Sliding window perf issue" -- tiles are partial, full or skipped.
+  2512): "Sliding window perf issue" -- tiles are partial, full or skipped;
+  description -- the backward pass per key column and the order in which
+  the key columns add into dQ.
 
 Every function computes the plain definition; none simulates a GPU order of
 operations.  Readings of points the pages leave open are listed in the
@@ -38,6 +40,10 @@ from .attention import (  # noqa: F401
     softmax_probs,
     lse_merge,
     fixed_m_bound,
+)
+from .backward import (  # noqa: F401
+    attention_backward,
+    attention_backward_heads,
 )
 from .blocks import (  # noqa: F401
     FULL,

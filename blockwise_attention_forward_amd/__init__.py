@@ -21,12 +21,14 @@ __all__ = [
     "lib_path", "bwa_version", "bwa_status_string", "bwa_last_error", "bwa_attn_tile",
     "bwa_block_mask_size", "bwa_block_mask_build", "bwa_fixed_m_bound", "bwa_attn_fwd",
     "bwa_attn_fwd_carry", "bwa_attn_fwd_balanced", "bwa_attn_fwd_balanced_workspace", "bwa_lse_merge",
-    "bwa_attn_fwd_balanced_carry",
+    "bwa_attn_fwd_balanced_carry", "BWA_ORDER_ASC", "BWA_ORDER_DESC", "BWA_ORDER_OUTSIDE_IN",
+    "BWA_ORDER_CUSTOM", "bwa_attn_bwd", "bwa_attn_bwd_workspace",
 ]
 
 BWA_F32, BWA_BF16 = 0, 1
 BWA_MODE_ONLINE, BWA_MODE_FIXED_M, BWA_MODE_GATED = 0, 1, 2
 BWA_TILE_SKIP, BWA_TILE_FULL, BWA_TILE_PARTIAL = 0, 1, 2
+BWA_ORDER_ASC, BWA_ORDER_DESC, BWA_ORDER_OUTSIDE_IN, BWA_ORDER_CUSTOM = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libbwattn.so")
@@ -83,6 +85,8 @@ def _load():
         "bwa_attn_fwd_balanced_carry": (I32, [TP, TP, TP, MP, BP, F32, I32, P, P, TP, P, I32, P, I64, TP, P, P]),
         "bwa_attn_fwd_balanced_workspace": (I32, [I32, I64, I64, I64, I64, I64, I32, I64P, I64P, I32P]),
         "bwa_lse_merge": (I32, [I32, TP, ctypes.POINTER(ctypes.c_void_p), TP, P, P]),
+        "bwa_attn_bwd": (I32, [TP, TP, TP, TP, P, TP, MP, F32, I32, P, P, I64, TP, TP, TP, P]),
+        "bwa_attn_bwd_workspace": (I32, [MP, I64, I64, I64, I64, I64P, I64P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -356,3 +360,41 @@ def bwa_lse_merge(o_parts, lse_parts, o_out=None, lse_out=None, out_dtype=torch.
     _check(_lib.bwa_lse_merge(n, parts, lps, ctypes.byref(ot), _ptr(lse_out), _stream(dev)),
            "bwa_lse_merge")
     return o_out, lse_out
+
+
+def bwa_attn_bwd_workspace(mask, B, H, Lq, Lk, device="cuda", tiles=False):
+    """Workspace bytes of bwa_attn_bwd; with tiles=True, (bytes, 64-key tiles)."""
+    mk = Mask.of(mask, device)
+    n, t = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.bwa_attn_bwd_workspace(ctypes.byref(mk.struct), int(B), int(H), int(Lq), int(Lk), ctypes.byref(n),
+                                       ctypes.byref(t)), "bwa_attn_bwd_workspace")
+    return (n.value, t.value) if tiles else n.value
+
+
+def bwa_attn_bwd(q, k, v, o, lse, dout, mask=None, scale=None, order=BWA_ORDER_ASC, kv_order=None,
+                 workspace=None, dq=None, dk=None, dv=None, grad_dtype=torch.float32):
+    """Backward pass of bwa_attn_fwd (bf16 q/k/v/dout; o and lse from the
+    forward).  kv_order: a device int32 permutation of the 64-key tiles for
+    BWA_ORDER_CUSTOM.  workspace: a uint8 device tensor of at least
+    bwa_attn_bwd_workspace bytes (allocated here if None).  Returns
+    (dq, dk, dv)."""
+    B, Lq, H, D = q.shape
+    Lk = k.shape[1]
+    if scale is None:
+        scale = D ** -0.5
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
+    if dv is None:
+        dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
+    mk = Mask.of(mask, q.device)
+    if workspace is None:
+        n = bwa_attn_bwd_workspace(mk, B, H, Lq, Lk, q.device)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    ts = [_tensor(t) for t in (q, k, v, o, dout, dq, dk, dv)]
+    _check(_lib.bwa_attn_bwd(ctypes.byref(ts[0]), ctypes.byref(ts[1]), ctypes.byref(ts[2]), ctypes.byref(ts[3]),
+                             _ptr(lse), ctypes.byref(ts[4]), ctypes.byref(mk.struct), float(scale), int(order),
+                             _ptr(kv_order), _ptr(workspace), workspace.numel(), ctypes.byref(ts[5]),
+                             ctypes.byref(ts[6]), ctypes.byref(ts[7]), _stream(q.device)), "bwa_attn_bwd")
+    return dq, dk, dv

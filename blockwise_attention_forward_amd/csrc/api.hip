@@ -427,6 +427,86 @@ int32_t bwa_attn_fwd_balanced_carry(const bwa_tensor* q, const bwa_tensor* k, co
     return attn_fwd_impl(q, k, v, mask, blocks, scale, mode, m, gate, o_prev, lse_prev, o, lse, stream, &bal);
 }
 
+int32_t bwa_attn_bwd_workspace(const bwa_mask* mask, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t* bytes,
+                               int64_t* n_kv_tiles) {
+    if (!bytes) return fail(BWA_ERR_NULL_ARG, "bytes output is NULL");
+    if (B < 0 || H < 0 || Lq < 0 || Lk < 0) return fail(BWA_ERR_BAD_SHAPE, "negative size");
+    if (Lq > kMaxLen || Lk > kMaxLen) return fail(BWA_ERR_UNSUPPORTED, "length exceeds 2^30");
+    bwa::MaskDev md;
+    int32_t st = resolve_mask(mask, B, Lq, Lk, md);
+    if (st) return st;
+    const i64 lb = md.seg_mode >= 2 ? B : 1;
+    *bytes = bwa::bwd_workspace_bytes(B, H, Lq, Lk, lb);
+    if (n_kv_tiles) *n_kv_tiles = (Lk + 63) / 64;
+    return ok();
+}
+
+int32_t bwa_attn_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v, const bwa_tensor* o,
+                     const float* lse, const bwa_tensor* dout, const bwa_mask* mask, float scale, int32_t order,
+                     const int32_t* kv_order, void* workspace, int64_t workspace_bytes, bwa_tensor* dq,
+                     bwa_tensor* dk, bwa_tensor* dv, void* stream) {
+    int32_t st;
+    if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
+        (st = check_tensor(o, "o")) || (st = check_tensor(dout, "dout")) || (st = check_tensor(dq, "dq")) ||
+        (st = check_tensor(dk, "dk")) || (st = check_tensor(dv, "dv")))
+        return st;
+    if (q->dtype != BWA_BF16) return fail(BWA_ERR_UNSUPPORTED, "the backward pass computes bf16 inputs only");
+    if (k->dtype != q->dtype || v->dtype != q->dtype) return fail(BWA_ERR_BAD_DTYPE, "q, k and v must share a dtype");
+    if (dout->dtype != BWA_BF16) return fail(BWA_ERR_BAD_DTYPE, "dout must be bf16");
+    if (dk->dtype != dq->dtype || dv->dtype != dq->dtype)
+        return fail(BWA_ERR_BAD_DTYPE, "dq, dk and dv must share a dtype");
+    if (k->B != q->B || v->B != q->B || k->D != q->D || v->D != q->D || v->H != k->H || k->L != v->L)
+        return fail(BWA_ERR_BAD_SHAPE, "q, k, v disagree on B or D, or k and v on H or L");
+    if (q->H > 0 && (k->H <= 0 || q->H % k->H))
+        return fail(BWA_ERR_BAD_SHAPE, "%lld key/value heads do not divide %lld query heads", (long long)k->H,
+                    (long long)q->H);
+    auto same = [](const bwa_tensor* a, const bwa_tensor* b) {
+        return a->B == b->B && a->L == b->L && a->H == b->H && a->D == b->D;
+    };
+    if (!same(o, q) || !same(dout, q) || !same(dq, q)) return fail(BWA_ERR_BAD_SHAPE, "o, dout and dq must have q's shape");
+    if (!same(dk, k) || !same(dv, k)) return fail(BWA_ERR_BAD_SHAPE, "dk and dv must have k's shape");
+    if (order < BWA_ORDER_ASC || order > BWA_ORDER_CUSTOM) return fail(BWA_ERR_BAD_SHAPE, "unknown order %d", order);
+    const i64 B = q->B, H = q->H, Lq = q->L, Lk = k->L;
+    bwa::BwdLaunch a;
+    memset(&a, 0, sizeof(a));
+    if ((st = resolve_mask(mask, B, Lq, Lk, a.mask))) return st;
+    if (B * H * Lq > 0 && !lse) return fail(BWA_ERR_NULL_ARG, "lse is NULL");
+    if (order == BWA_ORDER_CUSTOM && Lk > 0 && !kv_order)
+        return fail(BWA_ERR_NULL_ARG, "BWA_ORDER_CUSTOM needs kv_order");
+    // One 256-work-item workgroup per (b, h, 128 rows) and per (b, h_kv, 128 keys); the delta pass
+    // runs D/8 work-items per row: each launch holds under 2^32 work-items.
+    if (B * H * ((Lq + 127) / 128) >= ((i64)1 << 23) || B * k->H * ((Lk + 127) / 128) >= ((i64)1 << 23) ||
+        B * H * Lq * (q->D / 8) >= ((i64)1 << 32) - 256)
+        return fail(BWA_ERR_UNSUPPORTED, "grid too large");
+    a.list_batch = a.mask.seg_mode >= 2 ? B : 1;
+    const i64 need = bwa::bwd_workspace_bytes(B, H, Lq, Lk, a.list_batch);
+    if (!workspace) return fail(BWA_ERR_NULL_ARG, "workspace is NULL");
+    if ((uintptr_t)workspace % 256) return fail(BWA_ERR_BAD_STRIDE, "workspace not 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(BWA_ERR_CAPACITY, "workspace of %lld bytes; %lld needed", (long long)workspace_bytes,
+                    (long long)need);
+    a.q = q->ptr; a.k = k->ptr; a.v = v->ptr; a.o = o->ptr; a.dout = dout->ptr;
+    a.q_sB = q->sB; a.q_sL = q->sL; a.q_sH = q->sH;
+    a.k_sB = k->sB; a.k_sL = k->sL; a.k_sH = k->sH;
+    a.v_sB = v->sB; a.v_sL = v->sL; a.v_sH = v->sH;
+    a.o_sB = o->sB; a.o_sL = o->sL; a.o_sH = o->sH;
+    a.do_sB = dout->sB; a.do_sL = dout->sL; a.do_sH = dout->sH;
+    a.lse = lse;
+    a.dq = dq->ptr; a.dq_sB = dq->sB; a.dq_sL = dq->sL; a.dq_sH = dq->sH;
+    a.dk = dk->ptr; a.dk_sB = dk->sB; a.dk_sL = dk->sL; a.dk_sH = dk->sH;
+    a.dv = dv->ptr; a.dv_sB = dv->sB; a.dv_sL = dv->sL; a.dv_sH = dv->sH;
+    a.B = (int)B; a.H = (int)H; a.Hk = (int)k->H; a.D = (int)q->D;
+    a.kv_group = H > 0 ? (int)(H / k->H) : 1;
+    a.Lq = Lq; a.Lk = Lk;
+    a.o_dtype = o->dtype;
+    a.grad_dtype = dq->dtype;
+    a.scale = scale;
+    a.order = order;
+    a.perm = order == BWA_ORDER_CUSTOM ? kv_order : nullptr;
+    bwa::bwd_workspace_layout(a, workspace);
+    return hip_status(bwa::launch_attn_bwd(a, (hipStream_t)stream), "attn_bwd launch");
+}
+
 int32_t bwa_lse_merge(int32_t n_parts, const bwa_tensor* o_parts, const float* const* lse_parts,
                       bwa_tensor* o_out, float* lse_out, void* stream) {
     if (n_parts < 1 || n_parts > bwa::kMaxParts)

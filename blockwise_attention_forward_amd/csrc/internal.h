@@ -178,6 +178,33 @@ struct BoundLaunch {
 };
 hipError_t launch_fixed_m_bound(const BoundLaunch& a, hipStream_t stream);
 
+// Backward pass: inputs, outputs and the planning arrays in the caller's
+// workspace (per-row delta and key intervals, per 64-row query tile
+// summaries, per 128-key block query-tile ranges).
+struct BwdLaunch {
+    const void* q; const void* k; const void* v; const void* o; const void* dout;
+    i64 q_sB, q_sL, q_sH, k_sB, k_sL, k_sH, v_sB, v_sL, v_sH, o_sB, o_sL, o_sH, do_sB, do_sL, do_sH;
+    const float* lse;
+    void* dq; i64 dq_sB, dq_sL, dq_sH;
+    void* dk; i64 dk_sB, dk_sL, dk_sH;
+    void* dv; i64 dv_sB, dv_sL, dv_sH;
+    int B, H, Hk, D, kv_group;
+    i64 Lq, Lk;
+    int o_dtype, grad_dtype;
+    float scale;
+    int order;          // BWA_ORDER_*
+    const int* perm;    // BWA_ORDER_CUSTOM: device [nkt]
+    float* delta;       // [B][H][Lq]
+    int* row_lo; int* row_hi;  // [list_batch][Lq]
+    int4* qsum;         // [list_batch][nqt]: envelope lo, hi; common part lo, hi
+    int* kfirst; int* klast;   // [list_batch][nkb]: query tiles meeting the key block
+    i64 list_batch, nqt, nkb, nkt;
+    MaskDev mask;
+};
+hipError_t launch_attn_bwd(const BwdLaunch& a, hipStream_t stream);
+i64 bwd_workspace_bytes(i64 B, i64 H, i64 Lq, i64 Lk, i64 list_batch);
+void bwd_workspace_layout(BwdLaunch& a, void* ws);
+
 constexpr int kMaxParts = 16;
 struct MergeLaunch {
     const float* o[kMaxParts];

@@ -4,7 +4,8 @@
  * The library computes blockwise scaled-dot-product attention forward with
  * online softmax or with a fixed per-query bound in place of the running max,
  * the log-sum-exp merge of key-chunk partials, the fixed-m bound and gate,
- * and the tile run lists that let the attention kernel skip whole tiles.
+ * the tile run lists that let the attention kernel skip whole tiles, and the
+ * deterministic backward pass of the same attention.
  *
  * Pages the operations follow (cited by title and section):
  *  [FIXEDM]  "Fixed-m softmax for 2D-ring x Ulysses attention (WAN 2.2)"
@@ -12,7 +13,8 @@
  *  [SPLASH]  "Let splash attention exceed 524,288 tokens when packing is off"
  *            (maxtext pull request 4929): description, Effect, review.
  *  [DKORDER] "Add more optimal dk order optional arg" (flash-attention pull
- *            request 2512): "Sliding window perf issue", "A simplish fix".
+ *            request 2512): description (the backward pass and the order of
+ *            the key columns), "Sliding window perf issue", "A simplish fix".
  *  [H3]      sglang pull request 47566 (H3 packed sequence): Motivation,
  *            Modifications.
  *  [ULYRING] maxdiffusion pull request 404 (ulysses_ring review): padding
@@ -45,7 +47,7 @@
 extern "C" {
 #endif
 
-#define BWATTN_VERSION 2
+#define BWATTN_VERSION 3
 
 /* Status codes. */
 enum {
@@ -72,6 +74,14 @@ enum {
 
 /* Tile kinds in run lists [DKORDER "Sliding window perf issue"]. */
 enum { BWA_TILE_SKIP = 0, BWA_TILE_FULL = 1, BWA_TILE_PARTIAL = 2 };
+
+/* Orders in which a query block's key tiles add into dQ [DKORDER description]. */
+enum {
+    BWA_ORDER_ASC = 0,         /* ascending key tiles */
+    BWA_ORDER_DESC = 1,        /* descending */
+    BWA_ORDER_OUTSIDE_IN = 2,  /* tiles 0, n-1, 1, n-2, ... of all n key tiles */
+    BWA_ORDER_CUSTOM = 3       /* the caller's permutation of the n key tiles */
+};
 
 /* A dense [B, L, H, D] tensor; d-stride is 1; strides in elements. */
 typedef struct bwa_tensor {
@@ -347,6 +357,59 @@ int32_t bwa_attn_fwd_balanced_carry(const bwa_tensor* q, const bwa_tensor* k, co
  */
 int32_t bwa_attn_fwd_balanced_workspace(int32_t dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
                                         int32_t n_cus, int64_t* bytes, int64_t* cut_blocks, int32_t* pieces);
+
+/*
+ * Backward pass of bwa_attn_fwd [DKORDER description: a program per key
+ * column computes that column's dK and dV, and each query block's dQ
+ * collects one contribution per key column in an order the caller chooses;
+ * a fixed order makes dQ repeat bit for bit].  For the loss
+ * sum_i dout_i . O_i, with P = exp(scale * Q K^T - LSE) over the visible
+ * pairs (0 elsewhere):
+ *   dV = P^T dout,  dS = P o (dout V^T - delta),  delta_i = dout_i . O_i,
+ *   dQ = scale * dS K,  dK = scale * dS^T Q,
+ * and with grouped-query heads a key/value head's dK and dV sum over the
+ * query heads that read it.
+ *   - q, k, v: BWA_BF16, shapes and mask as for bwa_attn_fwd (D 64 or 128).
+ *     o: the forward output (fp32 or bf16, q's shape); lse: the forward's
+ *     device fp32 [B][H][Lq]; dout: the upstream gradient, BWA_BF16, q's
+ *     shape.  dq (q's shape), dk and dv (k's shape): outputs, all fp32 or all
+ *     bf16; every element is written (keys no row sees and rows that see
+ *     nothing get 0).
+ *   - order: BWA_ORDER_*.  A query block adds the contributions of its key
+ *     tiles (64 keys each; n = ceil(Lk / 64) of them) into dQ in the order
+ *     of the tiles' positions in the permutation: ascending, descending,
+ *     outside-in, or kv_order (device int32 [n], required only for
+ *     BWA_ORDER_CUSTOM; it must be a permutation of 0..n-1: entries out of
+ *     range are ignored, a repeated entry is added twice).  dK and dV always
+ *     add query tiles in ascending order.  The order changes only dQ's
+ *     rounding; every order is deterministic.
+ *   - workspace: device memory of at least bwa_attn_bwd_workspace bytes for
+ *     the same B, H, Lq, Lk and mask, 256-byte aligned, owned by the caller;
+ *     calls that share it must be ordered (same stream).
+ * No workgroup waits for another and nothing is accumulated with atomics:
+ * the key-column kernel writes dK and dV, a query-block kernel recomputes
+ * the probabilities and writes dQ.  P and dS are rounded to bf16 as
+ * matrix-core operands; accumulation is fp32.
+ * Errors as for bwa_attn_fwd, plus BWA_ERR_UNSUPPORTED (q not bf16),
+ * BWA_ERR_BAD_DTYPE (dout not bf16, o or the gradients not fp32/bf16, or
+ * the gradients of mixed dtypes), BWA_ERR_BAD_SHAPE (an unknown order),
+ * BWA_ERR_NULL_ARG (workspace, lse or kv_order missing), BWA_ERR_BAD_STRIDE
+ * (workspace alignment), BWA_ERR_CAPACITY (workspace too small).
+ */
+int32_t bwa_attn_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v, const bwa_tensor* o,
+                     const float* lse, const bwa_tensor* dout, const bwa_mask* mask, float scale,
+                     int32_t order, const int32_t* kv_order, void* workspace, int64_t workspace_bytes,
+                     bwa_tensor* dq, bwa_tensor* dk, bwa_tensor* dv, void* stream);
+
+/*
+ * Workspace of bwa_attn_bwd for B, H query heads, Lq, Lk and mask (host
+ * only, no launch).  *bytes = pad(B*H*Lq*4) + 2 pad(c*Lq*4)
+ * + pad(c*ceil(Lq/64)*16) + 2 pad(c*ceil(Lk/128)*4), pad = round up to 256,
+ * c = B with per-token segment ids, else 1.  *n_kv_tiles (optional) = the
+ * number of 64-key tiles, the length of a BWA_ORDER_CUSTOM permutation.
+ */
+int32_t bwa_attn_bwd_workspace(const bwa_mask* mask, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                               int64_t* bytes, int64_t* n_kv_tiles);
 
 /*
  * Log-sum-exp merge of attention partials over disjoint key chunks

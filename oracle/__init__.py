@@ -44,6 +44,8 @@ from .attention import (  # noqa: F401
 from .backward import (  # noqa: F401
     attention_backward,
     attention_backward_heads,
+    attention_backward_rows,
+    attention_backward_keys,
 )
 from .blocks import (  # noqa: F401
     FULL,

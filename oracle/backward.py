@@ -33,7 +33,7 @@ gradients are the sums over the query heads that read it.
 
 import numpy as np
 
-from .attention import softmax_probs, kv_head
+from .attention import softmax_probs, kv_head, visibility, attention_rows
 
 
 def _as64(x):
@@ -78,3 +78,47 @@ def attention_backward_heads(q, k, v, do, mask, scale):
         dk[:, hk] += b
         dv[:, hk] += c
     return dq, dk, dv
+
+
+def attention_backward_rows(q, k, v, do, mask, scale, rows):
+    """``dQ[rows]`` of ``attention_backward`` for the selected query rows only.
+
+    Each row's gradient needs only its own probabilities: the same formulas
+    restricted to the rows.
+    """
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    rows = np.asarray(rows, dtype=np.int64)
+    p = softmax_probs(q, k, mask, scale, rows=rows)
+    o = p @ v
+    dp = do[rows] @ v.T
+    delta = (do[rows] * o).sum(axis=1)
+    ds = p * (dp - delta[:, None])
+    return scale * (ds @ k)
+
+
+def attention_backward_keys(q, k, v, do, mask, scale, keys, chunk=256):
+    """``(dK[keys], dV[keys])`` of ``attention_backward`` for selected keys.
+
+    A key's gradients sum over every row that sees it, and each of those
+    rows' probabilities needs the row's full log-sum-exp and output: these
+    come from ``attention_rows`` over all rows (``chunk`` rows at a time),
+    then the formulas run on the selected key columns only.
+    """
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    keys = np.asarray(keys, dtype=np.int64)
+    Lq, Lk = q.shape[0], k.shape[0]
+    dk = np.zeros((keys.size, k.shape[1]))
+    dv = np.zeros((keys.size, v.shape[1]))
+    for r0 in range(0, Lq, chunk):
+        rows = np.arange(r0, min(Lq, r0 + chunk))
+        o, lse = attention_rows(q, k, v, mask, scale, rows)
+        vis = visibility(rows, Lk, mask, Lq)[:, keys]
+        s = scale * (q[rows] @ k[keys].T)
+        lse_safe = np.where(np.isfinite(lse), lse, 0.0)
+        p = np.where(vis, np.exp(np.where(vis, s, 0.0) - lse_safe[:, None]), 0.0)
+        dp = do[rows] @ v[keys].T
+        delta = (do[rows] * o).sum(axis=1)
+        ds = p * (dp - delta[:, None])
+        dk += scale * (ds.T @ q[rows])
+        dv += p.T @ do[rows]
+    return dk, dv

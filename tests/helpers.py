@@ -87,3 +87,71 @@ def assert_close(o_gpu, lse_gpu, o_ref, lse_ref, in_dtype, what=""):
         assert np.all(err_l <= bound), (f"{what}: LSE err {err_l[worst]:.3e} > {bound[worst]:.3e} "
                                         f"at |lse| = {abs(lse_ref[live][worst]):.3g}")
     return mx, mean
+
+
+# ---------------------------------------------------------------- backward
+# Gradient tolerance, derived from the arithmetic (the pages fix none).  The
+# kernels round P and dS to bf16 (unit roundoff u = 2^-8) as matrix-core
+# operands and accumulate in fp32; delta = dO . O is computed from the
+# forward output, which in bf16 carries a relative error u per element.  So
+# each gradient element is within u * A of the exact value, where A sums the
+# magnitudes of the element's terms:
+#   dV[j,d]: A = sum_i P_ij |dO_id|
+#   dK[j,d]: A = scale * sum_i (|dS_ij| + P_ij e_i) |q_id|
+#   dQ[i,d]: A = scale * sum_j (|dS_ij| + P_ij e_i) |k_jd|
+# with e_i = sum_d |dO_id O_id| (the delta error bound over u).  fp32 score,
+# exponential and accumulation errors are orders below u; the bound used is
+# 2u * A + 1e-6 (a factor 2 of margin), plus u |ref| when the gradient is
+# stored in bf16.  Elements whose terms are all zero (keys no row sees, rows
+# that see nothing) must be exactly zero.
+BWD_U = 2.0 ** -8
+
+
+def bwd_terms(q, k, v, do, mask, scale, rows, keys, Lq, o_rows=None, lse_rows=None):
+    """P, dS and e on rows x keys of one (batch, head), from the oracle's
+    visibility and forward (O and LSE of the rows, computed here unless
+    given).  q, do: [Lq, D]; k, v: [Lk, D] (fp64)."""
+    if o_rows is None:
+        o_rows, lse_rows = oracle.attention_rows(q, k, v, mask, scale, rows)
+    vis = oracle.visibility(rows, k.shape[0], mask, Lq)[:, keys]
+    s = scale * (q[rows] @ k[keys].T)
+    lse = np.where(np.isfinite(lse_rows), lse_rows, 0.0)
+    p = np.where(vis, np.exp(np.where(vis, s, 0.0) - lse[:, None]), 0.0)
+    dp = do[rows] @ v[keys].T
+    delta = (do[rows] * o_rows).sum(axis=1)
+    ds = p * (dp - delta[:, None])
+    e = np.abs(do[rows] * o_rows).sum(axis=1)
+    return p, ds, e
+
+
+def bwd_bounds(q, k, v, do, mask, scale, rows, keys, chunk=512):
+    """Error scales A (see above) for dQ[rows] ([R, D]) and dK, dV[keys]
+    ([K, D]) of one (batch, head); dK/dV sum over every row in chunks."""
+    Lq = q.shape[0]
+    rows = np.asarray(rows)
+    keys = np.asarray(keys)
+    allk = np.arange(k.shape[0])
+    p, ds, e = bwd_terms(q, k, v, do, mask, scale, rows, allk, Lq)
+    a_dq = scale * ((np.abs(ds) + p * e[:, None]) @ np.abs(k))
+    a_dk = np.zeros((keys.size, q.shape[1]))
+    a_dv = np.zeros((keys.size, v.shape[1]))
+    for r0 in range(0, Lq, chunk):
+        rr = np.arange(r0, min(Lq, r0 + chunk))
+        p, ds, e = bwd_terms(q, k, v, do, mask, scale, rr, keys, Lq)
+        a_dk += scale * ((np.abs(ds) + p * e[:, None]).T @ np.abs(q[rr]))
+        a_dv += p.T @ np.abs(do[rr])
+    return a_dq, a_dk, a_dv
+
+
+def assert_grad_close(g, ref, a, bf16_out, what):
+    g = g if isinstance(g, np.ndarray) else np64(g)
+    assert g.shape == ref.shape, (what, g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite gradient"
+    zero = a == 0
+    assert np.all(g[zero] == 0), f"{what}: elements with no visible term must be exactly 0"
+    bound = 2 * BWD_U * a + 1e-6 + (BWD_U * np.abs(ref) if bf16_out else 0.0)
+    err = np.abs(g - ref)
+    worst = np.unravel_index(int(np.argmax(err - bound)), err.shape) if err.size else None
+    assert np.all(err <= bound), (f"{what}: err {err[worst]:.3e} > bound {bound[worst]:.3e} "
+                                  f"(ref {ref[worst]:.3e}, A {a[worst]:.3e}) at {worst}")
+    return float(err.max(initial=0)), float(err.mean()) if err.size else 0.0

@@ -84,7 +84,7 @@ int main(void) {
 
 
 def test_version_and_status_strings():
-    assert bw.bwa_version() == 2
+    assert bw.bwa_version() == 3
     for code in range(9):
         assert bw.bwa_status_string(code) != "unknown status"
     assert bw.bwa_status_string(99) == "unknown status"
@@ -302,3 +302,55 @@ def test_balanced_carry_needs_o_prev():
     assert L.bwa_attn_fwd_balanced_carry(ctypes.byref(_t()), ctypes.byref(_t()), ctypes.byref(_t()),
                                          ctypes.byref(_mask()), None, 0.1, 0, None, None, None, 0x30000, 4,
                                          0x100000, 1 << 30, ctypes.byref(_t()), 0x20000, None) == 1
+
+
+# ---------------------------------------------------------------- backward
+def test_bwd_workspace_size():
+    n, t = ctypes.c_int64(), ctypes.c_int64()
+    f = L.bwa_attn_bwd_workspace
+    pad = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    # delta [B, H, Lq] fp32, row intervals [c, Lq] x 2, query-tile summaries
+    # [c, ceil(Lq/64)] x 16 bytes, key-block ranges [c, ceil(Lk/128)] x 2
+    m = _mask(causal=1, window=512)
+    assert f(ctypes.byref(m), 2, 16, 4096, 8192, ctypes.byref(n), ctypes.byref(t)) == 0
+    assert n.value == pad(2 * 16 * 4096 * 4) + 2 * pad(4096 * 4) + pad(64 * 16) + 2 * pad(64 * 4)
+    assert t.value == 128
+    # per-token segment ids: one copy per batch element
+    m = _mask(segment_ids_q=0x40000)
+    assert f(ctypes.byref(m), 3, 2, 1000, 1000, ctypes.byref(n), None) == 0
+    assert n.value == pad(3 * 2 * 1000 * 4) + 2 * pad(3 * 1000 * 4) + pad(3 * 16 * 16) + 2 * pad(3 * 8 * 4)
+    assert f(ctypes.byref(m), 3, 2, 1000, 1000, None, None) == 1
+    assert f(ctypes.byref(_mask()), -1, 2, 10, 10, ctypes.byref(n), None) == 2
+    assert f(ctypes.byref(_mask(causal=2)), 1, 2, 10, 10, ctypes.byref(n), None) == 5
+
+
+def _bwd(q=None, k=None, v=None, o=None, lse=0x20000, do=None, order=0, perm=None, ws=0x100000,
+         ws_bytes=1 << 30, dq=None, dk=None, dv=None, mask=None):
+    t = lambda x, **kw: x if x is not None else _t(**kw)  # noqa: E731
+    args = [t(q), t(k), t(v), t(o), t(do), t(dq, dtype=0), t(dk, dtype=0), t(dv, dtype=0)]
+    mask = mask or _mask()
+    return L.bwa_attn_bwd(*[ctypes.byref(a) for a in args[:4]], lse, ctypes.byref(args[4]), ctypes.byref(mask),
+                          0.1, order, perm, ws, ws_bytes, *[ctypes.byref(a) for a in args[5:]], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=_t(dtype=0), k=_t(dtype=0), v=_t(dtype=0)), 6),  # fp32 inputs: bf16 only
+    (dict(k=_t(dtype=0)), 4),                    # q, k, v share a dtype
+    (dict(do=_t(dtype=0)), 4),                   # dout must be bf16
+    (dict(dk=_t(dtype=1)), 4),                   # gradients share a dtype
+    (dict(o=_t(L=255)), 2),
+    (dict(dq=_t(dtype=0, H=4)), 2),
+    (dict(dv=_t(dtype=0, L=100)), 2),
+    (dict(k=_t(H=3), v=_t(H=3), dk=_t(dtype=0, H=3), dv=_t(dtype=0, H=3)), 2),
+    (dict(order=4), 2),
+    (dict(order=3), 1),                          # a custom order needs kv_order
+    (dict(lse=None), 1),
+    (dict(ws=None), 1),
+    (dict(ws=0x100010), 3),
+    (dict(ws_bytes=1000), 7),
+    (dict(mask=_mask(causal=2)), 5),
+    (dict(q=_t(D=96), k=_t(D=96), v=_t(D=96)), 6),
+])
+def test_bwd_argument_errors(kw, code):
+    assert _bwd(**kw) == code
+    assert bw.bwa_last_error() != ""

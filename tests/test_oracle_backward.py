@@ -14,7 +14,9 @@ The gradients are checked against facts other than their own formulas:
   rows that see something; keys no row sees and rows that see nothing get
   zero gradient;
 * grouped-query heads: a shared key/value head collects the gradients of its
-  query heads (finite differences on the shared tensor).
+  query heads (finite differences on the shared tensor);
+* the sampled forms (selected query rows, selected keys) equal the full
+  gradients on those rows and keys.
 
 The value width differs from the query/key width in the directional checks,
 so a transposed operand fails.
@@ -158,3 +160,17 @@ def test_grouped_heads_collect_gradients():
         hk = oracle.kv_head(h, H, Hk)
         a, _, _ = oracle.attention_backward(q[:, h], k[:, hk], v[:, hk], do[:, h], mask, scale)
         np.testing.assert_array_equal(dq[:, h], a)
+
+
+@pytest.mark.parametrize("mask", MASKS)
+def test_sampled_rows_and_keys_equal_full(mask):
+    Lq, Lk, D = 31, 29, 5
+    q, k, v, do = _inputs(Lq, Lk, D, D, 19)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, mask, 0.52)
+    rows = np.array([0, 3, 7, 30, 12])
+    keys = np.array([28, 0, 5, 13])
+    np.testing.assert_allclose(oracle.attention_backward_rows(q, k, v, do, mask, 0.52, rows), dq[rows],
+                               rtol=1e-12, atol=1e-13)
+    sk, sv = oracle.attention_backward_keys(q, k, v, do, mask, 0.52, keys, chunk=8)
+    np.testing.assert_allclose(sk, dk[keys], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(sv, dv[keys], rtol=1e-11, atol=1e-12)

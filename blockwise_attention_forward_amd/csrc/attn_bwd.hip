@@ -56,6 +56,7 @@ constexpr int kWaves = 4;     // waves per workgroup (one per SIMD)
 constexpr int kKeyBlock = 128;  // keys per dK/dV workgroup (32 per wave)
 constexpr int kRowBlock = 128;  // rows per dQ workgroup (32 per wave)
 constexpr int kTile = 64;       // rows of a streamed Q/dO tile, keys of a streamed K/V tile
+constexpr int kRing = 3;        // tile buffers in LDS
 constexpr int kAhead = 4;       // LDS operand reads run this many matrix-core steps ahead
 
 __device__ inline i64 xcd_remap(i64 id, i64 n) {
@@ -435,11 +436,12 @@ __device__ inline void kv_compute(const BwdLaunch& p, const uint8_t* qt, const u
 template <int D, int G, bool XM>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
     using C = Cfg<D>;
-    // Two tile buffers: the next tile's loads are in registers while this
-    // one is computed, and land in the other buffer afterwards.
-    __shared__ __attribute__((aligned(1024))) uint8_t qs[2][C::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t gs[2][C::TILE_BYTES];
-    __shared__ __attribute__((aligned(256))) float ss[2][256];  // LSE, delta, lo, hi of 64 rows
+    // Three tile buffers.  A tile's loads go to registers two iterations
+    // before it is computed and land in LDS one iteration before, so each
+    // load has a whole tile of compute to arrive.
+    __shared__ __attribute__((aligned(1024))) uint8_t qs[kRing][C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t gs[kRing][C::TILE_BYTES];
+    __shared__ __attribute__((aligned(256))) float ss[kRing][256];  // LSE, delta, lo, hi of 64 rows
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hb = lane >> 5;
     const i64 logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -467,23 +469,30 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
     const int m0 = ld_const(p.kfirst, lb * p.nkb + kb), m1 = ld_const(p.klast, lb * p.nkb + kb);
     QCursor cur{0, m0 - 1};
     bool have = m0 <= m1 && q_next(p, cur, lb, m0, m1, k0, k0 + kKeyBlock);
+    // Prologue: the first tile in LDS, the second in registers.
     KvStage<D> stg;
+    QCursor ahead = cur;  // the tile whose loads are in registers
+    bool staged = false;
     if (have) {
         kv_load<D>(p, stg, cur, b, hk, lb);
         kv_store<D>(stg, qs[0], gs[0], ss[0]);
+        staged = q_next(p, ahead, lb, m0, m1, k0, k0 + kKeyBlock);
+        if (staged) kv_load<D>(p, stg, ahead, b, hk, lb);
     }
     int buf = 0;
     while (have) {
-        // Buffer `buf` is complete, and every wave is done with the other one.
+        // Buffer `buf` is complete, and every wave is done with the buffer of
+        // the tile before it, which takes the staged tile now.
         __syncthreads();
-        QCursor nxt = cur;
-        const bool more = q_next(p, nxt, lb, m0, m1, k0, k0 + kKeyBlock);
-        if (more) kv_load<D>(p, stg, nxt, b, hk, lb);
+        const int nb = buf == kRing - 1 ? 0 : buf + 1;
+        if (staged) {
+            kv_store<D>(stg, qs[nb], gs[nb], ss[nb]);
+            staged = q_next(p, ahead, lb, m0, m1, k0, k0 + kKeyBlock);
+            if (staged) kv_load<D>(p, stg, ahead, b, hk, lb);
+        }
         kv_compute<D, XM>(p, qs[buf], gs[buf], ss[buf], kf, vf, dk, dv, cur, b, lb, kw0);
-        if (more) kv_store<D>(stg, qs[buf ^ 1], gs[buf ^ 1], ss[buf ^ 1]);
-        cur = nxt;
-        have = more;
-        buf ^= 1;
+        have = q_next(p, cur, lb, m0, m1, k0, k0 + kKeyBlock);
+        buf = nb;
     }
     if (key < p.Lk) {
         const i64 es = G == BWA_F32 ? 4 : 2;
@@ -619,8 +628,8 @@ __device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const ui
 template <int D, int G, bool XM>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dq(const BwdLaunch p) {
     using C = Cfg<D>;
-    __shared__ __attribute__((aligned(1024))) uint8_t ks[2][C::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t vs[2][C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t ks[kRing][C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t vs[kRing][C::TILE_BYTES];
     __shared__ int red[4 * kWaves];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hb = lane >> 5;
@@ -678,28 +687,33 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq(const BwdLaunch p) {
     const int t_lo = env_lo < env_hi ? env_lo / kTile : 0;
     const int t_hi = env_lo < env_hi ? (env_hi + kTile - 1) / kTile : 0;
 
+    // Same pipeline as the dK/dV kernel: loads two tiles ahead in registers,
+    // stores one tile ahead into a ring of three buffers.
     TCursor cur{-1, 0};
     bool have = t_next(p, cur, t_lo, t_hi);
     QStage<D> stg;
+    TCursor ahead = cur;
+    bool staged = false;
     if (have) {
         q_load<D>(p, stg, cur.t, b, hk);
         stage_store<D>(stg.k, ks[0]);
         stage_store<D>(stg.v, vs[0]);
+        staged = t_next(p, ahead, t_lo, t_hi);
+        if (staged) q_load<D>(p, stg, ahead.t, b, hk);
     }
     int buf = 0;
     while (have) {
         __syncthreads();
-        TCursor nxt = cur;
-        const bool more = t_next(p, nxt, t_lo, t_hi);
-        if (more) q_load<D>(p, stg, nxt.t, b, hk);
-        q_compute<D, XM>(p, ks[buf], vs[buf], qf, gf, dq, cur.t, full_lo, full_hi, lo, hi, lse2, delt, b, row);
-        if (more) {
-            stage_store<D>(stg.k, ks[buf ^ 1]);
-            stage_store<D>(stg.v, vs[buf ^ 1]);
+        const int nb = buf == kRing - 1 ? 0 : buf + 1;
+        if (staged) {
+            stage_store<D>(stg.k, ks[nb]);
+            stage_store<D>(stg.v, vs[nb]);
+            staged = t_next(p, ahead, t_lo, t_hi);
+            if (staged) q_load<D>(p, stg, ahead.t, b, hk);
         }
-        cur = nxt;
-        have = more;
-        buf ^= 1;
+        q_compute<D, XM>(p, ks[buf], vs[buf], qf, gf, dq, cur.t, full_lo, full_hi, lo, hi, lse2, delt, b, row);
+        have = t_next(p, cur, t_lo, t_hi);
+        buf = nb;
     }
     if (row_ok) {
         const i64 es = G == BWA_F32 ? 4 : 2;

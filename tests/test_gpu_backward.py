@@ -195,7 +195,7 @@ PAGE = [("sliding_window", 512, 4096, 4096), ("sliding_window", 1024, 4096, 8192
 def _page_mask(kind, W, Lq, Lk):
     if kind == "sliding_window":
         return {"causal": True, "window": W, "kv_offset": Lq - Lk}
-    return synth.make_page_mask(kind, Lq, Lk)
+    return synth.make_page_mask(kind, Lq, Lk)["mask"]
 
 
 @pytest.mark.slow

@@ -1,7 +1,7 @@
 """Benchmark of the blockwise attention forward hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dit_share]
-                    [--launch auto|plain|balanced]
+                    [--launch auto|plain|balanced] [--pass fwd|bwd]
 
 Prints ONE JSON line.  A step is one pass of the whole hot path over one
 batch of synthetic input already resident in HBM.  The default workload is
@@ -25,6 +25,11 @@ launch     = plain (one workgroup per query block) or balanced (one
              second kernel); auto takes balanced from 4 rounds of blocks up.
 cpu_baseline = the fp64 oracle timed on the host on a bounded sample of the
              same workload (rank 0, N = 1 only).
+--pass bwd  = (single-call workloads) time the backward pass instead: a step
+             is one bwa_attn_bwd call (dK/dV and dQ kernels plus their plan
+             and delta passes) on O and LSE from one forward call made before
+             the timed region; FLOPs are counted as 10*D per visible pair of
+             the same tiles (five matrix products: scores, dP, dV, dK, dQ).
 measured_ceilings = what this device sustains, beside the published peaks: a
              bf16 matrix-core probe (register operands only; libbwa_probe.so)
              and a plain 1 GiB elementwise copy.
@@ -299,7 +304,7 @@ def setup_single(torch, bw, synth, name, launch="auto"):
 
     info = dict(workload=desc, B=B, H=H, D=D, Lq=Lq, Lk=Lk, **launch_info)
     return dict(step=step, flops_step=flops, flops_dominant=flops, dominant="hop", info=info,
-                sample_oracle=sample_oracle)
+                sample_oracle=sample_oracle, data=d)
 
 
 def _measured_ceilings(torch):
@@ -367,6 +372,8 @@ def main():
                     help="dit_share (default) is the measured configuration; the others time one masked call")
     ap.add_argument("--launch", default="auto", choices=["auto", "plain", "balanced"],
                     help="attention launch; auto: balanced from 4 rounds of query blocks per compute unit up")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
+                    help="bwd: time the backward pass of a single-call workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 3 plain elementwise copies of MIB MiB (scale for HBM byte counters)")
@@ -393,6 +400,9 @@ def main():
         del src, dst
     if args.workload != "dit_share":
         return run_single(args, torch, bw, synth)
+    if args.which == "bwd":
+        print("--pass bwd times a single-call workload (window, varlen, a page mask, long_causal)", file=sys.stderr)
+        sys.exit(2)
     W = setup_dit_share(torch, bw, synth, args.launch)
     timer = Timer(torch)
     for _ in range(args.warmup):
@@ -486,9 +496,56 @@ def main():
     print(json.dumps(out))
 
 
+def setup_backward(torch, bw, synth, W):
+    """The backward pass of a single-call workload: O and LSE from one forward
+    call, then a step is one bwa_attn_bwd call (bf16 gradients)."""
+    d = W["data"]
+    q, k, v, scale = d["q"], d["k"], d["v"], d["scale"]
+    B, Lq, H, D = q.shape
+    Lk = k.shape[1]
+    mask = bw.Mask.of(d["mask"], "cuda")
+    o, lse = bw.bwa_attn_fwd(q, k, v, mask, scale=scale, out_dtype=torch.bfloat16)
+    do = synth.normal(tuple(q.shape), 404, "cuda", torch.bfloat16)
+    ws = torch.empty(max(bw.bwa_attn_bwd_workspace(mask, B, H, Lq, Lk, "cuda"), 1), dtype=torch.uint8, device="cuda")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    torch.cuda.synchronize()
+    flops = 2.5 * W["flops_step"]
+
+    def step(timer=None):
+        tok = timer.start("hop") if timer else None
+        bw.bwa_attn_bwd(q, k, v, o, lse, do, mask, scale=scale, workspace=ws, dq=dq, dk=dk, dv=dv)
+        if timer:
+            timer.stop(tok)
+
+    def sample_oracle():
+        import oracle
+        rows = synth.sample_rows(Lq, 512, seed=11, must=[0, Lq - 1])
+        m = dict(d["mask"])
+        for key in ("segment_ids_q", "segment_ids_kv"):  # batch element 0
+            if m.get(key) is not None and getattr(m[key], "ndim", 1) == 2:
+                m[key] = m[key][0]
+        qh, kh, vh, gh = (x[0, :, 0].double().cpu().numpy() for x in (q, k, v, do))
+        t0 = time.perf_counter()
+        oracle.attention_backward_rows(qh, kh, vh, gh, m, scale, rows)
+        dt = time.perf_counter() - t0
+        visible = sum(int(oracle.visibility([r], Lk, m, Lq).sum()) for r in rows)
+        fl = 8.0 * D * float(visible)
+        return fl, dt, (f"dQ of head 0, {len(rows)} seeded query rows against their visible keys, fp64; "
+                        "8*D FLOP per visible pair (scores, O, dP and dQ products)")
+
+    info = {key: W["info"][key] for key in ("workload", "B", "H", "D", "Lq", "Lk")}
+    info["workload"] = "backward of " + info["workload"] + "; bf16 gradients, O and LSE from one forward call"
+    return dict(step=step, flops_step=flops, flops_dominant=flops, dominant="hop", info=info,
+                sample_oracle=sample_oracle)
+
+
 def run_single(args, torch, bw, synth):
     """A masked workload: one attention call per step (bf16 in and out)."""
     W = setup_single(torch, bw, synth, args.workload, args.launch)
+    if args.which == "bwd":
+        W = setup_backward(torch, bw, synth, W)
     timer = Timer(torch)
     for _ in range(args.warmup):
         W["step"]()
@@ -508,13 +565,15 @@ def run_single(args, torch, bw, synth):
         fl, dt, what = W["sample_oracle"]()
         cpu = {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
                "sample": what, "seconds": round(dt, 3), "host_cores_available": len(os.sched_getaffinity(0))}
+    bwd = args.which == "bwd"
     out = {
-        "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak; ms per call",
+        "metric": ("attention bwd TFLOP/s and % of bf16 MFMA peak; ms per call" if bwd else
+                   "attention fwd TFLOP/s and % of bf16 MFMA peak; ms per call"),
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic", "config": W["info"],
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "ms_attention": round(ms_hop, 4),
+        ("ms_backward" if bwd else "ms_attention"): round(ms_hop, 4),
         "counted_TFLOP": round(W["flops_step"] / 1e12, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},

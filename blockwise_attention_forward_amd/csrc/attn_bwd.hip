@@ -35,10 +35,23 @@
 // skipped, run unmasked (every pair visible) or compare key by key, as in
 // the forward pass.
 
+#include <utility>
+
 #include "internal.h"
 
 namespace bwa {
 namespace {
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, each i a compile-time
+// constant in the body (array indices stay registers).
+template <class F, int... I>
+__device__ __attribute__((always_inline)) inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -54,7 +67,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBig = 0x7fffffff;
 constexpr int kWaves = 4;     // waves per workgroup (one per SIMD)
 constexpr int kKeyBlock = 128;  // keys per dK/dV workgroup (32 per wave)
-constexpr int kRowBlock = 128;  // rows per dQ workgroup (32 per wave)
+#ifndef BWA_DQ_WAVES
+#define BWA_DQ_WAVES 8
+#endif
+constexpr int kDqWaves = BWA_DQ_WAVES;  // waves per dQ workgroup (32 rows each; 8 = two per SIMD)
 constexpr int kTile = 64;       // rows of a streamed Q/dO tile, keys of a streamed K/V tile
 constexpr int kRing = 3;        // tile buffers in LDS
 constexpr int kAhead = 4;       // LDS operand reads run this many matrix-core steps ahead
@@ -110,31 +126,31 @@ __device__ inline int bswz(int r, int c) {
     return D == 128 ? c ^ (((r & 3) << 2) | ((r >> 2) & 3)) : c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
-// A 64-row tile staged through registers: each work-item loads D/32 chunks
-// of 16 bytes (chunk id = it*256 + tid: row id / NCH, chunk id % NCH, so a
-// row's chunks come from consecutive lanes), then stores each at its
+// A 64-row tile staged through registers: each of NT work-items loads 8D/NT
+// chunks of 16 bytes (chunk id = it*NT + tid: row id / NCH, chunk id % NCH,
+// so a row's chunks come from consecutive lanes), then stores each at its
 // swizzled place in LDS.  Rows at or past `nvalid` are zeros.
-template <int D>
+template <int D, int NT = 256>
 struct Staged {
-    uint4 c[D / 32];
+    uint4 c[8 * D / NT];
 };
 
-template <int D>
-__device__ inline void stage_load(Staged<D>& x, const __bf16* base, i64 sL, int nvalid) {
+template <int D, int NT = 256>
+__device__ inline void stage_load(Staged<D, NT>& x, const __bf16* base, i64 sL, int nvalid) {
     constexpr int NCH = Cfg<D>::NCH;
 #pragma unroll
-    for (int it = 0; it < D / 32; ++it) {
-        const int id = it * 256 + (int)threadIdx.x, r = id / NCH, c = id % NCH;
+    for (int it = 0; it < 8 * D / NT; ++it) {
+        const int id = it * NT + (int)threadIdx.x, r = id / NCH, c = id % NCH;
         x.c[it] = r < nvalid ? *(const uint4*)(base + (i64)r * sL + c * 8) : uint4{0, 0, 0, 0};
     }
 }
 
-template <int D>
-__device__ inline void stage_store(const Staged<D>& x, uint8_t* t) {
+template <int D, int NT = 256>
+__device__ inline void stage_store(const Staged<D, NT>& x, uint8_t* t) {
     constexpr int NCH = Cfg<D>::NCH;
 #pragma unroll
-    for (int it = 0; it < D / 32; ++it) {
-        const int id = it * 256 + (int)threadIdx.x, r = id / NCH, c = id % NCH;
+    for (int it = 0; it < 8 * D / NT; ++it) {
+        const int id = it * NT + (int)threadIdx.x, r = id / NCH, c = id % NCH;
         *(uint4*)(t + r * (D * 2) + bswz<D>(r, c) * 16) = x.c[it];
     }
 }
@@ -349,88 +365,95 @@ __device__ inline void kv_store(const KvStage<D>& x, uint8_t* qt, uint8_t* gt, f
     st[threadIdx.x] = x.st;
 }
 
+// One 64-row query tile against the wave's 32 keys: 64 matrix-core steps in
+// one stream, with the element-wise work of each 32-row chunk (P, dS and
+// their bf16 packing, in four slices of 4 rows) issued between the products
+// of the next phase, so that it runs while the matrix core works:
+//   steps [0, NS)            S, dP of chunk 0
+//   steps [NS, 2NS)          S, dP of chunk 1      + slices of chunk 0
+//   steps [2NS, 2NS+NM)      dV, dK of chunk 0     + slices of chunk 1
+//   steps [2NS+NM, 2NS+2NM)  dV, dK of chunk 1
+// (NS = 2 D/16 score steps, NM = 4 D/32 update steps per chunk).  S and dP
+// alternate between their two accumulation chains; LDS operand reads run
+// kAhead steps ahead of their use.
 template <int D, bool XM>
 __device__ inline void kv_compute(const BwdLaunch& p, const uint8_t* qt, const uint8_t* gt, const float* st,
                                   const uint4 (&kf)[D / 16], const uint4 (&vf)[D / 16], f32x16 (&dk)[D / 32],
                                   f32x16 (&dv)[D / 32], const QCursor& c, i64 b, i64 lb, int kw0) {
     using C = Cfg<D>;
+    constexpr int NS = 2 * C::NDS, NM = 4 * C::NDB, NT = 2 * NS + 2 * NM;
     const int lane = threadIdx.x & 63, l32 = lane & 31, hb = lane >> 5;
     const int key = kw0 + l32;
     const i32x4 s = ld_const((const i32x4*)p.qsum, lb * p.nqt + c.m);
     const bool masked = XM || !(s[2] <= kw0 && kw0 + 32 <= s[3]);
     const float sc = p.scale * kLog2e;
-#pragma unroll
-    for (int rc = 0; rc < 2; ++rc) {
-        // S = Q K^T and dP = dO V^T over this chunk of 32 rows: 2*NDS steps,
-        // operand reads kAhead steps ahead of their use.
-        constexpr int NS = 2 * C::NDS;
-        auto ld_sg = [&](int i) { return i < C::NDS ? frag_rows<D>(qt, rc, i) : frag_rows<D>(gt, rc, i - C::NDS); };
-        f32x16 S = {}, G = {};
-        uint4 fa[NS];
-#pragma unroll
-        for (int i = 0; i < kAhead; ++i) fa[i] = ld_sg(i);
-#pragma unroll
-        for (int i = 0; i < NS; ++i) {
-            if (i + kAhead < NS) fa[i + kAhead] = ld_sg(i + kAhead);
-            if (i < C::NDS) S = mfma(fa[i], kf[i], S);
-            else G = mfma(fa[i], vf[i - C::NDS], G);
-            __builtin_amdgcn_sched_barrier(0);
+    f32x16 S[2] = {f32x16{}, f32x16{}}, G[2] = {f32x16{}, f32x16{}};
+    uint4 pp[2][2], pd[2][2];  // bf16 P and dS per chunk and 16-row step
+
+    auto ld = [&](const int i) __attribute__((always_inline)) {
+        if (i < 2 * NS) {
+            const int rc = i / NS, j = i % NS;
+            return (j & 1) ? frag_rows<D>(gt, rc, j >> 1) : frag_rows<D>(qt, rc, j >> 1);
         }
-        // This lane's rows of the tile: rc*32 + 8*g + 4*hb + e.
-        uint4 pp[2], pd[2];
+        const int m = i - 2 * NS, rc = m / NM, j = m % NM;
+        const int k2 = j / (2 * C::NDB), w = (j / C::NDB) & 1, db = j % C::NDB;
+        return frag_cols<D>(w ? qt : gt, rc * 2 + k2, db);
+    };
+    // Rows rc*32 + 8g + 4hb + e of this lane: P and dS of slice g.
+    auto slice = [&](const int rc, const int g) __attribute__((always_inline)) {
+        const int rb = rc * 32 + 8 * g + 4 * hb;
+        const f32x4 L = *(const f32x4*)(st + rb);
+        const f32x4 Dl = *(const f32x4*)(st + 64 + rb);
+        float pv[4], dv4[4];
+        if (masked) {
+            const i32x4 lo = *(const i32x4*)(st + 128 + rb);
+            const i32x4 hi = *(const i32x4*)(st + 192 + rb);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int rb = rc * 32 + 8 * g + 4 * hb;
-            const f32x4 L = *(const f32x4*)(st + rb);
-            const f32x4 Dl = *(const f32x4*)(st + 64 + rb);
-            float pv[4], dv4[4];
-            if (masked) {
-                const i32x4 lo = *(const i32x4*)(st + 128 + rb);
-                const i32x4 hi = *(const i32x4*)(st + 192 + rb);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    bool vis = lo[e] <= key && key < hi[e];
-                    if (XM && vis) vis = xvisible(p, b, c.m * kTile + rb + e, key);
-                    const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * g + e], sc, -L[e] * kLog2e));
-                    pv[e] = vis ? x : 0.0f;
-                    dv4[e] = vis ? x * (G[4 * g + e] - Dl[e]) : 0.0f;
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * g + e], sc, -L[e] * kLog2e));
-                    dv4[e] = pv[e] * (G[4 * g + e] - Dl[e]);
-                }
+            for (int e = 0; e < 4; ++e) {
+                bool vis = lo[e] <= key && key < hi[e];
+                if (XM && vis) vis = xvisible(p, b, c.m * kTile + rb + e, key);
+                const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rc][4 * g + e], sc, -L[e] * kLog2e));
+                pv[e] = vis ? x : 0.0f;
+                dv4[e] = vis ? x * (G[rc][4 * g + e] - Dl[e]) : 0.0f;
             }
-            const uint32_t a0 = pack_bf16x2(pv[0], pv[1]), a1 = pack_bf16x2(pv[2], pv[3]);
-            const uint32_t b0 = pack_bf16x2(dv4[0], dv4[1]), b1 = pack_bf16x2(dv4[2], dv4[3]);
-            if (g & 1) {
-                pp[g >> 1].z = a0; pp[g >> 1].w = a1;
-                pd[g >> 1].z = b0; pd[g >> 1].w = b1;
-            } else {
-                pp[g >> 1].x = a0; pp[g >> 1].y = a1;
-                pd[g >> 1].x = b0; pd[g >> 1].y = b1;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rc][4 * g + e], sc, -L[e] * kLog2e));
+                dv4[e] = pv[e] * (G[rc][4 * g + e] - Dl[e]);
             }
         }
-        // dV^T += dO^T P and dK^T += Q^T dS over the chunk's two 16-row steps:
-        // step i = (k2, which, db) with which 0 = dV, 1 = dK.
-        constexpr int NM = 4 * C::NDB;
-        auto ld_m = [&](int i) {
-            const int k2 = i / (2 * C::NDB), w = (i / C::NDB) & 1, db = i % C::NDB;
-            return frag_cols<D>(w ? qt : gt, rc * 2 + k2, db);
-        };
-        uint4 fb[NM];
-#pragma unroll
-        for (int i = 0; i < kAhead; ++i) fb[i] = ld_m(i);
-#pragma unroll
-        for (int i = 0; i < NM; ++i) {
-            if (i + kAhead < NM) fb[i + kAhead] = ld_m(i + kAhead);
-            const int k2 = i / (2 * C::NDB), w = (i / C::NDB) & 1, db = i % C::NDB;
-            if (w) dk[db] = mfma(fb[i], pd[k2], dk[db]);
-            else dv[db] = mfma(fb[i], pp[k2], dv[db]);
-            __builtin_amdgcn_sched_barrier(0);
+        const uint32_t a0 = pack_bf16x2(pv[0], pv[1]), a1 = pack_bf16x2(pv[2], pv[3]);
+        const uint32_t b0 = pack_bf16x2(dv4[0], dv4[1]), b1 = pack_bf16x2(dv4[2], dv4[3]);
+        if (g & 1) {
+            pp[rc][g >> 1].z = a0; pp[rc][g >> 1].w = a1;
+            pd[rc][g >> 1].z = b0; pd[rc][g >> 1].w = b1;
+        } else {
+            pp[rc][g >> 1].x = a0; pp[rc][g >> 1].y = a1;
+            pd[rc][g >> 1].x = b0; pd[rc][g >> 1].y = b1;
         }
-    }
+    };
+
+    uint4 fa[NT];
+    static_for<kAhead>([&](auto ic) { fa[ic.value] = ld(ic.value); });
+    static_for<NT>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + kAhead < NT) fa[i + kAhead] = ld(i + kAhead);
+        if constexpr (i < 2 * NS) {
+            constexpr int rc = i / NS, j = i % NS;
+            if constexpr (j & 1) G[rc] = mfma(fa[i], vf[j >> 1], G[rc]);
+            else S[rc] = mfma(fa[i], kf[j >> 1], S[rc]);
+        } else {
+            constexpr int m = i - 2 * NS, rc = m / NM, j = m % NM;
+            constexpr int k2 = j / (2 * C::NDB), w = (j / C::NDB) & 1, db = j % C::NDB;
+            if constexpr (w) dk[db] = mfma(fa[i], pd[rc][k2], dk[db]);
+            else dv[db] = mfma(fa[i], pp[rc][k2], dv[db]);
+        }
+        if constexpr (i >= NS && i < 2 * NS && (i - NS) % (NS / 4) == NS / 4 - 1) slice(0, (i - NS) / (NS / 4));
+        if constexpr (i >= 2 * NS && i < 2 * NS + NM && (i - 2 * NS) % (NM / 4) == NM / 4 - 1)
+            slice(1, (i - 2 * NS) / (NM / 4));
+        __builtin_amdgcn_sched_barrier(0);
+    });
 }
 
 template <int D, int G, bool XM>
@@ -550,96 +573,167 @@ __device__ inline bool t_next(const BwdLaunch& p, TCursor& c, int t_lo, int t_hi
     }
 }
 
-template <int D>
+template <int D, int NT>
 struct QStage {
-    Staged<D> k, v;
+    Staged<D, NT> k, v;
 };
 
-template <int D>
-__device__ inline void q_load(const BwdLaunch& p, QStage<D>& x, int t, i64 b, i64 hk) {
+template <int D, int NT>
+__device__ inline void q_load(const BwdLaunch& p, QStage<D, NT>& x, int t, i64 b, i64 hk) {
     const i64 j0 = (i64)t * kTile;
     const int nk = (int)min((i64)kTile, p.mask.kv_valid - j0);
-    stage_load<D>(x.k, (const __bf16*)p.k + b * p.k_sB + j0 * p.k_sL + hk * p.k_sH, p.k_sL, nk);
-    stage_load<D>(x.v, (const __bf16*)p.v + b * p.v_sB + j0 * p.v_sL + hk * p.v_sH, p.v_sL, nk);
+    stage_load<D, NT>(x.k, (const __bf16*)p.k + b * p.k_sB + j0 * p.k_sL + hk * p.k_sH, p.k_sL, nk);
+    stage_load<D, NT>(x.v, (const __bf16*)p.v + b * p.v_sB + j0 * p.v_sL + hk * p.v_sH, p.v_sL, nk);
 }
 
+// One 64-key tile against the wave's 32 rows: 48 matrix-core steps in one
+// stream, the element-wise work of each 32-key half (dS and its bf16
+// packing, four slices of 4 keys) issued between the products of the next
+// phase:
+//   steps [0, NS)                S^T, dP^T of half 0
+//   steps [NS, 2NS)              S^T, dP^T of half 1   + slices of half 0
+//   steps [2NS, 2NS+NM/2)        dQ^T over half 0      + slices of half 1
+//   steps [2NS+NM/2, 2NS+NM)     dQ^T over half 1
 template <int D, bool XM>
 __device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const uint8_t* vt,
                                  const uint4 (&qf)[D / 16], const uint4 (&gf)[D / 16], f32x16 (&dq)[D / 32],
                                  int t, int full_lo, int full_hi, int lo, int hi, float lse2, float delt, i64 b,
                                  int row) {
     using C = Cfg<D>;
+    constexpr int NS = 2 * C::NDS, NM = 4 * C::NDB, NH = NM / 2, NT = 2 * NS + NM;
     const int lane = threadIdx.x & 63, hb = lane >> 5;
     const int j0 = t * kTile;
     const bool masked = XM || !(full_lo <= j0 && j0 + kTile <= full_hi);
     const float sc = p.scale * kLog2e;
-    uint4 pd[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        // S^T = K Q^T and dP^T = V dO^T over this half of 32 keys.
-        constexpr int NS = 2 * C::NDS;
-        auto ld_sg = [&](int i) { return i < C::NDS ? frag_rows<D>(kt, kb, i) : frag_rows<D>(vt, kb, i - C::NDS); };
-        f32x16 S = {}, G = {};
-        uint4 fa[NS];
-#pragma unroll
-        for (int i = 0; i < kAhead; ++i) fa[i] = ld_sg(i);
-#pragma unroll
-        for (int i = 0; i < NS; ++i) {
-            if (i + kAhead < NS) fa[i + kAhead] = ld_sg(i + kAhead);
-            if (i < C::NDS) S = mfma(fa[i], qf[i], S);
-            else G = mfma(fa[i], gf[i - C::NDS], G);
-            __builtin_amdgcn_sched_barrier(0);
+    f32x16 S[2] = {f32x16{}, f32x16{}}, G[2] = {f32x16{}, f32x16{}};
+    uint4 pd[2][2];  // bf16 dS per half and 16-key step
+
+    auto ld = [&](const int i) __attribute__((always_inline)) {
+        if (i < 2 * NS) {
+            const int kb = i / NS, j = i % NS;
+            return (j & 1) ? frag_rows<D>(vt, kb, j >> 1) : frag_rows<D>(kt, kb, j >> 1);
         }
-        // This lane's keys: j0 + kb*32 + 8*g + 4*hb + e.
+        const int m = i - 2 * NS;
+        return frag_cols<D>(kt, m / C::NDB, m % C::NDB);
+    };
+    // Keys j0 + kb*32 + 8g + 4hb + e of this lane's row: dS of slice g.
+    auto slice = [&](const int kb, const int g) __attribute__((always_inline)) {
+        float dsv[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            float dsv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * g + e], sc, -lse2));
-                if (masked) {
-                    const int key = j0 + kb * 32 + 8 * g + 4 * hb + e;
-                    bool vis = lo <= key && key < hi;
-                    if (XM && vis) vis = xvisible(p, b, row, key);
-                    dsv[e] = vis ? x * (G[4 * g + e] - delt) : 0.0f;
-                } else {
-                    dsv[e] = x * (G[4 * g + e] - delt);
-                }
+        for (int e = 0; e < 4; ++e) {
+            const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][4 * g + e], sc, -lse2));
+            if (masked) {
+                const int key = j0 + kb * 32 + 8 * g + 4 * hb + e;
+                bool vis = lo <= key && key < hi;
+                if (XM && vis) vis = xvisible(p, b, row, key);
+                dsv[e] = vis ? x * (G[kb][4 * g + e] - delt) : 0.0f;
+            } else {
+                dsv[e] = x * (G[kb][4 * g + e] - delt);
             }
-            const uint32_t a0 = pack_bf16x2(dsv[0], dsv[1]), a1 = pack_bf16x2(dsv[2], dsv[3]);
-            if (g & 1) { pd[kb][g >> 1].z = a0; pd[kb][g >> 1].w = a1; }
-            else { pd[kb][g >> 1].x = a0; pd[kb][g >> 1].y = a1; }
         }
-    }
-    // dQ^T += K^T dS^T over the tile's four 16-key steps.
-    constexpr int NM = 4 * C::NDB;
-    uint4 fb[NM];
-#pragma unroll
-    for (int i = 0; i < kAhead; ++i) fb[i] = frag_cols<D>(kt, i / C::NDB, i % C::NDB);
-#pragma unroll
-    for (int i = 0; i < NM; ++i) {
-        if (i + kAhead < NM) fb[i + kAhead] = frag_cols<D>(kt, (i + kAhead) / C::NDB, (i + kAhead) % C::NDB);
-        const int kk = i / C::NDB, db = i % C::NDB;
-        dq[db] = mfma(fb[i], pd[kk >> 1][kk & 1], dq[db]);
+        const uint32_t a0 = pack_bf16x2(dsv[0], dsv[1]), a1 = pack_bf16x2(dsv[2], dsv[3]);
+        if (g & 1) { pd[kb][g >> 1].z = a0; pd[kb][g >> 1].w = a1; }
+        else { pd[kb][g >> 1].x = a0; pd[kb][g >> 1].y = a1; }
+    };
+
+    uint4 fa[NT];
+    static_for<kAhead>([&](auto ic) { fa[ic.value] = ld(ic.value); });
+    static_for<NT>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + kAhead < NT) fa[i + kAhead] = ld(i + kAhead);
+        if constexpr (i < 2 * NS) {
+            constexpr int kb = i / NS, j = i % NS;
+            if constexpr (j & 1) G[kb] = mfma(fa[i], gf[j >> 1], G[kb]);
+            else S[kb] = mfma(fa[i], qf[j >> 1], S[kb]);
+        } else {
+            constexpr int m = i - 2 * NS, kk = m / C::NDB, db = m % C::NDB;
+            dq[db] = mfma(fa[i], pd[kk >> 1][kk & 1], dq[db]);
+        }
+        if constexpr (i >= NS && i < 2 * NS && (i - NS) % (NS / 4) == NS / 4 - 1) slice(0, (i - NS) / (NS / 4));
+        if constexpr (i >= 2 * NS && i < 2 * NS + NH && (i - 2 * NS) % (NH / 4) == NH / 4 - 1)
+            slice(1, (i - 2 * NS) / (NH / 4));
         __builtin_amdgcn_sched_barrier(0);
-    }
+    });
 }
 
-template <int D, int G, bool XM>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dq(const BwdLaunch p) {
+// The same tile with two waves per SIMD (the other wave's products cover
+// this one's element-wise work): each half runs its scores, its dS and its
+// own dQ products in turn, so only one half's scores and dS are live.
+template <int D, bool XM>
+__device__ inline void q_compute_seq(const BwdLaunch& p, const uint8_t* kt, const uint8_t* vt,
+                                     const uint4 (&qf)[D / 16], const uint4 (&gf)[D / 16], f32x16 (&dq)[D / 32],
+                                     int t, int full_lo, int full_hi, int lo, int hi, float lse2, float delt, i64 b,
+                                     int row) {
     using C = Cfg<D>;
+    constexpr int NS = 2 * C::NDS, NH = 2 * C::NDB, NP = NS + NH;  // steps per half
+    constexpr int AH = 2;                                            // read-ahead
+    const int lane = threadIdx.x & 63, hb = lane >> 5;
+    const int j0 = t * kTile;
+    const bool masked = XM || !(full_lo <= j0 && j0 + kTile <= full_hi);
+    const float sc = p.scale * kLog2e;
+    static_for<2>([&](auto kbc) {
+        constexpr int kb = decltype(kbc)::value;
+        f32x16 S = {}, G = {};
+        uint4 pd[2];
+        auto ld = [&](const int i) __attribute__((always_inline)) {
+            if (i < NS) return (i & 1) ? frag_rows<D>(vt, kb, i >> 1) : frag_rows<D>(kt, kb, i >> 1);
+            const int m = i - NS;
+            return frag_cols<D>(kt, kb * 2 + m / C::NDB, m % C::NDB);
+        };
+        uint4 fa[NP];
+        static_for<AH>([&](auto ic) { fa[ic.value] = ld(ic.value); });
+        static_for<NP>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (i + AH < NP) fa[i + AH] = ld(i + AH);
+            if constexpr (i < NS) {
+                if constexpr (i & 1) G = mfma(fa[i], gf[i >> 1], G);
+                else S = mfma(fa[i], qf[i >> 1], S);
+            } else {
+                constexpr int m = i - NS;
+                dq[m % C::NDB] = mfma(fa[i], pd[m / C::NDB], dq[m % C::NDB]);
+            }
+            if constexpr (i == NS - 1) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float dsv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * g + e], sc, -lse2));
+                        if (masked) {
+                            const int key = j0 + kb * 32 + 8 * g + 4 * hb + e;
+                            bool vis = lo <= key && key < hi;
+                            if (XM && vis) vis = xvisible(p, b, row, key);
+                            dsv[e] = vis ? x * (G[4 * g + e] - delt) : 0.0f;
+                        } else {
+                            dsv[e] = x * (G[4 * g + e] - delt);
+                        }
+                    }
+                    const uint32_t a0 = pack_bf16x2(dsv[0], dsv[1]), a1 = pack_bf16x2(dsv[2], dsv[3]);
+                    if (g & 1) { pd[g >> 1].z = a0; pd[g >> 1].w = a1; }
+                    else { pd[g >> 1].x = a0; pd[g >> 1].y = a1; }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    });
+}
+
+template <int D, int G, bool XM, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
+    using C = Cfg<D>;
+    constexpr int NT = NW * 64, RB = NW * 32;  // work-items, rows per workgroup
     __shared__ __attribute__((aligned(1024))) uint8_t ks[kRing][C::TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t vs[kRing][C::TILE_BYTES];
-    __shared__ int red[4 * kWaves];
+    __shared__ int red[4 * NW];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hb = lane >> 5;
-    const i64 nqb = (p.Lq + kRowBlock - 1) / kRowBlock;
+    const i64 nqb = (p.Lq + RB - 1) / RB;
     const i64 logical = xcd_remap(blockIdx.x, gridDim.x);
     const i64 bh = logical / nqb;
     const i64 qb = nqb - 1 - logical % nqb;  // the blocks with the most key tiles first
     const i64 b = bh / p.H, h = bh % p.H, hk = h / p.kv_group;
     const i64 lb = p.list_batch == 1 ? 0 : b;
-    const int row = (int)(qb * kRowBlock) + wave * 32 + l32;
+    const int row = (int)(qb * RB) + wave * 32 + l32;
     const bool row_ok = row < p.Lq;
     const bool row_in = row < p.mask.q_valid;  // rows past q_valid are zeros (and see nothing)
 
@@ -677,7 +771,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq(const BwdLaunch p) {
     __syncthreads();
     int env_lo = kBig, env_hi = 0, full_lo = 0, full_hi = kBig;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
         env_lo = min(env_lo, red[w * 4 + 0]);
         env_hi = max(env_hi, red[w * 4 + 1]);
         full_lo = max(full_lo, red[w * 4 + 2]);
@@ -691,27 +785,30 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq(const BwdLaunch p) {
     // stores one tile ahead into a ring of three buffers.
     TCursor cur{-1, 0};
     bool have = t_next(p, cur, t_lo, t_hi);
-    QStage<D> stg;
+    QStage<D, NT> stg;
     TCursor ahead = cur;
     bool staged = false;
     if (have) {
-        q_load<D>(p, stg, cur.t, b, hk);
-        stage_store<D>(stg.k, ks[0]);
-        stage_store<D>(stg.v, vs[0]);
+        q_load<D, NT>(p, stg, cur.t, b, hk);
+        stage_store<D, NT>(stg.k, ks[0]);
+        stage_store<D, NT>(stg.v, vs[0]);
         staged = t_next(p, ahead, t_lo, t_hi);
-        if (staged) q_load<D>(p, stg, ahead.t, b, hk);
+        if (staged) q_load<D, NT>(p, stg, ahead.t, b, hk);
     }
     int buf = 0;
     while (have) {
         __syncthreads();
         const int nb = buf == kRing - 1 ? 0 : buf + 1;
         if (staged) {
-            stage_store<D>(stg.k, ks[nb]);
-            stage_store<D>(stg.v, vs[nb]);
+            stage_store<D, NT>(stg.k, ks[nb]);
+            stage_store<D, NT>(stg.v, vs[nb]);
             staged = t_next(p, ahead, t_lo, t_hi);
-            if (staged) q_load<D>(p, stg, ahead.t, b, hk);
+            if (staged) q_load<D, NT>(p, stg, ahead.t, b, hk);
         }
-        q_compute<D, XM>(p, ks[buf], vs[buf], qf, gf, dq, cur.t, full_lo, full_hi, lo, hi, lse2, delt, b, row);
+        if constexpr (NW == 4)
+            q_compute<D, XM>(p, ks[buf], vs[buf], qf, gf, dq, cur.t, full_lo, full_hi, lo, hi, lse2, delt, b, row);
+        else
+            q_compute_seq<D, XM>(p, ks[buf], vs[buf], qf, gf, dq, cur.t, full_lo, full_hi, lo, hi, lse2, delt, b, row);
         have = t_next(p, cur, t_lo, t_hi);
         buf = nb;
     }
@@ -733,10 +830,13 @@ hipError_t launch_dg(const BwdLaunch& a, hipStream_t stream) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const i64 nqb_total = (i64)a.B * a.H * ((a.Lq + kRowBlock - 1) / kRowBlock);
+    constexpr int NW = kDqWaves;
+    const i64 nqb_total = (i64)a.B * a.H * ((a.Lq + 32 * NW - 1) / (32 * NW));
     if (nqb_total > 0) {
-        if (xm) hipLaunchKernelGGL((attn_bwd_dq<D, G, true>), dim3((unsigned)nqb_total), dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((attn_bwd_dq<D, G, false>), dim3((unsigned)nqb_total), dim3(256), 0, stream, a);
+        if (xm)
+            hipLaunchKernelGGL((attn_bwd_dq<D, G, true, NW>), dim3((unsigned)nqb_total), dim3(64 * NW), 0, stream, a);
+        else
+            hipLaunchKernelGGL((attn_bwd_dq<D, G, false, NW>), dim3((unsigned)nqb_total), dim3(64 * NW), 0, stream, a);
     }
     return hipGetLastError();
 }

@@ -193,12 +193,23 @@ __device__ inline f32x16 mfma(const uint4& a, const uint4& b, const f32x16& c) {
                                                    0, 0);
 }
 
-// Element terms of the mask beyond the row interval (dilated bands, document ids).
-__device__ inline bool xvisible(const BwdLaunch& p, i64 b, int row, int key) {
+// Element terms of the mask beyond the row interval: the dilated band's
+// residue, and equal document ids (row_id, key_id: the ids of the pair; the
+// callers read them without per-element memory loads).
+__device__ inline bool xvisible(const BwdLaunch& p, int row, int key, int row_id, int key_id) {
     bool ok = true;
     if (p.mask.dilation > 1) ok = ((unsigned)((i64)row - key - p.mask.kv_offset) % (unsigned)p.mask.dilation) == 0;
-    if (p.mask.seg_mode == 3) ok = ok && p.mask.ids_q[b * p.mask.lq + row] == p.mask.ids_kv[b * p.mask.lk + key];
+    if (p.mask.seg_mode == 3) ok = ok && row_id == key_id;
     return ok;
+}
+
+// Document ids of keys j .. j+7 (j the same in every lane; clamped to the
+// last key): scalar loads, so nothing waits behind the tile loads in flight.
+__device__ inline void key_ids8(const BwdLaunch& p, i64 b, int j, int (&id)[8]) {
+    const int* kid = p.mask.ids_kv + b * p.mask.lk;
+    const int last = (int)p.mask.lk - 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) id[i] = ld_const(kid, min(j + i, last));
 }
 
 __device__ inline int wave_min(int x) {
@@ -336,6 +347,7 @@ template <int D>
 struct KvStage {
     Staged<D> q, g;
     float st;
+    int id;  // document id of row tid (work-items 0..63, document masks only)
 };
 
 template <int D>
@@ -356,13 +368,15 @@ __device__ inline void kv_load(const BwdLaunch& p, KvStage<D>& x, const QCursor&
         else v = __int_as_float(p.row_hi[lb * p.Lq + row]);
     }
     x.st = v;
+    if (p.mask.seg_mode == 3 && wave == 0) x.id = row < p.Lq ? p.mask.ids_q[b * p.mask.lq + row] : -1;
 }
 
 template <int D>
-__device__ inline void kv_store(const KvStage<D>& x, uint8_t* qt, uint8_t* gt, float* st) {
+__device__ inline void kv_store(const BwdLaunch& p, const KvStage<D>& x, uint8_t* qt, uint8_t* gt, float* st) {
     stage_store<D>(x.q, qt);
     stage_store<D>(x.g, gt);
     st[threadIdx.x] = x.st;
+    if (p.mask.seg_mode == 3 && threadIdx.x < 64) st[256 + threadIdx.x] = __int_as_float(x.id);
 }
 
 // One 64-row query tile against the wave's 32 keys: 64 matrix-core steps in
@@ -379,7 +393,7 @@ __device__ inline void kv_store(const KvStage<D>& x, uint8_t* qt, uint8_t* gt, f
 template <int D, bool XM>
 __device__ inline void kv_compute(const BwdLaunch& p, const uint8_t* qt, const uint8_t* gt, const float* st,
                                   const uint4 (&kf)[D / 16], const uint4 (&vf)[D / 16], f32x16 (&dk)[D / 32],
-                                  f32x16 (&dv)[D / 32], const QCursor& c, i64 b, i64 lb, int kw0) {
+                                  f32x16 (&dv)[D / 32], const QCursor& c, i64 lb, int kw0, int key_id) {
     using C = Cfg<D>;
     constexpr int NS = 2 * C::NDS, NM = 4 * C::NDB, NT = 2 * NS + 2 * NM;
     const int lane = threadIdx.x & 63, l32 = lane & 31, hb = lane >> 5;
@@ -408,10 +422,12 @@ __device__ inline void kv_compute(const BwdLaunch& p, const uint8_t* qt, const u
         if (masked) {
             const i32x4 lo = *(const i32x4*)(st + 128 + rb);
             const i32x4 hi = *(const i32x4*)(st + 192 + rb);
+            i32x4 rid = {0, 0, 0, 0};
+            if (XM && p.mask.seg_mode == 3) rid = *(const i32x4*)(st + 256 + rb);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 bool vis = lo[e] <= key && key < hi[e];
-                if (XM && vis) vis = xvisible(p, b, c.m * kTile + rb + e, key);
+                if (XM && vis) vis = xvisible(p, c.m * kTile + rb + e, key, rid[e], key_id);
                 const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rc][4 * g + e], sc, -L[e] * kLog2e));
                 pv[e] = vis ? x : 0.0f;
                 dv4[e] = vis ? x * (G[rc][4 * g + e] - Dl[e]) : 0.0f;
@@ -464,7 +480,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
     // load has a whole tile of compute to arrive.
     __shared__ __attribute__((aligned(1024))) uint8_t qs[kRing][C::TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t gs[kRing][C::TILE_BYTES];
-    __shared__ __attribute__((aligned(256))) float ss[kRing][256];  // LSE, delta, lo, hi of 64 rows
+    __shared__ __attribute__((aligned(256))) float ss[kRing][320];  // LSE, delta, lo, hi, doc id of 64 rows
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hb = lane >> 5;
     const i64 logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -487,6 +503,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
     f32x16 dk[C::NDB], dv[C::NDB];
 #pragma unroll
     for (int d = 0; d < C::NDB; ++d) { dk[d] = f32x16{}; dv[d] = f32x16{}; }
+    const int key_id = (XM && p.mask.seg_mode == 3 && key < p.Lk) ? p.mask.ids_kv[b * p.mask.lk + key] : -1;
     wait_loads();
 
     const int m0 = ld_const(p.kfirst, lb * p.nkb + kb), m1 = ld_const(p.klast, lb * p.nkb + kb);
@@ -498,7 +515,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
     bool staged = false;
     if (have) {
         kv_load<D>(p, stg, cur, b, hk, lb);
-        kv_store<D>(stg, qs[0], gs[0], ss[0]);
+        kv_store<D>(p, stg, qs[0], gs[0], ss[0]);
         staged = q_next(p, ahead, lb, m0, m1, k0, k0 + kKeyBlock);
         if (staged) kv_load<D>(p, stg, ahead, b, hk, lb);
     }
@@ -509,11 +526,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
         __syncthreads();
         const int nb = buf == kRing - 1 ? 0 : buf + 1;
         if (staged) {
-            kv_store<D>(stg, qs[nb], gs[nb], ss[nb]);
+            kv_store<D>(p, stg, qs[nb], gs[nb], ss[nb]);
             staged = q_next(p, ahead, lb, m0, m1, k0, k0 + kKeyBlock);
             if (staged) kv_load<D>(p, stg, ahead, b, hk, lb);
         }
-        kv_compute<D, XM>(p, qs[buf], gs[buf], ss[buf], kf, vf, dk, dv, cur, b, lb, kw0);
+        kv_compute<D, XM>(p, qs[buf], gs[buf], ss[buf], kf, vf, dk, dv, cur, lb, kw0, key_id);
         have = q_next(p, cur, lb, m0, m1, k0, k0 + kKeyBlock);
         buf = nb;
     }
@@ -598,7 +615,7 @@ template <int D, bool XM>
 __device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const uint8_t* vt,
                                  const uint4 (&qf)[D / 16], const uint4 (&gf)[D / 16], f32x16 (&dq)[D / 32],
                                  int t, int full_lo, int full_hi, int lo, int hi, float lse2, float delt, i64 b,
-                                 int row) {
+                                 int row, int row_id) {
     using C = Cfg<D>;
     constexpr int NS = 2 * C::NDS, NM = 4 * C::NDB, NH = NM / 2, NT = 2 * NS + NM;
     const int lane = threadIdx.x & 63, hb = lane >> 5;
@@ -619,13 +636,15 @@ __device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const ui
     // Keys j0 + kb*32 + 8g + 4hb + e of this lane's row: dS of slice g.
     auto slice = [&](const int kb, const int g) __attribute__((always_inline)) {
         float dsv[4];
+        int kid[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (XM && masked && p.mask.seg_mode == 3) key_ids8(p, b, j0 + kb * 32 + 8 * g, kid);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][4 * g + e], sc, -lse2));
             if (masked) {
                 const int key = j0 + kb * 32 + 8 * g + 4 * hb + e;
                 bool vis = lo <= key && key < hi;
-                if (XM && vis) vis = xvisible(p, b, row, key);
+                if (XM && vis) vis = xvisible(p, row, key, row_id, hb ? kid[4 + e] : kid[e]);
                 dsv[e] = vis ? x * (G[kb][4 * g + e] - delt) : 0.0f;
             } else {
                 dsv[e] = x * (G[kb][4 * g + e] - delt);
@@ -663,7 +682,7 @@ template <int D, bool XM>
 __device__ inline void q_compute_seq(const BwdLaunch& p, const uint8_t* kt, const uint8_t* vt,
                                      const uint4 (&qf)[D / 16], const uint4 (&gf)[D / 16], f32x16 (&dq)[D / 32],
                                      int t, int full_lo, int full_hi, int lo, int hi, float lse2, float delt, i64 b,
-                                     int row) {
+                                     int row, int row_id) {
     using C = Cfg<D>;
     constexpr int NS = 2 * C::NDS, NH = 2 * C::NDB, NP = NS + NH;  // steps per half
     constexpr int AH = 2;                                            // read-ahead
@@ -696,13 +715,15 @@ __device__ inline void q_compute_seq(const BwdLaunch& p, const uint8_t* kt, cons
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     float dsv[4];
+                    int kid[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                    if (XM && masked && p.mask.seg_mode == 3) key_ids8(p, b, j0 + kb * 32 + 8 * g, kid);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * g + e], sc, -lse2));
                         if (masked) {
                             const int key = j0 + kb * 32 + 8 * g + 4 * hb + e;
                             bool vis = lo <= key && key < hi;
-                            if (XM && vis) vis = xvisible(p, b, row, key);
+                            if (XM && vis) vis = xvisible(p, row, key, row_id, hb ? kid[4 + e] : kid[e]);
                             dsv[e] = vis ? x * (G[4 * g + e] - delt) : 0.0f;
                         } else {
                             dsv[e] = x * (G[4 * g + e] - delt);
@@ -746,6 +767,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
         lse2 = p.lse[li] * kLog2e;
         delt = p.delta[li];
     }
+    const int row_id = (XM && p.mask.seg_mode == 3 && row_ok) ? p.mask.ids_q[b * p.mask.lq + row] : -1;
     // Q and dO rows of this lane as the B operand: d = ds*16 + hb*8 + 0..7.
     uint4 qf[C::NDS], gf[C::NDS];
     const __bf16* qp = (const __bf16*)p.q + b * p.q_sB + (i64)row * p.q_sL + h * p.q_sH;
@@ -806,9 +828,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
             if (staged) q_load<D, NT>(p, stg, ahead.t, b, hk);
         }
         if constexpr (NW == 4)
-            q_compute<D, XM>(p, ks[buf], vs[buf], qf, gf, dq, cur.t, full_lo, full_hi, lo, hi, lse2, delt, b, row);
+            q_compute<D, XM>(p, ks[buf], vs[buf], qf, gf, dq, cur.t, full_lo, full_hi, lo, hi, lse2, delt, b, row,
+                             row_id);
         else
-            q_compute_seq<D, XM>(p, ks[buf], vs[buf], qf, gf, dq, cur.t, full_lo, full_hi, lo, hi, lse2, delt, b, row);
+            q_compute_seq<D, XM>(p, ks[buf], vs[buf], qf, gf, dq, cur.t, full_lo, full_hi, lo, hi, lse2, delt, b, row,
+                                 row_id);
         have = t_next(p, cur, t_lo, t_hi);
         buf = nb;
     }

@@ -51,6 +51,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
@@ -328,6 +329,32 @@ __device__ inline void xmask32(f32x16& s, int jb, int xres, int xdoc, const XMas
     }
 }
 
+// The same for the bf16 walk, with the tile's key ids staged in LDS next to
+// its K and V (kidl: ids of the tile's 64 keys; kb0: 0 or 32, the block's
+// first key in the tile).  A lane reads its 16 keys' ids as 4 runs of 4.
+__device__ inline void xmask32_lds(f32x16& s, int jb, int kb0, int xres, int xdoc, const XMask& xm,
+                                   const int* kidl) {
+    const int hb = (threadIdx.x >> 5) & 1;
+    const int jl = jb + hb * 4;  // the key of r = 0
+    unsigned bits = 0xffffffffu;
+    if (xm.g > 1) {
+        const int m = ((xres - jl % xm.g) % xm.g + xm.g) % xm.g;
+        bits = m < 32 ? (xm.pat << m) : 0u;
+    }
+    i32x4 idg[4] = {};
+    if (xm.kid) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) idg[q] = *(const i32x4*)(kidl + kb0 + hb * 4 + 8 * q);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int o = 8 * (r >> 2) + (r & 3);
+        bool ok = (bits >> o) & 1u;
+        if (xm.kid) ok = ok && jl + o < xm.lk && idg[r >> 2][r & 3] == xdoc;
+        s[r] = ok ? s[r] : kNegInf;
+    }
+}
+
 template <int NKB, int NDB>
 __device__ inline void online_update(f32x16 (&s)[NKB], f32x16 (&acc)[NDB], float& m_run, float& l_run,
                                      float scale_l2) {
@@ -510,11 +537,19 @@ template <int D> __device__ inline int v_swz(int r, int c) {
 }
 
 // Issue the HBM -> LDS copies of one K and one V tile (rows past kv_lim read as zero).
-template <int D, int NW>
+template <int D, int NW, bool XM = false>
 __device__ inline void bf16_issue_tile(const AttnLaunch& p, const __bf16* kbase, const __bf16* vbase, int j0,
-                                       int kv_lim, uint8_t* kl, uint8_t* vl) {
+                                       int kv_lim, uint8_t* kl, uint8_t* vl, int* kidl, const XMask& xm) {
     using C = Bf16Cfg<D, NW>;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (XM && xm.kid) {
+        // Document ids of the tile's keys (4 bytes per lane; every wave
+        // writes the same bytes, so each wave's copy count stays the same).
+        const int n = uni(min(max(xm.lk - j0, 0), C::TILE));
+        const __amdgpu_buffer_rsrc_t ir = __builtin_amdgcn_make_buffer_rsrc((void*)(xm.kid + j0), 0, n * 4,
+                                                                            kRsrcFlags);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ir, (lds_void*)kidl, 4, (unsigned)(lane * 4), 0, 0, 0);
+    }
     const int nvalid = uni(min(max(kv_lim - j0, 0), C::TILE));
     const int kbytes = uni((int)(nvalid * p.k_sL * 2)), vbytes = uni((int)(nvalid * p.v_sL * 2));
     const __amdgpu_buffer_rsrc_t kr =
@@ -600,7 +635,7 @@ __device__ inline float half_online_ref(const Half& x, float& m_run, float scale
 
 template <int D, int NW, int BODY, bool XM>
 __device__ inline void bf16_compute_tile(const uint8_t* kl, const uint8_t* vl, Bf16State<D, NW>& st, int j0,
-                                         bool masked, const XMask& xm) {
+                                         bool masked, const XMask& xm, const int* kidl) {
     using C = Bf16Cfg<D, NW>;
     constexpr int NDS = C::NDS, NDB = C::NDB;
     const int lane = threadIdx.x & 63, l32 = lane & 31, hb = lane >> 5;
@@ -657,7 +692,7 @@ __device__ inline void bf16_compute_tile(const uint8_t* kl, const uint8_t* vl, B
     float alpha = 1.0f;
     if (masked) {
         half_mask(h0, j0, 0, st.lo, st.hi);
-        if (XM) xmask32(h0.s, j0, st.xres, st.xdoc, xm);
+        if (XM) xmask32_lds(h0.s, j0, 0, st.xres, st.xdoc, xm, kidl);
     }
     uint4 vf[4 * NDB];
 #pragma unroll
@@ -686,7 +721,7 @@ __device__ inline void bf16_compute_tile(const uint8_t* kl, const uint8_t* vl, B
     // online reference settled under the first step, as above).
     if (masked) {
         half_mask(h1, j0, 1, st.lo, st.hi);
-        if (XM) xmask32(h1.s, j0 + 32, st.xres, st.xdoc, xm);
+        if (XM) xmask32_lds(h1.s, j0 + 32, 32, st.xres, st.xdoc, xm, kidl);
     }
     bool resc1 = false;
     float alpha1 = 1.0f;
@@ -730,6 +765,22 @@ __device__ inline void wait_vm(int n) {
     else __builtin_amdgcn_s_waitcnt(0x0F7C);
 }
 
+// Wait until at most n (0 .. 8) of this wave's vector-memory operations are
+// in flight; n is wave-uniform.
+__device__ inline void wait_vm_exact(int n) {
+    switch (n) {
+        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+        case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+        case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+        case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+        case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+}
+
 // The copy ring: NBUF K/V tile buffers, each its own LDS object, visited in
 // a compile-time unrolled order.  Reads of buffer I can then be told apart
 // from the copies still landing in the other buffers, so they do not wait
@@ -740,6 +791,7 @@ struct Ring {
     using C = Bf16Cfg<D, NW>;
     uint8_t* k[C::NBUF];
     uint8_t* v[C::NBUF];
+    int* kid[C::NBUF];  // document ids of the keys (element-test kernels only)
 };
 
 template <int D, int NW, int BODY, bool XM, int I, class W>
@@ -755,15 +807,16 @@ __device__ __attribute__((always_inline)) inline bool bf16_step(const AttnLaunch
     const bool masked = cur.masked(walk.Lk);
     // This tile's copies are complete in every wave, and every wave is done
     // with the buffer the next copy goes to (the previous tile's).
-    wait_vm(n_after * LOADS);
+    if (XM && xm.kid) wait_vm_exact(n_after * (LOADS + 1));  // K, V and the key ids
+    else wait_vm(n_after * LOADS);
     __syncthreads();
     if (more) more = ahead.next(walk);
     if (more) {
         constexpr int J = (I + NB - 1) % NB;
-        bf16_issue_tile<D, NW>(p, kbase, vbase, ahead.j0, kv_lim, ring.k[J], ring.v[J]);
+        bf16_issue_tile<D, NW, XM>(p, kbase, vbase, ahead.j0, kv_lim, ring.k[J], ring.v[J], ring.kid[J], xm);
         ++n_after;
     }
-    bf16_compute_tile<D, NW, BODY, XM>(ring.k[I], ring.v[I], st, j0, masked, xm);
+    bf16_compute_tile<D, NW, BODY, XM>(ring.k[I], ring.v[I], st, j0, masked, xm, ring.kid[I]);
     const bool have = cur.next(walk);
     if (have) --n_after;
     return have;
@@ -789,11 +842,11 @@ __device__ inline void bf16_walk(const AttnLaunch& p, Bf16State<D, NW>& st, cons
     ahead = cur;
     bool more = have;
     int n_after = 0;  // tiles issued beyond the current one
-    if (have) bf16_issue_tile<D, NW>(p, kbase, vbase, ahead.j0, kv_lim, ring.k[0], ring.v[0]);
+    if (have) bf16_issue_tile<D, NW, XM>(p, kbase, vbase, ahead.j0, kv_lim, ring.k[0], ring.v[0], ring.kid[0], xm);
     if (NB == 3) {
         if (more) more = ahead.next(walk);
         if (more) {
-            bf16_issue_tile<D, NW>(p, kbase, vbase, ahead.j0, kv_lim, ring.k[1], ring.v[1]);
+            bf16_issue_tile<D, NW, XM>(p, kbase, vbase, ahead.j0, kv_lim, ring.k[1], ring.v[1], ring.kid[1], xm);
             ++n_after;
         }
     }
@@ -825,9 +878,14 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_bf16(const 
     __shared__ __attribute__((aligned(1024))) uint8_t k1[C::TILE_BYTES], v1[C::TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t k2[C::NBUF == 3 ? C::TILE_BYTES : 16];
     __shared__ __attribute__((aligned(1024))) uint8_t v2[C::NBUF == 3 ? C::TILE_BYTES : 16];
+    __shared__ __attribute__((aligned(256))) int kd0[XM ? 64 : 1], kd1[XM ? 64 : 1], kd2[XM ? 64 : 1];
     Ring<D, NW> ring;
     ring.k[0] = k0; ring.v[0] = v0; ring.k[1] = k1; ring.v[1] = v1;
     if (C::NBUF == 3) { ring.k[C::NBUF - 1] = k2; ring.v[C::NBUF - 1] = v2; }
+    if (XM) {
+        ring.kid[0] = kd0; ring.kid[1] = kd1;
+        if (C::NBUF == 3) ring.kid[C::NBUF - 1] = kd2;
+    }
     __shared__ int red[4 * NW];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;

@@ -137,6 +137,8 @@ __global__ __launch_bounds__(256) void runs_kernel(const BlocksLaunch a) {
 // there passes the dilation test (j = row position mod g) and has the row's
 // document id; the block is FULL iff every row of the block sees every key
 // of it.  One wavefront per (copy, query block) as above.
+constexpr int kMaxIds = 8;  // distinct document ids per key block on the fast test
+
 template <bool FILL>
 __global__ __launch_bounds__(256) void runs_exact_kernel(const BlocksLaunch a) {
     const i64 wg = (i64)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -203,13 +205,39 @@ __global__ __launch_bounds__(256) void runs_exact_kernel(const BlocksLaunch a) {
                     dmax = max(dmax, __shfl_xor(dmax, o));
                 }
             }
+            // The block's distinct document ids, up to kMaxIds (ballots over the
+            // keys, one id per round): a row whose interval covers the whole
+            // block sees it iff its id is among them, with no key scan.
+            int dset[kMaxIds];
+            int nd = 0;
+            bool few = docs && g == 1;
+            if (few) {
+                for (int u0 = j0; u0 < j1 && few; u0 += 64) {
+                    const int j = u0 + lane;
+                    const int myid = j < j1 ? kid[j] : 0;
+                    unsigned long long left = __ballot(j < j1);
+                    while (left) {
+                        const int src = __builtin_ctzll(left);
+                        const int d = __shfl(myid, src);
+                        bool known = false;
+                        for (int i = 0; i < nd; ++i) known |= dset[i] == d;
+                        if (!known) {
+                            if (nd == kMaxIds) { few = false; break; }
+                            dset[nd++] = d;
+                        }
+                        left &= ~__ballot(myid == d);
+                    }
+                }
+            }
             bool sees = false, misses = false;  // some row sees a key / some row misses a key
 #pragma unroll
             for (int t = 0; t < kMaxRowsPerLane; ++t) {
                 if (!rex[t]) continue;
                 const int lo = max(rlo[t], j0), hi = min(rhi[t], j1);
                 bool vis = false;
-                if (lo < hi && (!docs || (rdoc[t] >= dmin && rdoc[t] <= dmax))) {
+                if (few && lo == j0 && hi == j1) {
+                    for (int i = 0; i < nd; ++i) vis |= dset[i] == rdoc[t];
+                } else if (lo < hi && (!docs || (rdoc[t] >= dmin && rdoc[t] <= dmax))) {
                     // first key >= lo with the row's residue, then every g-th
                     int j = lo + ((rres[t] - lo % g) % g + g) % g;
                     if (!docs) {

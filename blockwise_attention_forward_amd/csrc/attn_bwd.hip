@@ -14,8 +14,10 @@
 //   * dK/dV: one workgroup per (batch, key/value head, 128-key block); it
 //     walks the query tiles that meet its keys (all query heads of a
 //     grouped-query head, in order) and writes dK and dV once.
-//   * dQ: one workgroup per (batch, head, 128-row block); it walks the key
+//   * dQ: one workgroup per (batch, head, 256-row block); it walks the key
 //     tiles of its rows in the chosen order and writes dQ once.
+// Both run 8 waves, two per SIMD, so that one wave's element-wise work and
+// LDS waits hide under the other's matrix products.
 // The score and probability tiles are computed in both kernels (two extra
 // matrix products over a pass that adds into dQ from the key-column
 // programs); in exchange every output is written exactly once, no atomics
@@ -26,12 +28,12 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - delta),  delta_i = dO_i . O_i,
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 // Matrix products run on the 32x32x16 bf16 matrix cores with fp32
-// accumulation; P and dS are rounded to bf16 as operands.  Tiles stream from
-// HBM straight into LDS (buffer loads with an LDS destination) in an XOR
-// swizzle of 16-byte chunks that serves both ways each tile is read: row by
-// row (an operand whose rows are the tile's rows) and transposed (the LDS
-// transpose read, an operand whose rows are the tile's columns); each read
-// hits distinct banks.  Per-row key intervals decide which tiles are
+// accumulation; P and dS are rounded to bf16 as operands.  Tiles are staged
+// through registers into LDS, each tile's loads issued a tile or two before
+// it is used, in an XOR swizzle of 16-byte chunks that serves both ways each
+// tile is read: row by row (an operand whose rows are the tile's rows) and
+// transposed (the LDS transpose read, an operand whose rows are the tile's
+// columns); each read hits distinct banks.  Per-row key intervals decide which tiles are
 // skipped, run unmasked (every pair visible) or compare key by key, as in
 // the forward pass.
 
@@ -65,15 +67,11 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBig = 0x7fffffff;
-constexpr int kWaves = 4;     // waves per workgroup (one per SIMD)
 constexpr int kKeyBlock = 128;  // keys per dK/dV workgroup (32 per wave)
-#ifndef BWA_DQ_WAVES
-#define BWA_DQ_WAVES 8
-#endif
-constexpr int kDqWaves = BWA_DQ_WAVES;  // waves per dQ workgroup (32 rows each; 8 = two per SIMD)
+constexpr int kDqWaves = 8;     // waves per dQ workgroup (32 rows each, two per SIMD)
 constexpr int kTile = 64;       // rows of a streamed Q/dO tile, keys of a streamed K/V tile
 constexpr int kRing = 3;        // tile buffers in LDS
-constexpr int kAhead = 4;       // LDS operand reads run this many matrix-core steps ahead
+constexpr int kAhead = 4;       // LDS operand reads run this many matrix-core steps ahead (4-wave dK/dV)
 
 __device__ inline i64 xcd_remap(i64 id, i64 n) {
     // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
@@ -319,12 +317,6 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdLaunch p) {
     if (r < n && (threadIdx.x % TPR) == 0) p.delta[(b * p.H + h) * p.Lq + i] = s;
 }
 
-// ---------------------------------------------------------------------------
-// dK / dV: 4 waves x 32 keys.  A wave keeps its keys' K and V rows as
-// operands in registers and accumulates dK^T and dV^T (32 d x 32 keys per
-// block of d) while 64-row tiles of Q and dO, with the rows' LSE, delta and
-// key intervals, stream through LDS.
-// ---------------------------------------------------------------------------
 struct QCursor {
     int g, m;  // query head within the group, query tile
 };
@@ -341,6 +333,239 @@ __device__ inline bool q_next(const BwdLaunch& p, QCursor& c, i64 lb, int m0, in
     }
 }
 
+// ---------------------------------------------------------------------------
+// dK / dV with two waves per SIMD: 8 waves = 4 key groups of 32 keys x 2 row
+// halves.  The workgroup's 128 keys of K and V sit in LDS (a wave's share of
+// 256 registers does not hold K, V and both accumulators); wave (kg, rh)
+// computes rows rh*32 .. rh*32+31 of every 64-row query tile against keys
+// kg*32 .. kg*32+31, and the two waves of a key group add their partial dK
+// and dV through LDS at the end (rh 0 + rh 1, a fixed order).  Query tiles
+// go through two LDS buffers, each tile's loads issued one tile ahead.
+// ---------------------------------------------------------------------------
+template <int D>
+struct KvStage8 {
+    Staged<D, 512> q, g;
+    float st;  // work-items 0..255: LSE, delta, lo, hi of row tid % 64
+};
+
+template <int D>
+__device__ inline void kv_load8(const BwdLaunch& p, KvStage8<D>& x, const QCursor& c, i64 b, i64 hk, i64 lb) {
+    const i64 h = hk * p.kv_group + c.g;
+    const i64 r0 = (i64)c.m * kTile;
+    const int nq = (int)min((i64)kTile, p.mask.q_valid - r0);
+    stage_load<D, 512>(x.q, (const __bf16*)p.q + b * p.q_sB + r0 * p.q_sL + h * p.q_sH, p.q_sL, nq);
+    stage_load<D, 512>(x.g, (const __bf16*)p.dout + b * p.do_sB + r0 * p.do_sL + h * p.do_sH, p.do_sL, nq);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const i64 row = r0 + lane;
+    const i64 li = (b * p.H + h) * p.Lq + row;
+    float v = 0.0f;
+    if (row < p.Lq) {
+        if (wave == 0) v = p.lse[li];
+        else if (wave == 1) v = p.delta[li];
+        else if (wave == 2) v = __int_as_float(p.row_lo[lb * p.Lq + row]);
+        else if (wave == 3) v = __int_as_float(p.row_hi[lb * p.Lq + row]);
+    }
+    x.st = v;
+}
+
+template <int D>
+__device__ inline void kv_store8(const BwdLaunch& p, const KvStage8<D>& x, uint8_t* qt, uint8_t* gt, float* st) {
+    stage_store<D, 512>(x.q, qt);
+    stage_store<D, 512>(x.g, gt);
+    if (threadIdx.x < 256) st[threadIdx.x] = x.st;
+}
+
+// Rows rh*32 .. rh*32+31 of one query tile against the wave's 32 keys (K and
+// V rows kg*32 + l32 of the LDS key tiles kt, vt): 2 D/16 score steps with
+// the S and dP chains alternating, the element-wise work, then 4 D/32 update
+// steps; LDS operand reads two steps ahead.
+template <int D>
+__device__ inline void kv_compute8(const BwdLaunch& p, const uint8_t* qt, const uint8_t* gt, const float* st,
+                                   const uint8_t* kt, const uint8_t* vt, int kr, f32x16 (&dk)[D / 32],
+                                   f32x16 (&dv)[D / 32], const QCursor& c, i64 lb, int kw0, int rh) {
+    using C = Cfg<D>;
+    constexpr int NS = 2 * C::NDS, NM = 4 * C::NDB, NT = NS + NM, AH = 2;
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hb = lane >> 5;
+    const int key = kw0 + l32;
+    const i32x4 s = ld_const((const i32x4*)p.qsum, lb * p.nqt + c.m);
+    const bool masked = !(s[2] <= kw0 && kw0 + 32 <= s[3]);
+    const float sc = p.scale * kLog2e;
+    f32x16 S = {}, G = {};
+    uint4 pp[2], pd[2];
+    // step i: A operand (and, for the score steps, the B operand) from LDS
+    struct Ops {
+        uint4 a, b;
+    };
+    auto ld = [&](const int i) __attribute__((always_inline)) {
+        Ops o;
+        if (i < NS) {
+            const int ds = i >> 1;
+            if (i & 1) { o.a = frag_rows<D>(gt, rh, ds); o.b = frag_rows<D>(vt, kr, ds); }
+            else { o.a = frag_rows<D>(qt, rh, ds); o.b = frag_rows<D>(kt, kr, ds); }
+        } else {
+            const int m = i - NS, k2 = m / (2 * C::NDB), w = (m / C::NDB) & 1, db = m % C::NDB;
+            o.a = frag_cols<D>(w ? qt : gt, rh * 2 + k2, db);
+            o.b = uint4{0, 0, 0, 0};
+        }
+        return o;
+    };
+    Ops fa[NT];
+    static_for<AH>([&](auto ic) { fa[ic.value] = ld(ic.value); });
+    static_for<NT>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + AH < NT) fa[i + AH] = ld(i + AH);
+        if constexpr (i < NS) {
+            if constexpr (i & 1) G = mfma(fa[i].a, fa[i].b, G);
+            else S = mfma(fa[i].a, fa[i].b, S);
+        } else {
+            constexpr int m = i - NS, k2 = m / (2 * C::NDB), w = (m / C::NDB) & 1, db = m % C::NDB;
+            if constexpr (w) dk[db] = mfma(fa[i].a, pd[k2], dk[db]);
+            else dv[db] = mfma(fa[i].a, pp[k2], dv[db]);
+        }
+        if constexpr (i == NS - 1) {
+            // P and dS of this lane's rows rh*32 + 8g + 4hb + e
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int rb = rh * 32 + 8 * g + 4 * hb;
+                const f32x4 L = *(const f32x4*)(st + rb);
+                const f32x4 Dl = *(const f32x4*)(st + 64 + rb);
+                float pv[4], dv4[4];
+                if (masked) {
+                    const i32x4 lo = *(const i32x4*)(st + 128 + rb);
+                    const i32x4 hi = *(const i32x4*)(st + 192 + rb);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bool vis = lo[e] <= key && key < hi[e];
+                        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * g + e], sc, -L[e] * kLog2e));
+                        pv[e] = vis ? x : 0.0f;
+                        dv4[e] = vis ? x * (G[4 * g + e] - Dl[e]) : 0.0f;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * g + e], sc, -L[e] * kLog2e));
+                        dv4[e] = pv[e] * (G[4 * g + e] - Dl[e]);
+                    }
+                }
+                const uint32_t a0 = pack_bf16x2(pv[0], pv[1]), a1 = pack_bf16x2(pv[2], pv[3]);
+                const uint32_t b0 = pack_bf16x2(dv4[0], dv4[1]), b1 = pack_bf16x2(dv4[2], dv4[3]);
+                if (g & 1) {
+                    pp[g >> 1].z = a0; pp[g >> 1].w = a1;
+                    pd[g >> 1].z = b0; pd[g >> 1].w = b1;
+                } else {
+                    pp[g >> 1].x = a0; pp[g >> 1].y = a1;
+                    pd[g >> 1].x = b0; pd[g >> 1].y = b1;
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv8(const BwdLaunch p) {
+    using C = Cfg<D>;
+    // K and V of the 128 keys (two 64-row tiles each), Q / dO tiles (two
+    // buffers) and the rows' statistics.  At the end the four arrays hold the
+    // row-half-1 waves' partial dK and dV, one array per key group.
+    __shared__ __attribute__((aligned(1024))) uint8_t ks[2][C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t vs[2][C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t qs[2][C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t gs[2][C::TILE_BYTES];
+    __shared__ __attribute__((aligned(256))) float ss[2][256];  // LSE, delta, lo, hi of 64 rows
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31;
+    const int kg = wave & 3, rh = wave >> 2;  // key group, row half (waves w and w+4 share a SIMD)
+    const i64 logical = xcd_remap(blockIdx.x, gridDim.x);
+    const i64 bhk = logical / p.nkb, kb = logical % p.nkb;
+    const i64 b = bhk / p.Hk, hk = bhk % p.Hk;
+    const i64 lb = p.list_batch == 1 ? 0 : b;
+    const int k0 = (int)kb * kKeyBlock, kw0 = k0 + kg * 32;
+    const int key = kw0 + l32;
+
+    // The block's K and V rows (past kv_valid: zeros) into LDS.
+    {
+        Staged<D, 512> x;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int j0 = k0 + 64 * half;
+            const int nk = (int)min((i64)kTile, p.mask.kv_valid - j0);
+            stage_load<D, 512>(x, (const __bf16*)p.k + b * p.k_sB + (i64)j0 * p.k_sL + hk * p.k_sH, p.k_sL, nk);
+            stage_store<D, 512>(x, ks[half]);
+            stage_load<D, 512>(x, (const __bf16*)p.v + b * p.v_sB + (i64)j0 * p.v_sL + hk * p.v_sH, p.v_sL, nk);
+            stage_store<D, 512>(x, vs[half]);
+        }
+    }
+    f32x16 dk[C::NDB], dv[C::NDB];
+#pragma unroll
+    for (int d = 0; d < C::NDB; ++d) { dk[d] = f32x16{}; dv[d] = f32x16{}; }
+
+    const int m0 = ld_const(p.kfirst, lb * p.nkb + kb), m1 = ld_const(p.klast, lb * p.nkb + kb);
+    QCursor cur{0, m0 - 1};
+    bool have = m0 <= m1 && q_next(p, cur, lb, m0, m1, k0, k0 + kKeyBlock);
+    KvStage8<D> stg;
+    if (have) {
+        kv_load8<D>(p, stg, cur, b, hk, lb);
+        kv_store8<D>(p, stg, qs[0], gs[0], ss[0]);
+    }
+    wait_loads();
+    int buf = 0;
+    while (have) {
+        // Buffer `buf` (and the key tiles) are complete, and every wave is done
+        // with the other buffer.
+        __syncthreads();
+        QCursor nxt = cur;
+        const bool more = q_next(p, nxt, lb, m0, m1, k0, k0 + kKeyBlock);
+        if (more) kv_load8<D>(p, stg, nxt, b, hk, lb);
+        kv_compute8<D>(p, qs[buf], gs[buf], ss[buf], ks[kg >> 1], vs[kg >> 1], kg & 1, dk, dv, cur, lb, kw0, rh);
+        if (more) kv_store8<D>(p, stg, qs[buf ^ 1], gs[buf ^ 1], ss[buf ^ 1]);
+        cur = nxt;
+        have = more;
+        buf ^= 1;
+    }
+    // The row-half-1 wave of each key group hands its partial sums to the
+    // row-half-0 wave: lane-major, 8 D/32 x 16 floats per lane (32 KB).
+    __syncthreads();
+    float* red = (float*)(kg == 0 ? &ks[0][0] : kg == 1 ? &vs[0][0] : kg == 2 ? &qs[0][0] : &gs[0][0]);
+    if (rh == 1) {
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                red[((2 * db) * 16 + j) * 64 + lane] = dk[db][j];
+                red[((2 * db + 1) * 16 + j) * 64 + lane] = dv[db][j];
+            }
+    }
+    __syncthreads();
+    if (rh == 0) {
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                dk[db][j] += red[((2 * db) * 16 + j) * 64 + lane];
+                dv[db][j] += red[((2 * db + 1) * 16 + j) * 64 + lane];
+            }
+        if (key < p.Lk) {
+            const i64 es = G == BWA_F32 ? 4 : 2;
+            char* dkr = (char*)p.dk + (b * p.dk_sB + (i64)key * p.dk_sL + hk * p.dk_sH) * es;
+            char* dvr = (char*)p.dv + (b * p.dv_sB + (i64)key * p.dv_sL + hk * p.dv_sH) * es;
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db) {
+                store_tile<G>(dkr, dk[db], db, p.scale);
+                store_tile<G>(dvr, dv[db], db, 1.0f);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV for masks with element terms (dilated bands, document ids): 4 waves
+// x 32 keys, one wave per SIMD.  A wave keeps its keys' K and V rows as
+// operands in registers and accumulates dK^T and dV^T (32 d x 32 keys per
+// block of d) while 64-row tiles of Q and dO, with the rows' LSE, delta, key
+// intervals and document ids, stream through LDS.  The element test needs
+// registers that the two-wave form above does not have to spare.
+// ---------------------------------------------------------------------------
 // Loads of one query tile (Q, dO and the rows' LSE, delta and key interval)
 // into registers; the work-items of wave w load statistic w.
 template <int D>
@@ -390,16 +615,14 @@ __device__ inline void kv_store(const BwdLaunch& p, const KvStage<D>& x, uint8_t
 // (NS = 2 D/16 score steps, NM = 4 D/32 update steps per chunk).  S and dP
 // alternate between their two accumulation chains; LDS operand reads run
 // kAhead steps ahead of their use.
-template <int D, bool XM>
+template <int D>
 __device__ inline void kv_compute(const BwdLaunch& p, const uint8_t* qt, const uint8_t* gt, const float* st,
                                   const uint4 (&kf)[D / 16], const uint4 (&vf)[D / 16], f32x16 (&dk)[D / 32],
-                                  f32x16 (&dv)[D / 32], const QCursor& c, i64 lb, int kw0, int key_id) {
+                                  f32x16 (&dv)[D / 32], const QCursor& c, int kw0, int key_id) {
     using C = Cfg<D>;
     constexpr int NS = 2 * C::NDS, NM = 4 * C::NDB, NT = 2 * NS + 2 * NM;
     const int lane = threadIdx.x & 63, l32 = lane & 31, hb = lane >> 5;
     const int key = kw0 + l32;
-    const i32x4 s = ld_const((const i32x4*)p.qsum, lb * p.nqt + c.m);
-    const bool masked = XM || !(s[2] <= kw0 && kw0 + 32 <= s[3]);
     const float sc = p.scale * kLog2e;
     f32x16 S[2] = {f32x16{}, f32x16{}}, G[2] = {f32x16{}, f32x16{}};
     uint4 pp[2][2], pd[2][2];  // bf16 P and dS per chunk and 16-row step
@@ -418,26 +641,18 @@ __device__ inline void kv_compute(const BwdLaunch& p, const uint8_t* qt, const u
         const int rb = rc * 32 + 8 * g + 4 * hb;
         const f32x4 L = *(const f32x4*)(st + rb);
         const f32x4 Dl = *(const f32x4*)(st + 64 + rb);
+        const i32x4 lo = *(const i32x4*)(st + 128 + rb);
+        const i32x4 hi = *(const i32x4*)(st + 192 + rb);
+        i32x4 rid = {0, 0, 0, 0};
+        if (p.mask.seg_mode == 3) rid = *(const i32x4*)(st + 256 + rb);
         float pv[4], dv4[4];
-        if (masked) {
-            const i32x4 lo = *(const i32x4*)(st + 128 + rb);
-            const i32x4 hi = *(const i32x4*)(st + 192 + rb);
-            i32x4 rid = {0, 0, 0, 0};
-            if (XM && p.mask.seg_mode == 3) rid = *(const i32x4*)(st + 256 + rb);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bool vis = lo[e] <= key && key < hi[e];
-                if (XM && vis) vis = xvisible(p, c.m * kTile + rb + e, key, rid[e], key_id);
-                const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rc][4 * g + e], sc, -L[e] * kLog2e));
-                pv[e] = vis ? x : 0.0f;
-                dv4[e] = vis ? x * (G[rc][4 * g + e] - Dl[e]) : 0.0f;
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rc][4 * g + e], sc, -L[e] * kLog2e));
-                dv4[e] = pv[e] * (G[rc][4 * g + e] - Dl[e]);
-            }
+        for (int e = 0; e < 4; ++e) {
+            bool vis = lo[e] <= key && key < hi[e];
+            if (vis) vis = xvisible(p, c.m * kTile + rb + e, key, rid[e], key_id);
+            const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rc][4 * g + e], sc, -L[e] * kLog2e));
+            pv[e] = vis ? x : 0.0f;
+            dv4[e] = vis ? x * (G[rc][4 * g + e] - Dl[e]) : 0.0f;
         }
         const uint32_t a0 = pack_bf16x2(pv[0], pv[1]), a1 = pack_bf16x2(pv[2], pv[3]);
         const uint32_t b0 = pack_bf16x2(dv4[0], dv4[1]), b1 = pack_bf16x2(dv4[2], dv4[3]);
@@ -472,7 +687,7 @@ __device__ inline void kv_compute(const BwdLaunch& p, const uint8_t* qt, const u
     });
 }
 
-template <int D, int G, bool XM>
+template <int D, int G>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
     using C = Cfg<D>;
     // Three tile buffers.  A tile's loads go to registers two iterations
@@ -503,7 +718,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
     f32x16 dk[C::NDB], dv[C::NDB];
 #pragma unroll
     for (int d = 0; d < C::NDB; ++d) { dk[d] = f32x16{}; dv[d] = f32x16{}; }
-    const int key_id = (XM && p.mask.seg_mode == 3 && key < p.Lk) ? p.mask.ids_kv[b * p.mask.lk + key] : -1;
+    const int key_id = (p.mask.seg_mode == 3 && key < p.Lk) ? p.mask.ids_kv[b * p.mask.lk + key] : -1;
     wait_loads();
 
     const int m0 = ld_const(p.kfirst, lb * p.nkb + kb), m1 = ld_const(p.klast, lb * p.nkb + kb);
@@ -530,7 +745,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
             staged = q_next(p, ahead, lb, m0, m1, k0, k0 + kKeyBlock);
             if (staged) kv_load<D>(p, stg, ahead, b, hk, lb);
         }
-        kv_compute<D, XM>(p, qs[buf], gs[buf], ss[buf], kf, vf, dk, dv, cur, lb, kw0, key_id);
+        kv_compute<D>(p, qs[buf], gs[buf], ss[buf], kf, vf, dk, dv, cur, kw0, key_id);
         have = q_next(p, cur, lb, m0, m1, k0, k0 + kKeyBlock);
         buf = nb;
     }
@@ -547,9 +762,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ: 4 waves x 32 rows.  A wave keeps its rows' Q and dO as operands in
+
+// ---------------------------------------------------------------------------
+// dQ: 8 waves x 32 rows.  A wave keeps its rows' Q and dO as operands in
 // registers and accumulates dQ^T while 64-key tiles of K and V stream
-// through LDS in the chosen order.
+// through a ring of three LDS buffers in the chosen order.
 // ---------------------------------------------------------------------------
 // Key tiles of a query block in the chosen order: position r of a
 // permutation of all nkt tiles, keeping the tiles in [t_lo, t_hi).
@@ -603,83 +820,13 @@ __device__ inline void q_load(const BwdLaunch& p, QStage<D, NT>& x, int t, i64 b
     stage_load<D, NT>(x.v, (const __bf16*)p.v + b * p.v_sB + j0 * p.v_sL + hk * p.v_sH, p.v_sL, nk);
 }
 
-// One 64-key tile against the wave's 32 rows: 48 matrix-core steps in one
-// stream, the element-wise work of each 32-key half (dS and its bf16
-// packing, four slices of 4 keys) issued between the products of the next
-// phase:
-//   steps [0, NS)                S^T, dP^T of half 0
-//   steps [NS, 2NS)              S^T, dP^T of half 1   + slices of half 0
-//   steps [2NS, 2NS+NM/2)        dQ^T over half 0      + slices of half 1
-//   steps [2NS+NM/2, 2NS+NM)     dQ^T over half 1
+// One 64-key tile against the wave's 32 rows, with two waves per SIMD (the
+// other wave's products cover this one's element-wise work): each 32-key
+// half runs its S^T and dP^T products (the two chains alternating), its dS
+// and its own dQ^T products in turn, so only one half's scores and dS are
+// live; LDS operand reads run two steps ahead.
 template <int D, bool XM>
 __device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const uint8_t* vt,
-                                 const uint4 (&qf)[D / 16], const uint4 (&gf)[D / 16], f32x16 (&dq)[D / 32],
-                                 int t, int full_lo, int full_hi, int lo, int hi, float lse2, float delt, i64 b,
-                                 int row, int row_id) {
-    using C = Cfg<D>;
-    constexpr int NS = 2 * C::NDS, NM = 4 * C::NDB, NH = NM / 2, NT = 2 * NS + NM;
-    const int lane = threadIdx.x & 63, hb = lane >> 5;
-    const int j0 = t * kTile;
-    const bool masked = XM || !(full_lo <= j0 && j0 + kTile <= full_hi);
-    const float sc = p.scale * kLog2e;
-    f32x16 S[2] = {f32x16{}, f32x16{}}, G[2] = {f32x16{}, f32x16{}};
-    uint4 pd[2][2];  // bf16 dS per half and 16-key step
-
-    auto ld = [&](const int i) __attribute__((always_inline)) {
-        if (i < 2 * NS) {
-            const int kb = i / NS, j = i % NS;
-            return (j & 1) ? frag_rows<D>(vt, kb, j >> 1) : frag_rows<D>(kt, kb, j >> 1);
-        }
-        const int m = i - 2 * NS;
-        return frag_cols<D>(kt, m / C::NDB, m % C::NDB);
-    };
-    // Keys j0 + kb*32 + 8g + 4hb + e of this lane's row: dS of slice g.
-    auto slice = [&](const int kb, const int g) __attribute__((always_inline)) {
-        float dsv[4];
-        int kid[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (XM && masked && p.mask.seg_mode == 3) key_ids8(p, b, j0 + kb * 32 + 8 * g, kid);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][4 * g + e], sc, -lse2));
-            if (masked) {
-                const int key = j0 + kb * 32 + 8 * g + 4 * hb + e;
-                bool vis = lo <= key && key < hi;
-                if (XM && vis) vis = xvisible(p, row, key, row_id, hb ? kid[4 + e] : kid[e]);
-                dsv[e] = vis ? x * (G[kb][4 * g + e] - delt) : 0.0f;
-            } else {
-                dsv[e] = x * (G[kb][4 * g + e] - delt);
-            }
-        }
-        const uint32_t a0 = pack_bf16x2(dsv[0], dsv[1]), a1 = pack_bf16x2(dsv[2], dsv[3]);
-        if (g & 1) { pd[kb][g >> 1].z = a0; pd[kb][g >> 1].w = a1; }
-        else { pd[kb][g >> 1].x = a0; pd[kb][g >> 1].y = a1; }
-    };
-
-    uint4 fa[NT];
-    static_for<kAhead>([&](auto ic) { fa[ic.value] = ld(ic.value); });
-    static_for<NT>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        if constexpr (i + kAhead < NT) fa[i + kAhead] = ld(i + kAhead);
-        if constexpr (i < 2 * NS) {
-            constexpr int kb = i / NS, j = i % NS;
-            if constexpr (j & 1) G[kb] = mfma(fa[i], gf[j >> 1], G[kb]);
-            else S[kb] = mfma(fa[i], qf[j >> 1], S[kb]);
-        } else {
-            constexpr int m = i - 2 * NS, kk = m / C::NDB, db = m % C::NDB;
-            dq[db] = mfma(fa[i], pd[kk >> 1][kk & 1], dq[db]);
-        }
-        if constexpr (i >= NS && i < 2 * NS && (i - NS) % (NS / 4) == NS / 4 - 1) slice(0, (i - NS) / (NS / 4));
-        if constexpr (i >= 2 * NS && i < 2 * NS + NH && (i - 2 * NS) % (NH / 4) == NH / 4 - 1)
-            slice(1, (i - 2 * NS) / (NH / 4));
-        __builtin_amdgcn_sched_barrier(0);
-    });
-}
-
-// The same tile with two waves per SIMD (the other wave's products cover
-// this one's element-wise work): each half runs its scores, its dS and its
-// own dQ products in turn, so only one half's scores and dS are live.
-template <int D, bool XM>
-__device__ inline void q_compute_seq(const BwdLaunch& p, const uint8_t* kt, const uint8_t* vt,
                                      const uint4 (&qf)[D / 16], const uint4 (&gf)[D / 16], f32x16 (&dq)[D / 32],
                                      int t, int full_lo, int full_hi, int lo, int hi, float lse2, float delt, i64 b,
                                      int row, int row_id) {
@@ -827,12 +974,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
             staged = t_next(p, ahead, t_lo, t_hi);
             if (staged) q_load<D, NT>(p, stg, ahead.t, b, hk);
         }
-        if constexpr (NW == 4)
-            q_compute<D, XM>(p, ks[buf], vs[buf], qf, gf, dq, cur.t, full_lo, full_hi, lo, hi, lse2, delt, b, row,
-                             row_id);
-        else
-            q_compute_seq<D, XM>(p, ks[buf], vs[buf], qf, gf, dq, cur.t, full_lo, full_hi, lo, hi, lse2, delt, b, row,
-                                 row_id);
+        q_compute<D, XM>(p, ks[buf], vs[buf], qf, gf, dq, cur.t, full_lo, full_hi, lo, hi, lse2, delt, b, row,
+                         row_id);
         have = t_next(p, cur, t_lo, t_hi);
         buf = nb;
     }
@@ -849,8 +992,9 @@ hipError_t launch_dg(const BwdLaunch& a, hipStream_t stream) {
     const bool xm = a.mask.dilation > 1 || a.mask.seg_mode == 3;
     const i64 nkb_total = (i64)a.B * a.Hk * a.nkb;
     if (nkb_total > 0) {
-        if (xm) hipLaunchKernelGGL((attn_bwd_dkdv<D, G, true>), dim3((unsigned)nkb_total), dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((attn_bwd_dkdv<D, G, false>), dim3((unsigned)nkb_total), dim3(256), 0, stream, a);
+        // element masks: one wave per SIMD; interval masks: two
+        if (xm) hipLaunchKernelGGL((attn_bwd_dkdv<D, G>), dim3((unsigned)nkb_total), dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((attn_bwd_dkdv8<D, G>), dim3((unsigned)nkb_total), dim3(512), 0, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

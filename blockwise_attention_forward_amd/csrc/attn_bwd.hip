@@ -186,6 +186,15 @@ __device__ inline uint4 frag_cols(const uint8_t* t, int kk, int db) {
     return out;
 }
 
+// Keeps x where it is computed: with a masked select as its only user the
+// compiler would otherwise move the arithmetic that produces it into a
+// per-lane branch around the select (a branch and exec-mask updates per
+// element) instead of selecting.
+__device__ __attribute__((always_inline)) inline float pin(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 __device__ inline f32x16 mfma(const uint4& a, const uint4& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
                                                    0, 0);
@@ -436,9 +445,10 @@ __device__ inline void kv_compute8(const BwdLaunch& p, const uint8_t* qt, const 
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const bool vis = lo[e] <= key && key < hi[e];
-                        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * g + e], sc, -L[e] * kLog2e));
+                        const float x = pin(__builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * g + e], sc, -L[e] * kLog2e)));
+                        const float d = pin(x * (G[4 * g + e] - Dl[e]));
                         pv[e] = vis ? x : 0.0f;
-                        dv4[e] = vis ? x * (G[4 * g + e] - Dl[e]) : 0.0f;
+                        dv4[e] = vis ? d : 0.0f;
                     }
                 } else {
 #pragma unroll
@@ -650,9 +660,10 @@ __device__ inline void kv_compute(const BwdLaunch& p, const uint8_t* qt, const u
         for (int e = 0; e < 4; ++e) {
             bool vis = lo[e] <= key && key < hi[e];
             if (vis) vis = xvisible(p, c.m * kTile + rb + e, key, rid[e], key_id);
-            const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rc][4 * g + e], sc, -L[e] * kLog2e));
+            const float x = pin(__builtin_amdgcn_exp2f(__builtin_fmaf(S[rc][4 * g + e], sc, -L[e] * kLog2e)));
+            const float d = pin(x * (G[rc][4 * g + e] - Dl[e]));
             pv[e] = vis ? x : 0.0f;
-            dv4[e] = vis ? x * (G[rc][4 * g + e] - Dl[e]) : 0.0f;
+            dv4[e] = vis ? d : 0.0f;
         }
         const uint32_t a0 = pack_bf16x2(pv[0], pv[1]), a1 = pack_bf16x2(pv[2], pv[3]);
         const uint32_t b0 = pack_bf16x2(dv4[0], dv4[1]), b1 = pack_bf16x2(dv4[2], dv4[3]);
@@ -867,14 +878,14 @@ __device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const ui
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * g + e], sc, -lse2));
+                        float d = pin(x * (G[4 * g + e] - delt));
                         if (masked) {
                             const int key = j0 + kb * 32 + 8 * g + 4 * hb + e;
                             bool vis = lo <= key && key < hi;
                             if (XM && vis) vis = xvisible(p, row, key, row_id, hb ? kid[4 + e] : kid[e]);
-                            dsv[e] = vis ? x * (G[4 * g + e] - delt) : 0.0f;
-                        } else {
-                            dsv[e] = x * (G[4 * g + e] - delt);
+                            d = vis ? d : 0.0f;
                         }
+                        dsv[e] = d;
                     }
                     const uint32_t a0 = pack_bf16x2(dsv[0], dsv[1]), a1 = pack_bf16x2(dsv[2], dsv[3]);
                     if (g & 1) { pd[g >> 1].z = a0; pd[g >> 1].w = a1; }

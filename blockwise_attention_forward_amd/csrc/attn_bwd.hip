@@ -200,14 +200,19 @@ __device__ inline f32x16 mfma(const uint4& a, const uint4& b, const f32x16& c) {
                                                    0, 0);
 }
 
-// Element terms of the mask beyond the row interval: the dilated band's
-// residue, and equal document ids (row_id, key_id: the ids of the pair; the
-// callers read them without per-element memory loads).
-__device__ inline bool xvisible(const BwdLaunch& p, int row, int key, int row_id, int key_id) {
-    bool ok = true;
-    if (p.mask.dilation > 1) ok = ((unsigned)((i64)row - key - p.mask.kv_offset) % (unsigned)p.mask.dilation) == 0;
-    if (p.mask.seg_mode == 3) ok = ok && row_id == key_id;
-    return ok;
+// Dilated band, as a bit mask over 32 consecutive positions: bit o is set
+// when position base + o is congruent to res modulo g (pat holds the bits
+// 0, g, 2g, ... below 32; base >= 0).  One modulo per 32 positions instead
+// of one per element.
+__device__ inline unsigned dil_bits(int res, int base, int g, unsigned pat) {
+    const int m = ((res - base % g) % g + g) % g;
+    return m < 32 ? (pat << m) : 0u;
+}
+
+__device__ inline unsigned dil_pattern(int g) {
+    unsigned pat = 0u;
+    for (int o = 0; o < 32; o += g) pat |= 1u << o;
+    return pat;
 }
 
 // Document ids of keys j .. j+7 (j the same in every lane; clamped to the
@@ -364,7 +369,7 @@ __device__ inline void kv_load8(const BwdLaunch& p, KvStage8<D>& x, const QCurso
     const int nq = (int)min((i64)kTile, p.mask.q_valid - r0);
     stage_load<D, 512>(x.q, (const __bf16*)p.q + b * p.q_sB + r0 * p.q_sL + h * p.q_sH, p.q_sL, nq);
     stage_load<D, 512>(x.g, (const __bf16*)p.dout + b * p.do_sB + r0 * p.do_sL + h * p.do_sH, p.do_sL, nq);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const i64 row = r0 + lane;
     const i64 li = (b * p.H + h) * p.Lq + row;
     float v = 0.0f;
@@ -592,7 +597,7 @@ __device__ inline void kv_load(const BwdLaunch& p, KvStage<D>& x, const QCursor&
     const int nq = (int)min((i64)kTile, p.mask.q_valid - r0);
     stage_load<D>(x.q, (const __bf16*)p.q + b * p.q_sB + r0 * p.q_sL + h * p.q_sH, p.q_sL, nq);
     stage_load<D>(x.g, (const __bf16*)p.dout + b * p.do_sB + r0 * p.do_sL + h * p.do_sH, p.do_sL, nq);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const i64 row = r0 + lane;
     const i64 li = (b * p.H + h) * p.Lq + row;
     float v = 0.0f;
@@ -628,7 +633,8 @@ __device__ inline void kv_store(const BwdLaunch& p, const KvStage<D>& x, uint8_t
 template <int D>
 __device__ inline void kv_compute(const BwdLaunch& p, const uint8_t* qt, const uint8_t* gt, const float* st,
                                   const uint4 (&kf)[D / 16], const uint4 (&vf)[D / 16], f32x16 (&dk)[D / 32],
-                                  f32x16 (&dv)[D / 32], const QCursor& c, int kw0, int key_id) {
+                                  f32x16 (&dv)[D / 32], const QCursor& c, int kw0, int key_id, int key_res,
+                                  unsigned dpat) {
     using C = Cfg<D>;
     constexpr int NS = 2 * C::NDS, NM = 4 * C::NDB, NT = 2 * NS + 2 * NM;
     const int lane = threadIdx.x & 63, l32 = lane & 31, hb = lane >> 5;
@@ -646,7 +652,14 @@ __device__ inline void kv_compute(const BwdLaunch& p, const uint8_t* qt, const u
         const int k2 = j / (2 * C::NDB), w = (j / C::NDB) & 1, db = j % C::NDB;
         return frag_cols<D>(w ? qt : gt, rc * 2 + k2, db);
     };
-    // Rows rc*32 + 8g + 4hb + e of this lane: P and dS of slice g.
+    // Rows rc*32 + 8g + 4hb + e of this lane: P and dS of slice g.  With a
+    // dilated band the rows that see the key are those congruent to
+    // key + kv_offset modulo g: a bit per row of the 32-row chunk.
+    unsigned rbits[2] = {~0u, ~0u};
+    if (p.mask.dilation > 1) {
+#pragma unroll
+        for (int rc = 0; rc < 2; ++rc) rbits[rc] = dil_bits(key_res, c.m * kTile + rc * 32, p.mask.dilation, dpat);
+    }
     auto slice = [&](const int rc, const int g) __attribute__((always_inline)) {
         const int rb = rc * 32 + 8 * g + 4 * hb;
         const f32x4 L = *(const f32x4*)(st + rb);
@@ -658,8 +671,8 @@ __device__ inline void kv_compute(const BwdLaunch& p, const uint8_t* qt, const u
         float pv[4], dv4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            bool vis = lo[e] <= key && key < hi[e];
-            if (vis) vis = xvisible(p, c.m * kTile + rb + e, key, rid[e], key_id);
+            bool vis = lo[e] <= key && key < hi[e] && ((rbits[rc] >> (8 * g + 4 * hb + e)) & 1u);
+            if (p.mask.seg_mode == 3) vis = vis && rid[e] == key_id;
             const float x = pin(__builtin_amdgcn_exp2f(__builtin_fmaf(S[rc][4 * g + e], sc, -L[e] * kLog2e)));
             const float d = pin(x * (G[rc][4 * g + e] - Dl[e]));
             pv[e] = vis ? x : 0.0f;
@@ -730,6 +743,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
 #pragma unroll
     for (int d = 0; d < C::NDB; ++d) { dk[d] = f32x16{}; dv[d] = f32x16{}; }
     const int key_id = (p.mask.seg_mode == 3 && key < p.Lk) ? p.mask.ids_kv[b * p.mask.lk + key] : -1;
+    // (key + kv_offset) mod g: the rows congruent to it see the key
+    const int key_res = p.mask.dilation > 1
+                            ? (int)((((i64)key + p.mask.kv_offset) % p.mask.dilation + p.mask.dilation) % p.mask.dilation)
+                            : 0;
+    const unsigned dpat = p.mask.dilation > 1 ? dil_pattern(p.mask.dilation) : 0u;
     wait_loads();
 
     const int m0 = ld_const(p.kfirst, lb * p.nkb + kb), m1 = ld_const(p.klast, lb * p.nkb + kb);
@@ -756,7 +774,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
             staged = q_next(p, ahead, lb, m0, m1, k0, k0 + kKeyBlock);
             if (staged) kv_load<D>(p, stg, ahead, b, hk, lb);
         }
-        kv_compute<D>(p, qs[buf], gs[buf], ss[buf], kf, vf, dk, dv, cur, kw0, key_id);
+        kv_compute<D>(p, qs[buf], gs[buf], ss[buf], kf, vf, dk, dv, cur, kw0, key_id, key_res, dpat);
         have = q_next(p, cur, lb, m0, m1, k0, k0 + kKeyBlock);
         buf = nb;
     }
@@ -840,7 +858,7 @@ template <int D, bool XM>
 __device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const uint8_t* vt,
                                      const uint4 (&qf)[D / 16], const uint4 (&gf)[D / 16], f32x16 (&dq)[D / 32],
                                      int t, int full_lo, int full_hi, int lo, int hi, float lse2, float delt, i64 b,
-                                     int row, int row_id) {
+                                     int row, int row_id, int row_res, unsigned dpat) {
     using C = Cfg<D>;
     constexpr int NS = 2 * C::NDS, NH = 2 * C::NDB, NP = NS + NH;  // steps per half
     constexpr int AH = 2;                                            // read-ahead
@@ -870,6 +888,9 @@ __device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const ui
                 dq[m % C::NDB] = mfma(fa[i], pd[m / C::NDB], dq[m % C::NDB]);
             }
             if constexpr (i == NS - 1) {
+                // dilated band: the half's keys congruent to row - kv_offset mod g
+                unsigned kbits = ~0u;
+                if (XM && masked && p.mask.dilation > 1) kbits = dil_bits(row_res, j0 + kb * 32, p.mask.dilation, dpat);
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     float dsv[4];
@@ -882,7 +903,10 @@ __device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const ui
                         if (masked) {
                             const int key = j0 + kb * 32 + 8 * g + 4 * hb + e;
                             bool vis = lo <= key && key < hi;
-                            if (XM && vis) vis = xvisible(p, row, key, row_id, hb ? kid[4 + e] : kid[e]);
+                            if (XM) {
+                                vis = vis && ((kbits >> (8 * g + 4 * hb + e)) & 1u);
+                                if (p.mask.seg_mode == 3) vis = vis && row_id == (hb ? kid[4 + e] : kid[e]);
+                            }
                             d = vis ? d : 0.0f;
                         }
                         dsv[e] = d;
@@ -926,6 +950,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
         delt = p.delta[li];
     }
     const int row_id = (XM && p.mask.seg_mode == 3 && row_ok) ? p.mask.ids_q[b * p.mask.lq + row] : -1;
+    // (row - kv_offset) mod g: the keys congruent to it are seen
+    const int row_res = (XM && p.mask.dilation > 1)
+                            ? (int)((((i64)row - p.mask.kv_offset) % p.mask.dilation + p.mask.dilation) % p.mask.dilation)
+                            : 0;
+    const unsigned dpat = (XM && p.mask.dilation > 1) ? dil_pattern(p.mask.dilation) : 0u;
     // Q and dO rows of this lane as the B operand: d = ds*16 + hb*8 + 0..7.
     uint4 qf[C::NDS], gf[C::NDS];
     const __bf16* qp = (const __bf16*)p.q + b * p.q_sB + (i64)row * p.q_sL + h * p.q_sH;
@@ -986,7 +1015,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
             if (staged) q_load<D, NT>(p, stg, ahead.t, b, hk);
         }
         q_compute<D, XM>(p, ks[buf], vs[buf], qf, gf, dq, cur.t, full_lo, full_hi, lo, hi, lse2, delt, b, row,
-                         row_id);
+                         row_id, row_res, dpat);
         have = t_next(p, cur, t_lo, t_hi);
         buf = nb;
     }

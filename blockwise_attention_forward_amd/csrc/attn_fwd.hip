@@ -92,6 +92,22 @@ __device__ inline float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Scalar load (constant address space, uniform address): the value lands in a
+// scalar register and is waited for on the scalar/LDS counter, so reading a
+// run-list entry does not wait behind the tile copies in flight on the
+// vector-memory counter (which counts in order).
+template <class T>
+__device__ inline T ld_s(const T* p) {
+    return *((const __attribute__((address_space(4))) T*)p);
+}
+
+// Byte p through the scalar load of its aligned 4-byte word.
+__device__ inline int ld_s_u8(const uint8_t* p) {
+    const uintptr_t a = (uintptr_t)p;
+    const uint32_t w = ld_s((const uint32_t*)(a & ~(uintptr_t)3));
+    return (int)((w >> (8 * (a & 3))) & 0xffu);
+}
+
 // ---------------------------------------------------------------------------
 // Tile walk over runs [kb, ke) of one kind; every value is wave-uniform.
 // ---------------------------------------------------------------------------
@@ -103,9 +119,9 @@ struct Walk {
 
     __device__ inline void get(int r, int& kb, int& ke, int& kind) const {
         if (list) {
-            kb = uni(rb[r] * bkv);
-            ke = uni(min(re[r] * bkv, Lk));
-            kind = uni((int)rk[r]);
+            kb = ld_s(rb + r) * bkv;
+            ke = min(ld_s(re + r) * bkv, Lk);
+            kind = ld_s_u8(rk + r);
         } else if (r == 0) {
             kb = b0; ke = e0; kind = BWA_TILE_PARTIAL;
         } else if (r == 1) {

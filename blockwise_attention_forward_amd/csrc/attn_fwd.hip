@@ -628,6 +628,43 @@ __device__ inline void half_exp_slice(Half& x, int q, float scale_l2, float ms) 
     if (q & 1) { pb.z = a; pb.w = b; } else { pb.x = a; pb.y = b; }
 }
 
+// The same slice leaving the scores in x.s, for the speculative online order
+// below (the half may be redone against a new reference).
+__device__ inline void half_exp_slice_keep(Half& x, int q, float scale_l2, float ms) {
+    float e[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        e[r] = fast_exp2(__builtin_fmaf(x.s[4 * q + r], scale_l2, -ms));
+        x.rs += e[r];
+    }
+    const uint32_t a = pack_bf16x2(e[0], e[1]);
+    const uint32_t b = pack_bf16x2(e[2], e[3]);
+    uint4& pb = x.pb[q >> 1];
+    if (q & 1) { pb.z = a; pb.w = b; } else { pb.x = a; pb.y = b; }
+}
+
+// Whether some row's max in this half exceeds its reference by more than
+// 2^kLazy (base 2); mx: the lane's row max.  Nothing is changed.
+__device__ inline bool half_online_need(const Half& x, float m_run, float scale_l2, float& mx) {
+    const float a0 = fmaxf(fmaxf(x.s[0], x.s[1]), x.s[2]), a1 = fmaxf(fmaxf(x.s[3], x.s[4]), x.s[5]);
+    const float a2 = fmaxf(fmaxf(x.s[6], x.s[7]), x.s[8]), a3 = fmaxf(fmaxf(x.s[9], x.s[10]), x.s[11]);
+    const float a4 = fmaxf(fmaxf(x.s[12], x.s[13]), x.s[14]);
+    const float b0 = fmaxf(fmaxf(a0, a1), a2), b1 = fmaxf(fmaxf(a3, a4), x.s[15]);
+    mx = pair_max(fmaxf(b0, b1));
+    const bool need = mx * scale_l2 > (m_run == kNegInf ? kNegInf : m_run * scale_l2 + kLazy);
+    return __builtin_amdgcn_ballot_w64(need) != 0;
+}
+
+// The rare step: reference max(m_run, mx) for the lane's row; returns the
+// factor acc and l are scaled by.
+__device__ inline float online_move_ref(float& m_run, float mx, float scale_l2) {
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+    const float alpha = fast_exp2((m_run - m_use) * scale_l2);
+    m_run = m_new;
+    return alpha;
+}
+
 // Online reference update for one half: returns the factor acc and l must be
 // scaled by (1 when the reference stays), or sets rescale = false.
 __device__ inline float half_online_ref(const Half& x, float& m_run, float scale_l2, bool& rescale) {
@@ -649,7 +686,13 @@ __device__ inline float half_online_ref(const Half& x, float& m_run, float scale
     return alpha;
 }
 
-template <int D, int NW, int BODY, bool XM>
+// SPEC (online body only): a half's exponentials use the reference the rows
+// already have, while the check whether some row's max has moved past it by
+// more than 2^kLazy runs beside them; in the rare case it has, the half is
+// redone against the new reference.  The results are those of the plain
+// order (check first, then the exponentials), without the check on the
+// exponentials' critical path.
+template <int D, int NW, int BODY, bool XM, bool SPEC = false>
 __device__ inline void bf16_compute_tile(const uint8_t* kl, const uint8_t* vl, Bf16State<D, NW>& st, int j0,
                                          bool masked, const XMask& xm, const int* kidl) {
     using C = Bf16Cfg<D, NW>;
@@ -705,7 +748,8 @@ __device__ inline void bf16_compute_tile(const uint8_t* kl, const uint8_t* vl, B
     // step, which does not depend on it, so that its reduction runs under it.
     float ms = st.m_l2;  // fixed-m reference (scaled)
     bool resc = false;
-    float alpha = 1.0f;
+    float alpha = 1.0f, mx0 = 0.0f, mx1 = 0.0f;
+    if (SPEC) ms = (st.m_run == kNegInf ? 0.0f : st.m_run) * st.scale_l2;
     if (masked) {
         half_mask(h0, j0, 0, st.lo, st.hi);
         if (XM) xmask32_lds(h0.s, j0, 0, st.xres, st.xdoc, xm, kidl);
@@ -717,18 +761,32 @@ __device__ inline void bf16_compute_tile(const uint8_t* kl, const uint8_t* vl, B
         if (i + kPrefetch < 2 * NDS) kf[i + kPrefetch] = kfrag(i + kPrefetch);
         else vf[i + kPrefetch - 2 * NDS] = vfrag(i + kPrefetch - 2 * NDS);
         qk(h1, kf[i], ds);
-        if (BODY == BODY_ONLINE && ds == 0) {
-            alpha = half_online_ref(h0, st.m_run, st.scale_l2, resc);
-            ms = (st.m_run == kNegInf ? 0.0f : st.m_run) * st.scale_l2;
+        if constexpr (SPEC) {
+            if (ds < 4) half_exp_slice_keep(h0, ds, st.scale_l2, ms);
+            if (ds == (NDS > 4 ? 4 : NDS - 1)) resc = half_online_need(h0, st.m_run, st.scale_l2, mx0);
+        } else {
+            if (BODY == BODY_ONLINE && ds == 0) {
+                alpha = half_online_ref(h0, st.m_run, st.scale_l2, resc);
+                ms = (st.m_run == kNegInf ? 0.0f : st.m_run) * st.scale_l2;
+            }
+            if (BODY == BODY_ONLINE ? (ds >= 1 && ds <= 4) : ds < 4)
+                half_exp_slice(h0, BODY == BODY_ONLINE ? ds - 1 : ds, st.scale_l2, ms);
         }
-        if (BODY == BODY_ONLINE ? (ds >= 1 && ds <= 4) : ds < 4)
-            half_exp_slice(h0, BODY == BODY_ONLINE ? ds - 1 : ds, st.scale_l2, ms);
         __builtin_amdgcn_sched_barrier(0);
     }
-    // Slices the loop had no step for (online body, fewer than 5 steps).
+    if constexpr (!SPEC) {
+        // Slices the loop had no step for (online body, fewer than 5 steps).
 #pragma unroll
-    for (int q = (BODY == BODY_ONLINE ? NDS - 1 : 4); q < 4; ++q) half_exp_slice(h0, q, st.scale_l2, ms);
+        for (int q = (BODY == BODY_ONLINE ? NDS - 1 : 4); q < 4; ++q) half_exp_slice(h0, q, st.scale_l2, ms);
+    }
     if (BODY == BODY_ONLINE && resc) {  // rare: the row max moved by more than 2^kLazy
+        if constexpr (SPEC) {
+            alpha = online_move_ref(st.m_run, mx0, st.scale_l2);
+            ms = (st.m_run == kNegInf ? 0.0f : st.m_run) * st.scale_l2;
+            h0.rs = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) half_exp_slice_keep(h0, q, st.scale_l2, ms);
+        }
         st.l_run *= alpha;
 #pragma unroll
         for (int d = 0; d < NDB; ++d) st.acc[d] *= alpha;
@@ -745,17 +803,31 @@ __device__ inline void bf16_compute_tile(const uint8_t* kl, const uint8_t* vl, B
     for (int j = 0; j < 2 * NDB; ++j) {
         if (j + kPrefetch < 4 * NDB) vf[j + kPrefetch] = vfrag(j + kPrefetch);
         pv(vf[j], h0.pb[j / NDB], j % NDB);
-        if (BODY == BODY_ONLINE && j == 0) {
-            alpha1 = half_online_ref(h1, st.m_run, st.scale_l2, resc1);
-            ms = (st.m_run == kNegInf ? 0.0f : st.m_run) * st.scale_l2;
+        if constexpr (SPEC) {
+            if (j < 4) half_exp_slice_keep(h1, j, st.scale_l2, ms);
+            if (j == (2 * NDB > 4 ? 4 : 2 * NDB - 1)) resc1 = half_online_need(h1, st.m_run, st.scale_l2, mx1);
+        } else {
+            if (BODY == BODY_ONLINE && j == 0) {
+                alpha1 = half_online_ref(h1, st.m_run, st.scale_l2, resc1);
+                ms = (st.m_run == kNegInf ? 0.0f : st.m_run) * st.scale_l2;
+            }
+            if (BODY == BODY_ONLINE ? (j >= 1 && j <= 4) : j < 4)
+                half_exp_slice(h1, BODY == BODY_ONLINE ? j - 1 : j, st.scale_l2, ms);
         }
-        if (BODY == BODY_ONLINE ? (j >= 1 && j <= 4) : j < 4)
-            half_exp_slice(h1, BODY == BODY_ONLINE ? j - 1 : j, st.scale_l2, ms);
         __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (!SPEC) {
 #pragma unroll
-    for (int q = (BODY == BODY_ONLINE ? 2 * NDB - 1 : 4); q < 4; ++q) half_exp_slice(h1, q, st.scale_l2, ms);
+        for (int q = (BODY == BODY_ONLINE ? 2 * NDB - 1 : 4); q < 4; ++q) half_exp_slice(h1, q, st.scale_l2, ms);
+    }
     if (BODY == BODY_ONLINE && resc1) {
+        if constexpr (SPEC) {
+            alpha1 = online_move_ref(st.m_run, mx1, st.scale_l2);
+            ms = (st.m_run == kNegInf ? 0.0f : st.m_run) * st.scale_l2;
+            h1.rs = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) half_exp_slice_keep(h1, q, st.scale_l2, ms);
+        }
         st.l_run = (st.l_run + h0.rs) * alpha1;
         h0.rs = 0.0f;
 #pragma unroll
@@ -810,7 +882,7 @@ struct Ring {
     int* kid[C::NBUF];  // document ids of the keys (element-test kernels only)
 };
 
-template <int D, int NW, int BODY, bool XM, int I, class W>
+template <int D, int NW, int BODY, bool XM, int I, bool SPEC, class W>
 __device__ __attribute__((always_inline)) inline bool bf16_step(const AttnLaunch& p, Bf16State<D, NW>& st,
                                                                const W& walk, const Ring<D, NW>& ring,
                                                                Cursor<64>& cur, Cursor<64>& ahead, bool& more,
@@ -832,14 +904,14 @@ __device__ __attribute__((always_inline)) inline bool bf16_step(const AttnLaunch
         bf16_issue_tile<D, NW, XM>(p, kbase, vbase, ahead.j0, kv_lim, ring.k[J], ring.v[J], ring.kid[J], xm);
         ++n_after;
     }
-    bf16_compute_tile<D, NW, BODY, XM>(ring.k[I], ring.v[I], st, j0, masked, xm, ring.kid[I]);
+    bf16_compute_tile<D, NW, BODY, XM, SPEC>(ring.k[I], ring.v[I], st, j0, masked, xm, ring.kid[I]);
     const bool have = cur.next(walk);
     if (have) --n_after;
     return have;
 }
 
 // Every tile of the walk, accumulated into st; the caller stores the result.
-template <int D, int NW, int BODY, bool XM, class W>
+template <int D, int NW, int BODY, bool XM, bool SPEC = false, class W>
 __device__ inline void bf16_walk(const AttnLaunch& p, Bf16State<D, NW>& st, const W& walk,
                                  const Ring<D, NW>& ring, i64 b, i64 h) {
     using C = Bf16Cfg<D, NW>;
@@ -867,23 +939,23 @@ __device__ inline void bf16_walk(const AttnLaunch& p, Bf16State<D, NW>& st, cons
         }
     }
     while (have) {
-        have = bf16_step<D, NW, BODY, XM, 0>(p, st, walk, ring, cur, ahead, more, n_after, kbase, vbase, kv_lim,
+        have = bf16_step<D, NW, BODY, XM, 0, SPEC>(p, st, walk, ring, cur, ahead, more, n_after, kbase, vbase, kv_lim,
                                              xm);
         if (!have) break;
-        have = bf16_step<D, NW, BODY, XM, 1>(p, st, walk, ring, cur, ahead, more, n_after, kbase, vbase, kv_lim,
+        have = bf16_step<D, NW, BODY, XM, 1, SPEC>(p, st, walk, ring, cur, ahead, more, n_after, kbase, vbase, kv_lim,
                                              xm);
         if (NB == 3) {
             if (!have) break;
-            have = bf16_step<D, NW, BODY, XM, NB - 1>(p, st, walk, ring, cur, ahead, more, n_after, kbase, vbase,
+            have = bf16_step<D, NW, BODY, XM, NB - 1, SPEC>(p, st, walk, ring, cur, ahead, more, n_after, kbase, vbase,
                                                       kv_lim, xm);
         }
     }
 }
 
-template <int D, int NW, int BODY, int OUT, bool XM>
+template <int D, int NW, int BODY, int OUT, bool XM, bool SPEC = false>
 __device__ inline void bf16_run(const AttnLaunch& p, Bf16State<D, NW>& st, const Walk& walk,
                                 const Ring<D, NW>& ring, i64 b, i64 h, i64 row) {
-    bf16_walk<D, NW, BODY, XM>(p, st, walk, ring, b, h);
+    bf16_walk<D, NW, BODY, XM, SPEC>(p, st, walk, ring, b, h);
     store_out<D, OUT, BODY>(p, st.acc, st.m_run, st.l_run, st.m_fixed, b, h, row);
 }
 
@@ -960,7 +1032,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_bf16(const 
         if (fixed) bf16_run<D, NW, BODY_FIXED, OUT, XM>(p, st, walk, ring, b, h, row);
         else bf16_run<D, NW, BODY_ONLINE, OUT, XM>(p, st, walk, ring, b, h, row);
     } else {
-        bf16_run<D, NW, MODE, OUT, XM>(p, st, walk, ring, b, h, row);
+        bf16_run<D, NW, MODE, OUT, XM, MODE == BODY_ONLINE && !XM>(p, st, walk, ring, b, h, row);
     }
 }
 
@@ -1048,7 +1120,8 @@ __device__ inline void bal_item(const AttnLaunch& p, const Ring<D, NW>& ring, in
         const i64 n = walk_tiles(walk, C::TILE);
         const int s = piece < 0 ? 1 : p.split_s;
         const int c = piece < 0 ? 0 : piece;
-        bf16_walk<D, NW, BODY, false>(p, st, clip_walk<C::TILE>(walk, c * n / s, (c + 1) * n / s), ring, b, h);
+        bf16_walk<D, NW, BODY, false, MODE == BODY_ONLINE>(p, st, clip_walk<C::TILE>(walk, c * n / s, (c + 1) * n / s),
+                                                           ring, b, h);
         if (piece < 0) {
             store_out<D, OUT, BODY>(p, st.acc, st.m_run, st.l_run, st.m_fixed, b, h, row);
         } else {

@@ -281,6 +281,31 @@ def test_fixed_m_attention_and_gated_pair(D):
         assert torch.equal(o3, o2) and torch.equal(l3, l2)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", [{}, {"causal": True}])
+def test_online_reference_moves_mid_walk(D, mask):
+    """Online softmax with rows whose max jumps far past their running
+    reference (by much more than the lazy margin) after earlier tiles have
+    been accumulated, in the middle and in the ragged last tile of the key
+    walk: the rare rescale, and the redo of a half's exponentials in the
+    online-only launches, against the oracle (plain and balanced launches)."""
+    B, H, L = 1, 3, 700
+    dtype = torch.bfloat16
+    q = _rand((B, L, H, D), 90, dtype)
+    k = _rand((B, L, H, D), 91, dtype)
+    v = _rand((B, L, H, D), 92, dtype)
+    k[0, 300, 0] *= 30
+    k[0, 333, 1] *= 12
+    k[0, 20, 2] *= 8
+    k[0, 690, 2] *= 60
+    scale = 1 / math.sqrt(D)
+    o_ref, l_ref = oracle_attention(q, k, v, mask, scale)
+    o1, l1 = bw.bwa_attn_fwd(q, k, v, mask, scale=scale, mode=bw.BWA_MODE_ONLINE)
+    assert_close(o1, l1, o_ref, l_ref, dtype, f"plain {mask}")
+    o2, l2 = bw.bwa_attn_fwd_balanced(q, k, v, mask, scale=scale, mode=bw.BWA_MODE_ONLINE, n_cus=4)
+    assert_close(o2, l2, o_ref, l_ref, dtype, f"balanced {mask}")
+
+
 @pytest.mark.parametrize("n_parts", [1, 2, 3])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_lse_merge_against_oracle(n_parts, out_dtype):

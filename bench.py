@@ -92,9 +92,9 @@ class Timer:
         self.pairs = {}
 
 
-def _source_sha():
-    """Hash of the attention kernel source without comments and blank lines."""
-    p = os.path.join(ROOT, "blockwise_attention_forward_amd", "csrc", "attn_fwd.hip")
+def _source_sha(fname="attn_fwd.hip"):
+    """Hash of a kernel source file without comments and blank lines."""
+    p = os.path.join(ROOT, "blockwise_attention_forward_amd", "csrc", fname)
     code = []
     for line in open(p, encoding="utf-8"):
         line = line.split("//", 1)[0].rstrip()
@@ -103,8 +103,8 @@ def _source_sha():
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
-def _traffic(kernel_key):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+def _traffic(kernel_key, fname="attn_fwd.hip"):
+    """HBM bytes per launch (or per call) from committed rocprofv3 counter runs, if still current."""
     p = os.path.join(ROOT, "profiles", "attn_traffic.json")
     if not os.path.exists(p):
         return None
@@ -113,7 +113,7 @@ def _traffic(kernel_key):
     except ValueError:
         return None
     rec = d.get(kernel_key)
-    if not rec or rec.get("source_sha") != _source_sha():
+    if not rec or rec.get("source_sha") != _source_sha(fname):
         return None
     return rec.get("bytes_per_launch")
 
@@ -576,7 +576,9 @@ def run_single(args, torch, bw, synth):
         ("ms_backward" if bwd else "ms_attention"): round(ms_hop, 4),
         "counted_TFLOP": round(W["flops_step"] / 1e12, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic("attn_bwd_window", "attn_bwd.hip") if bwd and args.workload == "window"
+                     else None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

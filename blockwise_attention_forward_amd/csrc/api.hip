@@ -55,6 +55,20 @@ int32_t check_tensor(const bwa_tensor* t, const char* name) {
     if ((t->sB * es) % 16 || (t->sL * es) % 16 || (t->sH * es) % 16)
         return fail(BWA_ERR_BAD_STRIDE, "%s: strides must be multiples of 16 bytes", name);
     if (t->sB < 0 || t->sL < 0 || t->sH < 0) return fail(BWA_ERR_BAD_STRIDE, "%s: negative stride", name);
+    // No two (b, l, h) rows may share an element: broadcast views (a zero
+    // stride) and strides that interleave rows are rejected.  Sufficient
+    // test: taken by increasing stride, each dimension of extent > 1 steps
+    // past everything the dimensions inside it span.
+    struct Dim { i64 n, s; } dims[3] = {{t->B, t->sB}, {t->L, t->sL}, {t->H, t->sH}};
+    std::sort(dims, dims + 3, [](const Dim& a, const Dim& b) { return a.s < b.s; });
+    i64 span = t->D;  // elements one row covers
+    for (const Dim& d : dims) {
+        if (d.n <= 1) continue;
+        if (d.s < span)
+            return fail(BWA_ERR_BAD_STRIDE, "%s: overlapping layout (stride %lld over an extent of %lld elements)",
+                        name, (long long)d.s, (long long)span);
+        span = d.s * (d.n - 1) + span;
+    }
     return BWA_OK;
 }
 

@@ -30,8 +30,9 @@
 // description):
 //   online : running row max m, p = exp(s*scale - m*scale), l and O rescaled
 //            by exp((m_old - m_new)*scale) when the max moves;
-//   fixed-m: p = exp(s*scale - m_i) with the caller's per-row bound m_i; no
-//            max, no rescale.
+//   fixed-m: p = 2^32 exp(s*scale - m_i) with the caller's per-row bound
+//            m_i; no max, no rescale (the constant factor cancels in O and
+//            is taken out of LSE).
 // Each body is its own loop (a fixed-m launch compiles a single branch-free
 // body; that page's Notes measured a 3x loss when two bodies share the hot
 // loop).  The gated mode picks one of the two loops per workgroup from the
@@ -54,6 +55,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Fixed-m reference: p = 2^(kFixedShift) * exp(s - m_i), i.e. the exponent is
+// taken against m_i less kFixedShift*ln 2.  With |s| <= m_i the exponents of
+// a row lie in [kFixedShift - 2 m_i log2 e, kFixedShift]: the shift moves the
+// worst row (every key anti-aligned, s = -m_i) away from the bottom of the
+// fp32/bf16 normal range while p stays at most 2^32, so l and O keep more
+// than 2^90 of headroom.  The bound's gate admits a head only when
+// 2 m_i log2 e <= 116, so the largest p of every row is at least 2^-84 and
+// 2^30 keys flushed below 2^-126 carry at most 2^-12 of its weight.
+constexpr float kFixedShift = 32.0f;
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
 
@@ -434,7 +445,7 @@ __device__ inline void store_rows(const AttnLaunch& p, f32x16 (&acc)[D / 32], fl
     const float l = pair_sum(l_run);
     if (!row_ok) return;
     const bool any = l > 0.0f;
-    float lse = any ? (BODY == BODY_FIXED ? m_fixed : m_run * p.scale) + __logf(l) : kNegInf;
+    float lse = any ? (BODY == BODY_FIXED ? m_fixed - kFixedShift * kLn2 : m_run * p.scale) + __logf(l) : kNegInf;
     const float w_own = any ? 1.0f / l : 0.0f;  // normalizes this call's partial
     float w_cur = 1.0f, w_prev = 0.0f;
     if (prev_o) {
@@ -567,7 +578,10 @@ __device__ inline void bf16_issue_tile(const AttnLaunch& p, const __bf16* kbase,
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ir, (lds_void*)kidl, 4, (unsigned)(lane * 4), 0, 0, 0);
     }
     const int nvalid = uni(min(max(kv_lim - j0, 0), C::TILE));
-    const int kbytes = uni((int)(nvalid * p.k_sL * 2)), vbytes = uni((int)(nvalid * p.v_sL * 2));
+    // The range ends with the last valid row's D elements: reads of later
+    // rows fall outside it and return zero.
+    const int kbytes = uni(nvalid > 0 ? (int)(((nvalid - 1) * p.k_sL + D) * 2) : 0);
+    const int vbytes = uni(nvalid > 0 ? (int)(((nvalid - 1) * p.v_sL + D) * 2) : 0);
     const __amdgpu_buffer_rsrc_t kr =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (i64)j0 * p.k_sL), 0, kbytes, kRsrcFlags);
     const __amdgpu_buffer_rsrc_t vr =
@@ -1017,7 +1031,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_bf16(const 
     st.m_l2 = 0.0f;
     if (fixed && row_ok) {
         st.m_fixed = p.m[bh * p.Lq + row];
-        st.m_l2 = st.m_fixed * kLog2e;
+        st.m_l2 = st.m_fixed * kLog2e - kFixedShift;
     }
     st.scale_l2 = p.scale * kLog2e;
     st.xres = 0;
@@ -1108,7 +1122,7 @@ __device__ inline void bal_item(const AttnLaunch& p, const Ring<D, NW>& ring, in
     st.m_l2 = 0.0f;
     if (fixed && row_ok) {
         st.m_fixed = p.m[bh * p.Lq + row];
-        st.m_l2 = st.m_fixed * kLog2e;
+        st.m_l2 = st.m_fixed * kLog2e - kFixedShift;
     }
     st.scale_l2 = p.scale * kLog2e;
     const bool ne = row_ok && lo < hi;
@@ -1265,7 +1279,7 @@ __device__ inline void f32_run(const AttnLaunch& p, const Walk& walk, float* ks,
                                int lo, int hi, float m_fixed, i64 b, i64 h, i64 row) {
     constexpr int TILE = 32, NDB = D / 32, LD = D + 1;
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hb = lane >> 5;
-    const float scale_l2 = p.scale * kLog2e, m_l2 = m_fixed * kLog2e;
+    const float scale_l2 = p.scale * kLog2e, m_l2 = m_fixed * kLog2e - kFixedShift;
     f32x16 acc[NDB];
 #pragma unroll
     for (int d = 0; d < NDB; ++d) acc[d] = f32x16{};

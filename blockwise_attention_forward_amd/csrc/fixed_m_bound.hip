@@ -6,7 +6,14 @@
 // taken over every K shard (Notes: global over all shards, so a head's m is
 // the same on every hop; Tests: a caller's per-shard max||k|| is promoted to
 // the global bound).  A head passes the gate iff max_i m_i <= tau (Notes:
-// the two-sided halved bound 106.5).
+// the two-sided halved bound 106.5) and the bound is one that the fixed-m
+// body can prove safe in its own arithmetic (description: heads whose bound
+// cannot be proven safe keep online softmax).  That body takes exponents
+// against m_i less 32 ln 2, so with |s| <= m_i a row's exponents lie in
+// [32 - 2 m_i log2 e, 32] (base 2).  Keeping the row's largest term at or
+// above 2^-84 (its keys flushed below the fp32/bf16 normal range 2^-126 then
+// weigh at most 2^30 * 2^-126 / 2^-84 = 2^-12 of it, for any row of up to
+// 2^30 keys) needs 2 m_i log2 e <= 116, i.e. m_i <= 58 ln 2 = 40.2.
 //
 // The work is one streaming pass over Q and every K chunk (HBM-bound, no
 // reuse): each row's 2-norm is an fp32 sum of squares (bf16 products are
@@ -24,6 +31,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+constexpr float kFixedSafeMax = 40.2025375f;  // 58 ln 2: the largest bound the fixed-m body proves safe
 constexpr int kRowsPerTask = 1024;  // rows of the flattened [B, L, H] order per workgroup
 constexpr int kMaxHeadsLds = 256;   // per-head maxima kept in LDS up to this many heads
 
@@ -159,7 +167,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(const BoundLaunch a) {
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         const float mm = (a.scale * a.mmax_out[bh]) * kmax;
         a.mmax_out[bh] = mm;
-        a.gate_out[bh] = (mm <= a.tau) ? 1 : 0;
+        a.gate_out[bh] = (mm <= a.tau && mm <= kFixedSafeMax) ? 1 : 0;
     }
 }
 

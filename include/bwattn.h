@@ -23,8 +23,12 @@
  * Conventions shared by every entry point
  *  - Tensors are token-major [B, L, H, D] with the last dimension contiguous;
  *    strides are in elements.  Base pointers and the B/L/H strides must be
- *    multiples of 16 bytes.  Per-row statistics (lse, m) are dense
- *    fp32 [B, H, L].
+ *    multiples of 16 bytes, and no two (b, l, h) rows may share an element:
+ *    taken by increasing stride, each dimension of extent > 1 must step past
+ *    everything the dimensions inside it span (so broadcast views with a zero
+ *    stride, and L or H strides under D, return BWA_ERR_BAD_STRIDE; any
+ *    permutation of B, L, H and padded row pitches are fine).  Per-row
+ *    statistics (lse, m) are dense fp32 [B, H, L].
  *  - Every pointer inside a tensor or mask, and every output pointer, is a
  *    device pointer unless the argument says "host".  The caller allocates
  *    and owns every buffer; the library allocates no device memory and keeps
@@ -214,7 +218,16 @@ int32_t bwa_block_mask_build(const bwa_mask* mask, int64_t B, int64_t lq, int64_
  *                e.g. other ring ranks', promoted to the global bound);
  *   m[b,h,i]   = scale * ||q[b,i,h,:]||_2 * kmax[b,h]   (natural-log units);
  *   mmax[b,h]  = max over i < q_valid of m[b,h,i]   (0 when q_valid == 0);
- *   gate[b,h]  = 1 if mmax[b,h] <= tau else 0   (a tie passes).
+ *   gate[b,h]  = 1 if mmax[b,h] <= tau and mmax[b,h] <= 58 ln 2 (= 40.2025)
+ *                else 0   (a tie passes; compared in fp32).
+ * The second term is the largest bound for which the fixed-m body of
+ * bwa_attn_fwd is provably accurate in its own arithmetic (heads whose bound
+ * cannot be proven safe keep online softmax [FIXEDM description]): with
+ * |s_ij| <= m_i, a row's terms 2^32 exp(s - m_i) all lie in
+ * [2^(32 - 2 m_i log2 e), 2^32]; at 2 m_i log2 e <= 116 the largest is at least
+ * 2^-84, so up to 2^30 keys flushed under the fp32/bf16 normal range 2^-126
+ * carry at most 2^-12 of its weight.  A tau above 40.2 (the page's 106.5)
+ * therefore still sends heads with 40.2 < mmax <= tau to the online loop.
  * q: [B, Lq, H, D]; k_chunks: host array of n_chunks tensors [B, Lk_c, H, D]
  * with q's dtype, B, H and D; kv_valid: host array [n_chunks] (NULL = all
  * keys valid; entries < 0 mean Lk_c); kmax_in: device [n_kmax_in][B][H]
@@ -233,11 +246,14 @@ int32_t bwa_fixed_m_bound(const bwa_tensor* q, const bwa_tensor* k_chunks, int32
  *   LSE[b,h,i] = ln sum_j exp(scale * q_i . k_j)  (natural log),
  * computed tile by tile over the listed key blocks with
  *   BWA_MODE_ONLINE : a running row max and rescale of the partial sums,
- *   BWA_MODE_FIXED_M: p_ij = exp(scale * q_i . k_j - m[b,h,i]) with the
+ *   BWA_MODE_FIXED_M: p_ij = 2^32 exp(scale * q_i . k_j - m[b,h,i]) with the
  *                     caller's per-row bound m (from bwa_fixed_m_bound); no
- *                     max and no rescale [FIXEDM description].  The result
+ *                     max and no rescale [FIXEDM description]; the factor
+ *                     2^32 cancels in O and is taken out of LSE.  The result
  *                     is exact in real arithmetic whenever m bounds the row's
- *                     scores; m is trusted, not checked.
+ *                     scores, and accurate in this arithmetic whenever in
+ *                     addition m_i <= 58 ln 2 (the gate of
+ *                     bwa_fixed_m_bound); m is trusted, not checked.
  * q: [B, Lq, H, D]; k, v: [B, Lk, H, D]; q, k, v share a dtype (BWA_BF16
  * computes Q K^T and P V on bf16 matrix cores with fp32 accumulation and
  * rounds P to bf16; BWA_F32 computes in fp32 throughout).  D is 64 or 128.

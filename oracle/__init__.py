@@ -37,6 +37,7 @@ from .attention import (  # noqa: F401
     row_intervals,
     attention,
     attention_rows,
+    fixed_m_safe_max,
     softmax_probs,
     lse_merge,
     fixed_m_bound,

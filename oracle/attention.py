@@ -259,6 +259,25 @@ def lse_merge(parts):
     return o, lse
 
 
+def fixed_m_safe_max():
+    """Largest per-row bound whose fixed-m softmax is provably safe in the
+    library's arithmetic (reading of "Fixed-m softmax for 2D-ring x Ulysses
+    attention (WAN 2.2)", description: heads whose bound cannot be proven safe
+    keep online softmax).
+
+    The fixed-m body forms ``p = 2**32 * exp(s - m_i)`` in fp32 and rounds it
+    to bf16 for the value product.  With ``|s| <= m_i`` the largest ``p`` of a
+    row is at least ``2**(32 - 2 m_i log2 e)``.  Terms under the fp32/bf16
+    normal range may be flushed; for a row of up to ``2**30`` keys their weight
+    stays under ``2**-12`` of the row's largest term when that term is at least
+    ``2**30 * tiny / 2**-12``.  Solving for ``m_i`` gives ``58 ln 2``.
+    """
+    tiny_exp = int(np.log2(np.finfo(np.float32).tiny))  # -126
+    shift, max_keys_exp, weight_exp = 32, 30, -12
+    floor_exp = max_keys_exp + tiny_exp - weight_exp     # the largest term's lowest exponent
+    return (shift - floor_exp) / (2.0 * np.log2(np.e))
+
+
 def fixed_m_bound(q, k_chunks, scale, tau, q_valid=None, kv_valid=None,
                   kmax_in=None):
     """Per-query Cauchy-Schwarz bound and per-head gate for one (batch, head).
@@ -272,9 +291,11 @@ def fixed_m_bound(q, k_chunks, scale, tau, q_valid=None, kv_valid=None,
       (the per-shard value is promoted to the global bound).
     * ``m_i = scale * ||q_i||_2 * kmax`` bounds every score of row ``i``.
     * The head passes the gate iff ``max_{i < q_valid} m_i <= tau`` (a tie
-      passes).  The decision is taken in fp32, the precision the bound is
-      produced in: the fp64 maximum is rounded to fp32 and compared with
-      ``float32(tau)``.
+      passes) and ``max m_i <= fixed_m_safe_max()`` (the bound must also be
+      one the fixed-m arithmetic can prove safe).  The decision is taken in
+      fp32, the precision the bound is produced in: the fp64 maximum is
+      rounded to fp32 and compared with ``float32(tau)`` and
+      ``float32(fixed_m_safe_max())``.
 
     Padded keys (``j >= kv_valid`` of their chunk) do not enter ``kmax``.
     Returns ``(kmax, m[Lq], mmax, gate)`` with fp64 values and a bool gate.
@@ -292,7 +313,7 @@ def fixed_m_bound(q, k_chunks, scale, tau, q_valid=None, kv_valid=None,
         kmax = max(kmax, float(np.max(_as64(kmax_in))))
     m = scale * np.sqrt((q ** 2).sum(axis=1)) * kmax
     mmax = float(m[:q_valid].max()) if q_valid > 0 else 0.0
-    gate = bool(np.float32(mmax) <= np.float32(tau))
+    gate = bool(np.float32(mmax) <= np.float32(tau) and np.float32(mmax) <= np.float32(fixed_m_safe_max()))
     return kmax, m, mmax, gate
 
 

@@ -121,6 +121,11 @@ def _attn(q, k, v, o, mask=None, mode=0, m=None, lse=0x20000):
     (dict(v=dict(L=100)), 2),
     (dict(k=dict(H=3), v=dict(H=3)), 2),       # 3 key heads do not divide 2 query heads
     (dict(k=dict(H=1), v=dict(H=2)), 2),       # k and v heads differ
+    (dict(k=dict(sL=0)), 3),                   # keys broadcast along L (an expanded view)
+    (dict(v=dict(sL=64)), 3),                  # rows overlap (L stride under D)
+    (dict(q=dict(sH=64)), 3),                  # heads overlap
+    (dict(o=dict(sH=0)), 3),                   # output heads aliased
+    (dict(k=dict(B=2, sB=1024), v=dict(B=2), q=dict(B=2), o=dict(B=2)), 3),  # batch elements overlap
 ])
 def test_attn_fwd_argument_errors(case, code):
     args = {n: _t(**case.get(n, {})) for n in ("q", "k", "v", "o")}
@@ -149,6 +154,18 @@ def test_mask_errors(mask, code):
     assert _attn(q, _t(), _t(), _t(), mask=_mask(**mask)) == code
 
 
+def test_non_overlapping_layouts_pass_the_stride_check():
+    # head-major [B, H, L, D] views, a padded row pitch and a single row per
+    # head with a zero stride are valid layouts: each call gets past the
+    # tensor checks and stops at the bad mask (nothing is launched)
+    hm = dict(sL=128, sH=256 * 128)
+    bad = _mask(causal=2)
+    assert _attn(_t(**hm), _t(**hm), _t(**hm), _t(**hm), mask=bad) == 5
+    assert _attn(_t(sL=2 * 128 + 64, sB=256 * 320), _t(), _t(), _t(), mask=bad) == 5
+    one = dict(L=1, sL=0)
+    assert _attn(_t(**one), _t(**one), _t(**one), _t(**one), mask=bad) == 5
+
+
 def _carry(q, k, v, o, o_prev, lse_prev=0x30000, lse=0x20000):
     return L.bwa_attn_fwd_carry(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(_mask()), None,
                                 0.1, 0, None, None, ctypes.byref(o_prev) if o_prev is not None else None,
@@ -161,7 +178,7 @@ def _carry(q, k, v, o, o_prev, lse_prev=0x30000, lse=0x20000):
     (dict(dtype=0, L=255), {}, 0x30000, 2),          # not q's shape
     (dict(dtype=0), {}, None, 1),                    # lse_prev missing
     (dict(dtype=0, ptr=0x50000), dict(ptr=0x50000), 0x30000, 3),   # alias with a bf16 output
-    (dict(dtype=0, ptr=0x50000, sH=256), dict(ptr=0x50000, dtype=0), 0x30000, 3),  # alias, other strides
+    (dict(dtype=0, ptr=0x50000, sL=128, sH=256 * 128), dict(ptr=0x50000, dtype=0), 0x30000, 3),  # alias, other strides
 ])
 def test_attn_fwd_carry_argument_errors(o_prev, o, lse_prev, code):
     op = _t(**o_prev) if o_prev is not None else None

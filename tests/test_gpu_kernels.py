@@ -138,6 +138,36 @@ def test_segment_ids_per_batch_and_strided_views():
     assert torch.equal(o, o2) and torch.equal(l, l2)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_head_major_and_padded_layouts(dtype):
+    # K/V rows whose L stride is exactly D (head-major views of [B, H, L, D])
+    # or wider than a token (padded pitch) read every valid row, and rows past
+    # kv_valid as nothing; the same results as contiguous token-major copies.
+    B, H, Lq, Lk, D = 1, 2, 300, 333, 128
+    q = _rand((B, H, Lq, D), 11, dtype).transpose(1, 2)
+    k = _rand((B, H, Lk, D), 12, dtype).transpose(1, 2)
+    vp = _rand((B, Lk, H, D + 64), 13, dtype)[..., :D]  # row pitch H * (D + 64)
+    mask = {"causal": True, "kv_offset": Lq - Lk, "kv_valid": 301}
+    o_ref, l_ref = oracle_attention(q, k, vp, mask, 0.1)
+    o, l = bw.bwa_attn_fwd(q, k, vp, mask, scale=0.1)
+    assert_close(o, l, o_ref, l_ref, dtype, "head-major / padded")
+    o2, l2 = bw.bwa_attn_fwd(q.contiguous(), k.contiguous(), vp.contiguous(), mask, scale=0.1)
+    assert torch.equal(o, o2) and torch.equal(l, l2)
+
+
+def test_overlapping_layouts_are_rejected():
+    q = _rand((1, 200, 2, 128), 1, torch.bfloat16)
+    k1 = _rand((1, 1, 2, 128), 2, torch.bfloat16)
+    kx = k1.expand(1, 200, 2, 128)  # one key broadcast along L: stride 0
+    with pytest.raises(bw.BwaError) as e:
+        bw.bwa_attn_fwd(q, kx, kx, {})
+    assert e.value.status == 3
+    with pytest.raises(bw.BwaError):
+        bw.bwa_attn_fwd(q, k1.expand(1, 200, 2, 128).contiguous(), kx, {})
+    with pytest.raises(bw.BwaError):
+        bw.bwa_fixed_m_bound(q, [kx], 0.1, 106.5)
+
+
 @pytest.mark.parametrize("mi", range(len(MASKS)))
 @pytest.mark.parametrize("bq,bkv", [(128, 128), (128, 64), (64, 192)])
 def test_block_lists_bit_exact(mi, bq, bkv):
@@ -279,6 +309,48 @@ def test_fixed_m_attention_and_gated_pair(D):
         o3, l3 = bw.bwa_attn_fwd(q, k, v, mask, scale=scale, mode=bw.BWA_MODE_GATED, m=m, gate=gate,
                                  out_dtype=torch.float32)
         assert torch.equal(o3, o2) and torch.equal(l3, l2)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_fixed_m_rows_far_below_their_bound(dtype):
+    # Rows whose every key points away from the query with the largest norm:
+    # all scores sit near -m_i, about 2 m_i below the bound.  Head 0's bound
+    # is just under the largest one the fixed-m arithmetic proves safe, so it
+    # passes the gate and its rows sit ~72 below m_i; head 1's bound (~100)
+    # is under the page's 106.5 but out of that range, so it fails the gate
+    # and takes the online loop.  Both must match the oracle, in fixed-m,
+    # gated and balanced launches.
+    B, H, Lq, Lk, D = 1, 2, 300, 700, 128
+    scale = 1 / math.sqrt(D)
+    g = torch.Generator(device="cpu").manual_seed(60)
+    qdir = torch.randn(H, D, generator=g, dtype=torch.float64)
+    qdir /= qdir.norm(dim=1, keepdim=True)
+    a = torch.rand(Lk, H, generator=g, dtype=torch.float64) * 0.1 + 0.9
+    a[0] = 1.0
+    k = (-a[:, :, None] * qdir[None]).unsqueeze(0)
+    m_target = torch.tensor([0.99 * oracle.fixed_m_safe_max(), 100.0], dtype=torch.float64)
+    qn = (m_target / scale) * (0.95 + 0.05 * torch.rand(Lq, H, generator=g, dtype=torch.float64))
+    q = (qn[:, :, None] * qdir[None]).unsqueeze(0)
+    q, k = q.to(DEV, dtype), k.to(DEV, dtype)
+    v = _rand((B, Lk, H, D), 61, dtype)
+    kmax, mmax, m, gate = bw.bwa_fixed_m_bound(q, [k], scale, 106.5)
+    assert gate[0].tolist() == [1, 0] and mmax[0, 1].item() < 106.5
+    for h in range(H):
+        assert oracle.fixed_m_bound(np64(q[0, :, h]), [np64(k[0, :, h])], scale, 106.5)[3] == (h == 0)
+    o_ref, l_ref = oracle_attention(q, k, v, {}, scale)
+    s_max = (np64(q[0, :, 0]) @ np64(k[0, :, 0]).T).max(axis=1) * scale
+    assert np.all(np64(m[0, 0]) - s_max > 70.0)
+    o, l = bw.bwa_attn_fwd(q, k, v, {}, scale=scale, mode=bw.BWA_MODE_FIXED_M, m=m, gate=gate,
+                           out_dtype=torch.float32)
+    assert_close(o[:, :, :1], l[:, :1], o_ref[:, :, :1], l_ref[:, :1], dtype, "fixed-m, rows far below m")
+    o2, l2 = bw.bwa_attn_fwd(q, k, v, {}, scale=scale, mode=bw.BWA_MODE_GATED, m=m, gate=gate,
+                             out_dtype=torch.float32)
+    assert_close(o2, l2, o_ref, l_ref, dtype, "gated")
+    assert torch.equal(o2[:, :, :1], o[:, :, :1]) and torch.equal(l2[:, :1], l[:, :1])
+    if dtype == torch.bfloat16:
+        o3, l3 = bw.bwa_attn_fwd_balanced(q, k, v, {}, scale=scale, mode=bw.BWA_MODE_GATED, m=m, gate=gate,
+                                          n_cus=16, out_dtype=torch.float32)
+        assert_close(o3, l3, o_ref, l_ref, dtype, "gated, balanced")
 
 
 @pytest.mark.parametrize("D", [64, 128])

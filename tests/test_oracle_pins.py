@@ -126,6 +126,32 @@ def test_triple_loop_agrees(mask):
     np.testing.assert_allclose(lse[f], lse_ref[f], rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("chunk", [64, 7, 1])
+def test_attention_rows_over_many_chunks(chunk):
+    # attention_rows is what every sampled parity check and the CPU baseline
+    # run: ~300 unordered rows (repeats, invalid rows, segment edges) must give
+    # the rows of the whole call, however they are chunked.
+    Lq, Lk, D = 320, 257, 16
+    q, k, v = _qkv(Lq, Lk, D, seed=41)
+    v = v[:, :11]
+    mask = {"cu_seqlens_q": [0, 130, 300, 320], "cu_seqlens_kv": [0, 120, 250, 257], "causal": True,
+            "kv_offset": -9, "q_valid": 310}
+    rng = np.random.Generator(np.random.PCG64(42))
+    rows = np.concatenate([rng.permutation(Lq)[:250], [0, 129, 130, 299, 300, 309, 310, 319, 5, 5]])
+    rng.shuffle(rows)
+    o_all, lse_all = oracle.attention(q, k, v, mask, 0.3)
+    o, lse = oracle.attention_rows(q, k, v, mask, 0.3, rows, chunk=chunk)
+    assert o.shape == (rows.size, 11) and lse.shape == (rows.size,)
+    np.testing.assert_allclose(o, o_all[rows], rtol=1e-12, atol=1e-13)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(lse_all[rows]))
+    f = np.isfinite(lse_all[rows])
+    np.testing.assert_allclose(lse[f], lse_all[rows][f], rtol=1e-12, atol=1e-13)
+    # and against the triple loop on a slice of the rows
+    sub = rows[:70]
+    o_py, lse_py = _attention_py(q.tolist(), k.tolist(), v.tolist(), mask, 0.3)
+    np.testing.assert_allclose(o[:70], o_py[sub], rtol=1e-12, atol=1e-13)
+
+
 def test_segment_ids_triple_loop():
     Lq = Lk = 27
     ids = np.array([0] * 5 + [1] * 11 + [2] * 3 + [4] * 8)
@@ -320,6 +346,68 @@ def test_fixed_m_gate_sink_padding_and_promotion():
     # a tie passes
     kmax_t, m_t, mm_t, _ = oracle.fixed_m_bound(q, [k], scale, 106.5)
     assert oracle.fixed_m_bound(q, [k], scale, float(np.float32(mm_t)))[3]
+
+
+def _bf16_rne(x):
+    """fp32 values rounded to bf16 (round to nearest even), returned as fp32."""
+    b = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32)
+
+
+def _fixed_m_fp32(q, k, v, scale, m, shift):
+    """The fixed-m body in fp32 as a GPU computes it: p = 2^(shift) exp(s - m_i)
+    by base-2 exponentials whose results under 2^-126 are flushed to zero,
+    l summed in fp32, P rounded to bf16 for the value product."""
+    f = np.float32
+    s = (q.astype(f) @ k.astype(f).T).astype(f)
+    e = s * f(scale * math.log2(math.e)) - (m.astype(f) * f(math.log2(math.e)) - f(shift))[:, None]
+    p = np.exp2(e.astype(f)).astype(f)
+    p[p < np.finfo(f).tiny] = 0.0
+    l = p.sum(axis=1, dtype=f)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        o = (_bf16_rne(p) @ v.astype(f)) / l[:, None]
+    return np.nan_to_num(o, nan=0.0)
+
+
+def test_fixed_m_safe_range_is_what_fp32_supports():
+    # Worst rows for a fixed reference: every key points away from the query
+    # with the largest norm, so every score sits near -m_i, about 2 m_i below
+    # the reference.  Just under the safe maximum the fp32 fixed-m arithmetic
+    # stays within the bf16 tolerance of the exact result; at a bound the
+    # page's gate (106.5) admits, every term underflows and the row is lost,
+    # which is why the gate also requires m_i <= fixed_m_safe_max().
+    D, Lk, scale = 16, 4096, 0.25
+    rng = np.random.Generator(np.random.PCG64(50))
+    qdir = rng.standard_normal(D)
+    qdir /= np.linalg.norm(qdir)
+    v = rng.standard_normal((Lk, D))
+    assert 40.0 < oracle.fixed_m_safe_max() < 40.3
+    for m_target, safe in ((0.999 * oracle.fixed_m_safe_max(), True), (103.0, False)):
+        a = rng.uniform(0.9, 1.0, Lk)  # key norms; the largest sets kmax
+        a[0] = 1.0
+        k = -a[:, None] * qdir[None, :]
+        qn = m_target / scale  # ||q|| with kmax = 1
+        q = qn * qdir[None, :]
+        kmax, m, mmax, gate = oracle.fixed_m_bound(q, [k], scale, 106.5)
+        assert gate == safe and mmax == pytest.approx(m_target, rel=1e-12)
+        s = scale * q @ k.T
+        assert s.max() <= -0.89 * m_target  # every key far below the bound
+        o_ref, _ = oracle.attention(q, k, v, {}, scale)
+        o32 = _fixed_m_fp32(q, k, v, scale, m, shift=32)
+        err = np.abs(o32 - o_ref).max()
+        assert (err <= 2e-2) == safe, err
+    # the gate's boundary: a tie with the safe maximum passes, the next fp32 fails
+    edge = float(np.float32(oracle.fixed_m_safe_max()))
+    q1 = np.zeros((1, 4))
+    k1 = np.zeros((1, 4))
+    q1[0, 0], k1[0, 0] = edge, 1.0
+    assert oracle.fixed_m_bound(q1, [k1], 1.0, 106.5)[3]
+    q1[0, 0] = float(np.nextafter(np.float32(edge), np.float32(100)))
+    assert not oracle.fixed_m_bound(q1, [k1], 1.0, 106.5)[3]
+    # a caller's tau below the safe maximum still decides
+    q1[0, 0] = 30.0
+    assert oracle.fixed_m_bound(q1, [k1], 1.0, 106.5)[3] and not oracle.fixed_m_bound(q1, [k1], 1.0, 29.0)[3]
 
 
 def test_new_masks_reduce_to_known_ones():

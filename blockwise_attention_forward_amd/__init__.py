@@ -22,7 +22,7 @@ __all__ = [
     "bwa_block_mask_size", "bwa_block_mask_build", "bwa_fixed_m_bound", "bwa_attn_fwd",
     "bwa_attn_fwd_carry", "bwa_attn_fwd_balanced", "bwa_attn_fwd_balanced_workspace", "bwa_lse_merge",
     "bwa_attn_fwd_balanced_carry", "BWA_ORDER_ASC", "BWA_ORDER_DESC", "BWA_ORDER_OUTSIDE_IN",
-    "BWA_ORDER_CUSTOM", "bwa_attn_bwd", "bwa_attn_bwd_workspace",
+    "BWA_ORDER_CUSTOM", "bwa_attn_bwd", "bwa_attn_bwd_workspace", "bwa_attn_fwd_balanced_noalloc",
 ]
 
 BWA_F32, BWA_BF16 = 0, 1
@@ -84,6 +84,7 @@ def _load():
         "bwa_attn_fwd_balanced": (I32, [TP, TP, TP, MP, BP, F32, I32, P, P, I32, P, I64, TP, P, P]),
         "bwa_attn_fwd_balanced_carry": (I32, [TP, TP, TP, MP, BP, F32, I32, P, P, TP, P, I32, P, I64, TP, P, P]),
         "bwa_attn_fwd_balanced_workspace": (I32, [I32, I64, I64, I64, I64, I64, I32, I64P, I64P, I32P]),
+        "bwa_attn_fwd_balanced_noalloc": (I32, [TP, TP, TP, MP, BP, F32, I32, P, P, I32, TP, P, P]),
         "bwa_lse_merge": (I32, [I32, TP, ctypes.POINTER(ctypes.c_void_p), TP, P, P]),
         "bwa_attn_bwd": (I32, [TP, TP, TP, TP, P, TP, MP, F32, I32, P, P, I64, TP, TP, TP, P]),
         "bwa_attn_bwd_workspace": (I32, [MP, I64, I64, I64, I64, I64P, I64P]),
@@ -342,6 +343,28 @@ def bwa_attn_fwd_balanced(q, k, v, mask=None, blocks=None, scale=None, mode=BWA_
                                       ctypes.byref(mk.struct), bs, float(scale), int(mode), _ptr(m), _ptr(gate),
                                       int(n_cus), _ptr(workspace), nbytes, ctypes.byref(ot),
                                       _ptr(lse), _stream(q.device)), "bwa_attn_fwd_balanced")
+    return o, lse
+
+
+def bwa_attn_fwd_balanced_noalloc(q, k, v, mask=None, blocks=None, scale=None, mode=BWA_MODE_ONLINE, m=None,
+                                  gate=None, n_cus=0, o=None, lse=None, out_dtype=None):
+    """bwa_attn_fwd_balanced with the library's static device scratch in
+    place of a caller workspace (the call allocates nothing; o and lse are
+    allocated here with torch only when not given).  Returns (o, lse)."""
+    B, Lq, H, D = q.shape
+    if scale is None:
+        scale = D ** -0.5
+    if o is None:
+        o = torch.empty(B, Lq, H, D, dtype=out_dtype or q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, H, Lq, dtype=torch.float32, device=q.device)
+    mk = Mask.of(mask, q.device)
+    qt, kt, vt, ot = _tensor(q), _tensor(k), _tensor(v), _tensor(o)
+    bs = ctypes.byref(blocks.struct) if blocks is not None else None
+    _check(_lib.bwa_attn_fwd_balanced_noalloc(ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt),
+                                              ctypes.byref(mk.struct), bs, float(scale), int(mode), _ptr(m),
+                                              _ptr(gate), int(n_cus), ctypes.byref(ot), _ptr(lse),
+                                              _stream(q.device)), "bwa_attn_fwd_balanced_noalloc")
     return o, lse
 
 

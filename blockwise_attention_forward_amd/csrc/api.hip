@@ -1,7 +1,8 @@
 // C ABI entry points: argument validation on the host, then one or more
 // asynchronous launches on the caller's stream.  Nothing here allocates
 // device memory, synchronises or keeps state between calls (the last-error
-// string is thread-local).
+// string is thread-local; the allocation-free balanced launch caches the
+// address of its static scratch per device).
 
 #include <cstdarg>
 #include <cstdio>
@@ -424,6 +425,35 @@ int32_t bwa_attn_fwd_balanced(const bwa_tensor* q, const bwa_tensor* k, const bw
     if ((st = resolve_cus(n_cus, &bal.n_cus))) return st;
     bal.ws = workspace;
     bal.ws_bytes = workspace_bytes;
+    return attn_fwd_impl(q, k, v, mask, blocks, scale, mode, m, gate, nullptr, nullptr, o, lse, stream, &bal);
+}
+
+int32_t bwa_attn_fwd_balanced_noalloc(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
+                                      const bwa_mask* mask, const bwa_blocks* blocks, float scale, int32_t mode,
+                                      const float* m, const uint8_t* gate, int32_t n_cus, bwa_tensor* o, float* lse,
+                                      void* stream) {
+    Balance bal;
+    int32_t st;
+    if ((st = resolve_cus(n_cus, &bal.n_cus))) return st;
+    // The plan's workspace must fit the static scratch; checked before any
+    // launch (shapes as validated again by attn_fwd_impl).
+    if (q && k && q->dtype == BWA_BF16 && (q->D == 64 || q->D == 128) && q->B >= 0 && q->H >= 0 && q->L >= 0 &&
+        k->L >= 0) {
+        const i64 bq = bwa::attn_rows_per_block(q->dtype, (int)q->D);
+        const i64 units = q->B * q->H * ((q->L + bq - 1) / bq);
+        const i64 need = units > 0 ? bwa::split_workspace_bytes(bwa::split_plan(units, bal.n_cus, k->L), (int)bq,
+                                                                  (int)q->D)
+                                   : 0;
+        if (need > bwa::kNoAllocScratchBytes)
+            return fail(BWA_ERR_CAPACITY,
+                        "the balanced plan needs %lld bytes of workspace; the static scratch holds %lld "
+                        "(use bwa_attn_fwd_balanced with a workspace)",
+                        (long long)need, (long long)bwa::kNoAllocScratchBytes);
+    }
+    void* ws = nullptr;
+    if ((st = hip_status(bwa::noalloc_scratch(&ws), "static scratch address"))) return st;
+    bal.ws = ws;
+    bal.ws_bytes = bwa::kNoAllocScratchBytes;
     return attn_fwd_impl(q, k, v, mask, blocks, scale, mode, m, gate, nullptr, nullptr, o, lse, stream, &bal);
 }
 

@@ -41,6 +41,7 @@
 // the scale; LSE is returned in natural-log units.
 
 #include <algorithm>
+#include <mutex>
 
 #include "internal.h"
 
@@ -1456,6 +1457,33 @@ void split_workspace_layout(AttnLaunch& a, void* ws, const SplitPlan& sp, int ro
     a.split_tail = sp.tail;
     a.split_wg = sp.wg;
     (void)D;
+}
+
+// Workspace of the allocation-free balanced launch: queue counters and the
+// cut blocks' partials.  Every device the library runs on holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: kernels get the address that hipGetSymbolAddress returns
+// for the current device.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 int attn_rows_per_block(int dtype, int D) { return dtype == BWA_BF16 ? 32 * kBf16Waves : 128; }

@@ -150,6 +150,11 @@ struct SplitPlan {
 constexpr int kMaxSplit = 16;  // pieces per cut block at most
 SplitPlan split_plan(i64 units, int n_cus, i64 lk);
 i64 split_workspace_bytes(const SplitPlan& sp, int rows_per_block, int D);
+// The allocation-free balanced launch keeps its workspace in a static device
+// array of this many bytes; noalloc_scratch returns the array's address on
+// the current device (looked up once per device).
+constexpr i64 kNoAllocScratchBytes = (i64)64 << 20;
+hipError_t noalloc_scratch(void** ptr);
 void split_workspace_layout(AttnLaunch& a, void* ws, const SplitPlan& sp, int rows_per_block, int D);
 int attn_rows_per_block(int dtype, int D);
 

@@ -346,6 +346,25 @@ int32_t bwa_attn_fwd_balanced(const bwa_tensor* q, const bwa_tensor* k, const bw
                               bwa_tensor* o, float* lse, void* stream);
 
 /*
+ * bwa_attn_fwd_balanced for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation with the same plan and bits, its
+ * workspace taken from a static device array of 64 MiB that the library
+ * holds on each device it runs on until the process ends (the array's
+ * address is looked up on the first call on a device).  The call itself
+ * allocates nothing.  Arguments, results and errors as for
+ * bwa_attn_fwd_balanced without the workspace, plus BWA_ERR_CAPACITY when
+ * the plan's workspace (bwa_attn_fwd_balanced_workspace) exceeds 64 MiB,
+ * reported before anything is enqueued.  Every call on a device shares that
+ * device's array: calls that may overlap on one device (other streams,
+ * other threads) race and must be ordered by the caller.
+ */
+int32_t bwa_attn_fwd_balanced_noalloc(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
+                                      const bwa_mask* mask, const bwa_blocks* blocks, float scale,
+                                      int32_t mode, const float* m, const uint8_t* gate, int32_t n_cus,
+                                      bwa_tensor* o, float* lse, void* stream);
+
+/*
  * bwa_attn_fwd_balanced with a carried partial, merged as in
  * bwa_attn_fwd_carry [FIXEDM Notes]: whole blocks merge it in their epilogue,
  * cut blocks as one more part of the piece merge.  Arguments, aliasing rules

@@ -371,3 +371,17 @@ def _bwd(q=None, k=None, v=None, o=None, lse=0x20000, do=None, order=0, perm=Non
 def test_bwd_argument_errors(kw, code):
     assert _bwd(**kw) == code
     assert bw.bwa_last_error() != ""
+
+
+def test_balanced_noalloc_rejects_plans_beyond_the_static_scratch():
+    # 37,800 query rows x 20 heads of 256-row blocks on 256 workgroups: 144
+    # blocks cut in 4 pieces need ~76 MB of partials, beyond the 64 MiB
+    # scratch; refused before anything is enqueued (no device is touched)
+    q = _t(L=37800, H=20, sL=20 * 128, sB=37800 * 20 * 128)
+    k = _t(L=37800, H=20, sL=20 * 128, sB=37800 * 20 * 128)
+    f = L.bwa_attn_fwd_balanced_noalloc
+    st = f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), ctypes.byref(_mask()), None, 0.1, 0, None, None, 256,
+           ctypes.byref(q), 0x20000, None)
+    assert st == 7 and "67108864" in bw.bwa_last_error()
+    assert f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), ctypes.byref(_mask()), None, 0.1, 0, None, None,
+             (1 << 16) + 1, ctypes.byref(q), 0x20000, None) == 6

@@ -552,7 +552,38 @@ struct Bf16State {
     float m_run, l_run, m_fixed, m_l2, scale_l2;
     int lo, hi;
     int xres, xdoc;  // dilated bands / document ids (the XM kernels only)
+    // The wave's rows (wave-uniform): every visible key lies in
+    // [w_lo_min, w_hi_max); every key of [w_lo_max, w_hi_min) is inside every
+    // row's interval (empty when some row of the wave sees nothing); w_doc is
+    // the document id of all the wave's rows that see something when they
+    // share one (w_doc_one).
+    int w_lo_min, w_hi_max, w_lo_max, w_hi_min;
+    int w_doc;
+    bool w_doc_one;
 };
+
+// The wave-level fields of st from the lane's row (lanes l and l + 32 hold
+// the same row).
+template <int D, int NW>
+__device__ inline void wave_rows(Bf16State<D, NW>& st, bool row_ok, int lo, int hi) {
+    const bool ne = row_ok && lo < hi;
+    int a = ne ? lo : 0x7fffffff, b = ne ? hi : 0;
+    int c = row_ok ? (ne ? lo : 0x7fffffff) : 0, d = row_ok ? (ne ? hi : -1) : 0x7fffffff;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        a = min(a, __shfl_xor(a, o));
+        b = max(b, __shfl_xor(b, o));
+        c = max(c, __shfl_xor(c, o));
+        d = min(d, __shfl_xor(d, o));
+    }
+    st.w_lo_min = uni(a);
+    st.w_hi_max = uni(b);
+    st.w_lo_max = uni(c);
+    st.w_hi_min = uni(d);
+    const unsigned long long seen = __builtin_amdgcn_ballot_w64(ne);
+    st.w_doc = seen ? __builtin_amdgcn_readlane(st.xdoc, __builtin_ctzll(seen)) : 0;
+    st.w_doc_one = __builtin_amdgcn_ballot_w64(ne && st.xdoc != st.w_doc) == 0;
+}
 
 // Swizzles of the 16-byte chunk index c of row r.  A 256-byte bank window
 // holds one row of D = 128 or two rows of D = 64; the XOR spreads the rows a
@@ -919,7 +950,24 @@ __device__ __attribute__((always_inline)) inline bool bf16_step(const AttnLaunch
         bf16_issue_tile<D, NW, XM>(p, kbase, vbase, ahead.j0, kv_lim, ring.k[J], ring.v[J], ring.kid[J], xm);
         ++n_after;
     }
-    bf16_compute_tile<D, NW, BODY, XM, SPEC>(ring.k[I], ring.v[I], st, j0, masked, xm, ring.kid[I]);
+    // Tiles listed as partial, classified again for the wave's own rows: a
+    // tile none of them sees is skipped (its terms would all be zero), a tile
+    // all of them see whole runs unmasked.  Both give the bits of the masked
+    // computation.  With document ids the tile's key ids (in LDS with its K
+    // and V) decide too, when the wave's rows share one document.
+    bool skip = false, wmasked = masked;
+    if (masked) {
+        if (j0 + C::TILE <= st.w_lo_min || j0 >= st.w_hi_max) skip = true;
+        else if (!XM && j0 >= st.w_lo_max && j0 + C::TILE <= st.w_hi_min) wmasked = false;
+        if (XM && !skip && xm.kid && xm.g == 1 && st.w_doc_one) {
+            const int lane = threadIdx.x & 63, key = j0 + lane;
+            const bool hit = ring.kid[I][lane] == st.w_doc && key >= st.w_lo_min && key < st.w_hi_max;
+            const unsigned long long m = __builtin_amdgcn_ballot_w64(hit);
+            if (m == 0ull) skip = true;
+            else if (m == ~0ull && j0 >= st.w_lo_max && j0 + C::TILE <= st.w_hi_min) wmasked = false;
+        }
+    }
+    if (!skip) bf16_compute_tile<D, NW, BODY, XM, SPEC>(ring.k[I], ring.v[I], st, j0, wmasked, xm, ring.kid[I]);
     const bool have = cur.next(walk);
     if (have) --n_after;
     return have;
@@ -1038,6 +1086,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_bf16(const 
     st.xres = 0;
     st.xdoc = 0;
     if (XM) xmask_row(p, b, row, row_ok, st.xres, st.xdoc);
+    wave_rows(st, row_ok, lo, hi);
 
     const bool ne = row_ok && lo < hi;
     const Walk walk = make_walk<C::TILE, C::NT>(p, b, qb, ne ? lo : 0x7fffffff, ne ? hi : 0,
@@ -1126,6 +1175,9 @@ __device__ inline void bal_item(const AttnLaunch& p, const Ring<D, NW>& ring, in
         st.m_l2 = st.m_fixed * kLog2e - kFixedShift;
     }
     st.scale_l2 = p.scale * kLog2e;
+    st.xres = 0;
+    st.xdoc = 0;
+    wave_rows(st, row_ok, lo, hi);
     const bool ne = row_ok && lo < hi;
     const Walk walk = make_walk<C::TILE, C::NT>(p, b, qb, ne ? lo : 0x7fffffff, ne ? hi : 0,
                                                 row_ok ? (ne ? lo : 0x7fffffff) : 0,

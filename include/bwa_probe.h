@@ -32,6 +32,21 @@ extern "C" {
  */
 int32_t bwa_probe_mfma_bf16(int32_t iters, int32_t blocks, float* sink, uint64_t* clocks, void* stream);
 
+/*
+ * HBM streaming probe: the bandwidth the device sustains for a mix of
+ * reads and writes.  src (device, 16-byte aligned) holds `ratio` streams of
+ * `chunks` 16-byte chunks each; every chunk is read once with non-temporal
+ * loads.  With dst (device, 16-byte aligned, `chunks` 16-byte chunks), chunk j
+ * of dst receives the XOR of chunk j of every stream: ratio * 16 bytes read
+ * per 16 bytes written (the LSE merge of two fp32 partials into bf16 reads
+ * 4 bytes per byte written).  With dst NULL nothing but sink (device, one
+ * float per work-item) is written: a read-only pass.  `blocks` workgroups of
+ * 256 work-items stride over the chunks.  Returns 0, 1 for bad arguments,
+ * or 8 when the launch fails.
+ */
+int32_t bwa_probe_stream(const void* src, int64_t chunks, int32_t ratio, void* dst, int32_t blocks, float* sink,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -47,7 +47,16 @@ def test_probe_library_exports_and_rejects_bad_arguments():
         pytest.skip("libbwa_probe.so not built")
     lib = ctypes.CDLL(PROBE_LIB)
     names = _declared(PROBE_HEADER)
-    assert names == ["bwa_probe_mfma_bf16"]
+    assert names == ["bwa_probe_mfma_bf16", "bwa_probe_stream"]
+    g = lib.bwa_probe_stream
+    g.restype = ctypes.c_int32
+    g.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    assert g(None, 16, 1, None, 1, ctypes.c_void_p(16), None) == 1
+    assert g(ctypes.c_void_p(16), 0, 1, None, 1, ctypes.c_void_p(16), None) == 1
+    assert g(ctypes.c_void_p(16), 16, 0, None, 1, ctypes.c_void_p(16), None) == 1
+    assert g(ctypes.c_void_p(16), 16, 1, None, 1, None, None) == 1
+    assert g(ctypes.c_void_p(24), 16, 1, ctypes.c_void_p(32), 1, None, None) == 1
     assert all(hasattr(lib, n) for n in names)
     f = lib.bwa_probe_mfma_bf16
     f.restype = ctypes.c_int32

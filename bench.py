@@ -341,6 +341,20 @@ def _measured_ceilings(torch):
                 best = (r, sum(ghz) / len(ghz))
         out["mfma_bf16_TFLOPs"] = round(best[0], 1)
         out["mfma_probe_clock_GHz"] = round(best[1], 3)
+        # the same products with one operand read from LDS per product (the
+        # attention kernel's inner loop without softmax, copies and barriers)
+        h = lib.bwa_probe_mfma_lds_bf16
+        h.restype = ctypes.c_int32
+        h.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        lsink = torch.empty(256 * 512, device="cuda")
+        assert h(iters // 10, 256, lsink.data_ptr(), stream) == 0
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(3):
+            assert h(iters, 256, lsink.data_ptr(), stream) == 0
+        b.record()
+        torch.cuda.synchronize()
+        out["mfma_lds_bf16_TFLOPs"] = round(256 * 8 * iters * 8 * 32768.0 * 3 / (a.elapsed_time(b) * 1e-3) / 1e12, 1)
         # streaming probes: the merge's mix (4 bytes read per byte written)
         # and a read-only pass (the bound's mix), 1 GiB of reads each
         g = lib.bwa_probe_stream

@@ -33,6 +33,18 @@ extern "C" {
 int32_t bwa_probe_mfma_bf16(int32_t iters, int32_t blocks, float* sink, uint64_t* clocks, void* stream);
 
 /*
+ * Matrix-core throughput with one operand from LDS, as in the attention
+ * kernel's inner loop: `blocks` workgroups of 512 work-items (8 wavefronts,
+ * one workgroup per compute unit), each wavefront running `iters` iterations
+ * of 8 v_mfma_f32_32x32x16_bf16 products, each taking a fresh 1 KB fragment
+ * read from LDS (16 bytes per lane) and a register operand, in two
+ * accumulation chains.  Work = blocks * 8 * iters * 8 * 32768 FLOP.  sink
+ * (device, blocks * 512 floats) receives one float per work-item.  Returns 0,
+ * 1 for bad arguments, or 8 when the launch fails.
+ */
+int32_t bwa_probe_mfma_lds_bf16(int32_t iters, int32_t blocks, float* sink, void* stream);
+
+/*
  * HBM streaming probe: the bandwidth the device sustains for a mix of
  * reads and writes.  src (device, 16-byte aligned) holds `ratio` streams of
  * `chunks` 16-byte chunks each; every chunk is read once with non-temporal

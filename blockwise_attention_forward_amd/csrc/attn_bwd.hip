@@ -124,42 +124,17 @@ __device__ inline int bswz(int r, int c) {
     return D == 128 ? c ^ (((r & 3) << 2) | ((r >> 2) & 3)) : c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
-// A 64-row tile staged through registers: each of NT work-items loads 8D/NT
-// chunks of 16 bytes (chunk id = it*NT + tid: row id / NCH, chunk id % NCH,
-// so a row's chunks come from consecutive lanes), then stores each at its
-// swizzled place in LDS.  Rows at or past `nvalid` are zeros.
-template <int D, int NT = 256>
-struct Staged {
-    uint4 c[8 * D / NT];
-};
-
-template <int D, int NT = 256>
-__device__ inline void stage_load(Staged<D, NT>& x, const __bf16* base, i64 sL, int nvalid) {
-    constexpr int NCH = Cfg<D>::NCH;
-#pragma unroll
-    for (int it = 0; it < 8 * D / NT; ++it) {
-        const int id = it * NT + (int)threadIdx.x, r = id / NCH, c = id % NCH;
-        x.c[it] = r < nvalid ? *(const uint4*)(base + (i64)r * sL + c * 8) : uint4{0, 0, 0, 0};
-    }
-}
-
-template <int D, int NT = 256>
-__device__ inline void stage_store(const Staged<D, NT>& x, uint8_t* t) {
-    constexpr int NCH = Cfg<D>::NCH;
-#pragma unroll
-    for (int it = 0; it < 8 * D / NT; ++it) {
-        const int id = it * NT + (int)threadIdx.x, r = id / NCH, c = id % NCH;
-        *(uint4*)(t + r * (D * 2) + bswz<D>(r, c) * 16) = x.c[it];
-    }
-}
-
+// (Each LDS address below is the tile's base plus one integer offset: the
+// compiler tells which LDS array a read touches only through a short chain of
+// address steps, and a read it cannot place waits for every copy into LDS in
+// flight.)
 // Operand fragment whose rows are tile rows rb*32 + l32 (16-deep step ds over
 // d: the lane holds d = ds*16 + hb*8 + 0..7).
 template <int D>
 __device__ inline uint4 frag_rows(const uint8_t* t, int rb, int ds) {
     const int lane = threadIdx.x & 63, l32 = lane & 31, hb = lane >> 5;
     const int r = rb * 32 + l32;
-    return *(const uint4*)(t + r * (D * 2) + bswz<D>(r, ds * 2 + hb) * 16);
+    return *(const uint4*)(t + (r * (D * 2) + bswz<D>(r, ds * 2 + hb) * 16));
 }
 
 // Operand fragment whose rows are tile columns d = db*32 + l32, over the 16
@@ -175,9 +150,67 @@ __device__ inline uint4 frag_cols(const uint8_t* t, int kk, int db) {
     const int c = db * 4 + g1 * 2 + (u >> 1);
     const int r0 = kk * 16 + hb * 4 + s_row, r1 = r0 + 8;
     const s16x4 x0 =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + r0 * (D * 2) + bswz<D>(r0, c) * 16 + (u & 1) * 8));
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + (r0 * (D * 2) + bswz<D>(r0, c) * 16 + (u & 1) * 8)));
     const s16x4 x1 =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + r1 * (D * 2) + bswz<D>(r1, c) * 16 + (u & 1) * 8));
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + (r1 * (D * 2) + bswz<D>(r1, c) * 16 + (u & 1) * 8)));
+    uint4 out;
+    out.x = __builtin_bit_cast(uint2, x0).x;
+    out.y = __builtin_bit_cast(uint2, x0).y;
+    out.z = __builtin_bit_cast(uint2, x1).x;
+    out.w = __builtin_bit_cast(uint2, x1).y;
+    return out;
+}
+
+// The lane's byte offsets of frag_rows(t, 0, ds) (ro[ds]) and of the two
+// transposing reads of frag_cols(t, 0, db) (co[2 db], co[2 db + 1]) within a
+// tile.  The swizzle depends on a row's index modulo 16 only, so another row
+// block rb or step kk adds the constant rb*32 or kk*16 rows.  A kernel that
+// reads several ring buffers computes these once and adds each buffer's base
+// (a constant that the LDS read takes as its immediate offset): without that
+// the compiler keeps one set of addresses per buffer alive across the loop.
+template <int D>
+struct FragOffs {
+    int ro[D / 16], co[D / 16];
+};
+
+template <int D>
+__device__ inline FragOffs<D> frag_offsets() {
+    FragOffs<D> f;
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hb = lane >> 5;
+    const int g1 = (lane >> 4) & 1, s_row = (lane >> 2) & 3, u = lane & 3;
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) f.ro[ds] = l32 * (D * 2) + bswz<D>(l32, ds * 2 + hb) * 16;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        const int c = db * 4 + g1 * 2 + (u >> 1);
+        const int r0 = hb * 4 + s_row, r1 = r0 + 8;
+        f.co[2 * db] = r0 * (D * 2) + bswz<D>(r0, c) * 16 + (u & 1) * 8;
+        f.co[2 * db + 1] = r1 * (D * 2) + bswz<D>(r1, c) * 16 + (u & 1) * 8;
+    }
+    return f;
+}
+
+// The offsets as new values: address arithmetic on them stays where it is
+// used instead of being hoisted out of the tile loop once per buffer.
+template <int D>
+__device__ __attribute__((always_inline)) inline void repin(FragOffs<D>& f) {
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+        asm volatile("" : "+v"(f.ro[i]));
+        asm volatile("" : "+v"(f.co[i]));
+    }
+}
+
+template <int D>
+__device__ inline uint4 frag_rows_at(const uint8_t* t, const FragOffs<D>& f, int rb, int ds) {
+    return *(const uint4*)(t + (rb * 32 * (D * 2) + f.ro[ds]));
+}
+
+template <int D>
+__device__ inline uint4 frag_cols_at(const uint8_t* t, const FragOffs<D>& f, int kk, int db) {
+    const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + (kk * 16 * (D * 2) + f.co[2 * db])));
+    const s16x4 x1 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + (kk * 16 * (D * 2) + f.co[2 * db + 1])));
     uint4 out;
     out.x = __builtin_bit_cast(uint2, x0).x;
     out.y = __builtin_bit_cast(uint2, x0).y;
@@ -249,6 +282,41 @@ __device__ inline void store_tile(void* row_ptr, const f32x16& acc, int db, floa
             *(f32x4*)((float*)row_ptr + d) = f32x4{a, b, c, e};
         } else {
             *(uint2*)((__bf16*)row_ptr + d) = uint2{pack_bf16x2(a, b), pack_bf16x2(c, e)};
+        }
+    }
+}
+
+// One 64-row tile (rows past nvalid read as zero) copied from HBM straight
+// into LDS: lane i of a buffer load with an LDS destination fills bytes
+// [16i, 16i + 16) of a 1 KB run, so each lane loads the global chunk whose
+// swizzled place (bswz, its own inverse) is its slot: row r of the tile holds
+// its 16-byte chunk c at r*2D + bswz(r, c)*16.  No registers, LDS stores or
+// waits on the way.  The buffer range ends with the last valid row's D
+// elements; loads past it return zero.  Each of the NW waves issues RUNS/NW
+// loads.
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D, int NW>
+struct TileCopy {
+    static constexpr int RUNS = Cfg<D>::TILE_BYTES / 1024;  // 1 KB runs per tile
+    static constexpr int PER_WAVE = (RUNS + NW - 1) / NW;  // loads per wave and tile
+};
+
+template <int D, int NW>
+__device__ inline void tile_issue(const __bf16* base, i64 sL, int nvalid, uint8_t* lds) {
+    using T = TileCopy<D, NW>;
+    constexpr int NCH = Cfg<D>::NCH;
+    const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int bytes = uni(nvalid > 0 ? (int)(((i64)(nvalid - 1) * sL + D) * 2) : 0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kRsrcFlags);
+#pragma unroll
+    for (int it = 0; it < T::PER_WAVE; ++it) {
+        const int run = wave * T::PER_WAVE + it;
+        if (T::RUNS % NW == 0 || run < T::RUNS) {
+            const int slot = run * 64 + lane, r = slot / NCH, c = bswz<D>(r, slot % NCH);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + run * 1024), 16,
+                                                     (unsigned)(r * sL * 2 + c * 16), 0, 0, 0);
         }
     }
 }
@@ -356,37 +424,28 @@ __device__ inline bool q_next(const BwdLaunch& p, QCursor& c, i64 lb, int m0, in
 // and dV through LDS at the end (rh 0 + rh 1, a fixed order).  Query tiles
 // go through two LDS buffers, each tile's loads issued one tile ahead.
 // ---------------------------------------------------------------------------
+// Copies of one query tile into LDS: its Q and dO rows (rows past q_valid
+// read as zero) and, by waves 0..3, the rows' LSE, delta and key interval
+// (64 values each; rows past Lq read as zero and see nothing).
 template <int D>
-struct KvStage8 {
-    Staged<D, 512> q, g;
-    float st;  // work-items 0..255: LSE, delta, lo, hi of row tid % 64
-};
-
-template <int D>
-__device__ inline void kv_load8(const BwdLaunch& p, KvStage8<D>& x, const QCursor& c, i64 b, i64 hk, i64 lb) {
+__device__ inline void kv_issue8(const BwdLaunch& p, const QCursor& c, i64 b, i64 hk, i64 lb, uint8_t* qt,
+                                 uint8_t* gt, float* st) {
     const i64 h = hk * p.kv_group + c.g;
     const i64 r0 = (i64)c.m * kTile;
-    const int nq = (int)min((i64)kTile, p.mask.q_valid - r0);
-    stage_load<D, 512>(x.q, (const __bf16*)p.q + b * p.q_sB + r0 * p.q_sL + h * p.q_sH, p.q_sL, nq);
-    stage_load<D, 512>(x.g, (const __bf16*)p.dout + b * p.do_sB + r0 * p.do_sL + h * p.do_sH, p.do_sL, nq);
+    const int nq = (int)max((i64)0, min((i64)kTile, p.mask.q_valid - r0));
+    tile_issue<D, 8>((const __bf16*)p.q + b * p.q_sB + r0 * p.q_sL + h * p.q_sH, p.q_sL, nq, lds_opaque(qt));
+    tile_issue<D, 8>((const __bf16*)p.dout + b * p.do_sB + r0 * p.do_sL + h * p.do_sH, p.do_sL, nq,
+                     lds_opaque(gt));
     const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const i64 row = r0 + lane;
-    const i64 li = (b * p.H + h) * p.Lq + row;
-    float v = 0.0f;
-    if (row < p.Lq) {
-        if (wave == 0) v = p.lse[li];
-        else if (wave == 1) v = p.delta[li];
-        else if (wave == 2) v = __int_as_float(p.row_lo[lb * p.Lq + row]);
-        else if (wave == 3) v = __int_as_float(p.row_hi[lb * p.Lq + row]);
+    if (wave < 4) {
+        const int nr = (int)max((i64)0, min((i64)kTile, p.Lq - r0));
+        const i64 li = (b * p.H + h) * p.Lq + r0, ri = lb * p.Lq + r0;
+        const void* src = wave == 0 ? (const void*)(p.lse + li) : wave == 1 ? (const void*)(p.delta + li)
+                        : wave == 2 ? (const void*)(p.row_lo + ri) : (const void*)(p.row_hi + ri);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, nr * 4, kRsrcFlags);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_opaque(st + wave * 64), 4,
+                                                 (unsigned)(lane * 4), 0, 0, 0);
     }
-    x.st = v;
-}
-
-template <int D>
-__device__ inline void kv_store8(const BwdLaunch& p, const KvStage8<D>& x, uint8_t* qt, uint8_t* gt, float* st) {
-    stage_store<D, 512>(x.q, qt);
-    stage_store<D, 512>(x.g, gt);
-    if (threadIdx.x < 256) st[threadIdx.x] = x.st;
 }
 
 // Rows rh*32 .. rh*32+31 of one query tile against the wave's 32 keys (K and
@@ -499,17 +558,14 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv8(const BwdLaunch p) {
     const int key = kw0 + l32;
 
     // The block's K and V rows (past kv_valid: zeros) into LDS.
-    {
-        Staged<D, 512> x;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int j0 = k0 + 64 * half;
-            const int nk = (int)min((i64)kTile, p.mask.kv_valid - j0);
-            stage_load<D, 512>(x, (const __bf16*)p.k + b * p.k_sB + (i64)j0 * p.k_sL + hk * p.k_sH, p.k_sL, nk);
-            stage_store<D, 512>(x, ks[half]);
-            stage_load<D, 512>(x, (const __bf16*)p.v + b * p.v_sB + (i64)j0 * p.v_sL + hk * p.v_sH, p.v_sL, nk);
-            stage_store<D, 512>(x, vs[half]);
-        }
+    for (int half = 0; half < 2; ++half) {
+        const int j0 = k0 + 64 * half;
+        const int nk = (int)max((i64)0, min((i64)kTile, p.mask.kv_valid - j0));
+        tile_issue<D, 8>((const __bf16*)p.k + b * p.k_sB + (i64)j0 * p.k_sL + hk * p.k_sH, p.k_sL, nk,
+                         lds_opaque(ks[half]));
+        tile_issue<D, 8>((const __bf16*)p.v + b * p.v_sB + (i64)j0 * p.v_sL + hk * p.v_sH, p.v_sL, nk,
+                         lds_opaque(vs[half]));
     }
     f32x16 dk[C::NDB], dv[C::NDB];
 #pragma unroll
@@ -518,22 +574,18 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv8(const BwdLaunch p) {
     const int m0 = ld_const(p.kfirst, lb * p.nkb + kb), m1 = ld_const(p.klast, lb * p.nkb + kb);
     QCursor cur{0, m0 - 1};
     bool have = m0 <= m1 && q_next(p, cur, lb, m0, m1, k0, k0 + kKeyBlock);
-    KvStage8<D> stg;
-    if (have) {
-        kv_load8<D>(p, stg, cur, b, hk, lb);
-        kv_store8<D>(p, stg, qs[0], gs[0], ss[0]);
-    }
-    wait_loads();
+    if (have) kv_issue8<D>(p, cur, b, hk, lb, qs[0], gs[0], ss[0]);
     int buf = 0;
     while (have) {
-        // Buffer `buf` (and the key tiles) are complete, and every wave is done
-        // with the other buffer.
+        // This wave's copies of buffer `buf` (and of the key tiles) have
+        // landed; after the barrier every wave's have, and every wave is done
+        // with the other buffer, which the next tile's copies then fill.
+        wait_loads();
         __syncthreads();
         QCursor nxt = cur;
         const bool more = q_next(p, nxt, lb, m0, m1, k0, k0 + kKeyBlock);
-        if (more) kv_load8<D>(p, stg, nxt, b, hk, lb);
+        if (more) kv_issue8<D>(p, nxt, b, hk, lb, qs[buf ^ 1], gs[buf ^ 1], ss[buf ^ 1]);
         kv_compute8<D>(p, qs[buf], gs[buf], ss[buf], ks[kg >> 1], vs[kg >> 1], kg & 1, dk, dv, cur, lb, kw0, rh);
-        if (more) kv_store8<D>(p, stg, qs[buf ^ 1], gs[buf ^ 1], ss[buf ^ 1]);
         cur = nxt;
         have = more;
         buf ^= 1;
@@ -581,42 +633,34 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv8(const BwdLaunch p) {
 // intervals and document ids, stream through LDS.  The element test needs
 // registers that the two-wave form above does not have to spare.
 // ---------------------------------------------------------------------------
-// Loads of one query tile (Q, dO and the rows' LSE, delta and key interval)
-// into registers; the work-items of wave w load statistic w.
+// Copies of one query tile into LDS: its Q and dO rows (rows past q_valid
+// read as zero), and by wave w statistic w of its rows (LSE, delta, key
+// interval lo, hi); with document ids every wave also copies the rows' ids
+// (the same bytes, so each wave's count of copies per tile is the same).
+// Rows past Lq read as zero and see nothing.
 template <int D>
-struct KvStage {
-    Staged<D> q, g;
-    float st;
-    int id;  // document id of row tid (work-items 0..63, document masks only)
-};
-
-template <int D>
-__device__ inline void kv_load(const BwdLaunch& p, KvStage<D>& x, const QCursor& c, i64 b, i64 hk, i64 lb) {
+__device__ inline void kv_issue(const BwdLaunch& p, const QCursor& c, i64 b, i64 hk, i64 lb, uint8_t* qt,
+                                uint8_t* gt, float* st) {
     const i64 h = hk * p.kv_group + c.g;
     const i64 r0 = (i64)c.m * kTile;
-    const int nq = (int)min((i64)kTile, p.mask.q_valid - r0);
-    stage_load<D>(x.q, (const __bf16*)p.q + b * p.q_sB + r0 * p.q_sL + h * p.q_sH, p.q_sL, nq);
-    stage_load<D>(x.g, (const __bf16*)p.dout + b * p.do_sB + r0 * p.do_sL + h * p.do_sH, p.do_sL, nq);
+    const int nq = (int)max((i64)0, min((i64)kTile, p.mask.q_valid - r0));
+    tile_issue<D, 4>((const __bf16*)p.q + b * p.q_sB + r0 * p.q_sL + h * p.q_sH, p.q_sL, nq, lds_opaque(qt));
+    tile_issue<D, 4>((const __bf16*)p.dout + b * p.do_sB + r0 * p.do_sL + h * p.do_sH, p.do_sL, nq,
+                     lds_opaque(gt));
     const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const i64 row = r0 + lane;
-    const i64 li = (b * p.H + h) * p.Lq + row;
-    float v = 0.0f;
-    if (row < p.Lq) {
-        if (wave == 0) v = p.lse[li];
-        else if (wave == 1) v = p.delta[li];
-        else if (wave == 2) v = __int_as_float(p.row_lo[lb * p.Lq + row]);
-        else v = __int_as_float(p.row_hi[lb * p.Lq + row]);
+    const int nr = (int)max((i64)0, min((i64)kTile, p.Lq - r0));
+    const i64 li = (b * p.H + h) * p.Lq + r0, ri = lb * p.Lq + r0;
+    const void* src = wave == 0 ? (const void*)(p.lse + li) : wave == 1 ? (const void*)(p.delta + li)
+                    : wave == 2 ? (const void*)(p.row_lo + ri) : (const void*)(p.row_hi + ri);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, nr * 4, kRsrcFlags);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_opaque(st + wave * 64), 4, (unsigned)(lane * 4), 0,
+                                             0, 0);
+    if (p.mask.seg_mode == 3) {
+        const __amdgpu_buffer_rsrc_t is =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(p.mask.ids_q + b * p.mask.lq + r0), 0, nr * 4, kRsrcFlags);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is, (lds_void*)lds_opaque(st + 256), 4, (unsigned)(lane * 4), 0, 0,
+                                                 0);
     }
-    x.st = v;
-    if (p.mask.seg_mode == 3 && wave == 0) x.id = row < p.Lq ? p.mask.ids_q[b * p.mask.lq + row] : -1;
-}
-
-template <int D>
-__device__ inline void kv_store(const BwdLaunch& p, const KvStage<D>& x, uint8_t* qt, uint8_t* gt, float* st) {
-    stage_store<D>(x.q, qt);
-    stage_store<D>(x.g, gt);
-    st[threadIdx.x] = x.st;
-    if (p.mask.seg_mode == 3 && threadIdx.x < 64) st[256 + threadIdx.x] = __int_as_float(x.id);
 }
 
 // One 64-row query tile against the wave's 32 keys: 64 matrix-core steps in
@@ -714,9 +758,8 @@ __device__ inline void kv_compute(const BwdLaunch& p, const uint8_t* qt, const u
 template <int D, int G>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
     using C = Cfg<D>;
-    // Three tile buffers.  A tile's loads go to registers two iterations
-    // before it is computed and land in LDS one iteration before, so each
-    // load has a whole tile of compute to arrive.
+    // Three tile buffers; a tile's copies into LDS are issued two tiles
+    // before it is computed.
     __shared__ __attribute__((aligned(1024))) uint8_t qs[kRing][C::TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t gs[kRing][C::TILE_BYTES];
     __shared__ __attribute__((aligned(256))) float ss[kRing][320];  // LSE, delta, lo, hi, doc id of 64 rows
@@ -753,29 +796,35 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
     const int m0 = ld_const(p.kfirst, lb * p.nkb + kb), m1 = ld_const(p.klast, lb * p.nkb + kb);
     QCursor cur{0, m0 - 1};
     bool have = m0 <= m1 && q_next(p, cur, lb, m0, m1, k0, k0 + kKeyBlock);
-    // Prologue: the first tile in LDS, the second in registers.
-    KvStage<D> stg;
-    QCursor ahead = cur;  // the tile whose loads are in registers
-    bool staged = false;
-    if (have) {
-        kv_load<D>(p, stg, cur, b, hk, lb);
-        kv_store<D>(p, stg, qs[0], gs[0], ss[0]);
-        staged = q_next(p, ahead, lb, m0, m1, k0, k0 + kKeyBlock);
-        if (staged) kv_load<D>(p, stg, ahead, b, hk, lb);
+    // Prologue: copies of the first two tiles.
+    constexpr int LOADS = 2 * TileCopy<D, 4>::PER_WAVE + 1;  // per wave and tile, plus the document ids
+    const int loads = LOADS + (p.mask.seg_mode == 3 ? 1 : 0);
+    QCursor ahead = cur;  // the last tile whose copies were issued
+    bool more = have;
+    int n_after = 0;      // tiles issued beyond cur
+    if (have) kv_issue<D>(p, cur, b, hk, lb, qs[0], gs[0], ss[0]);
+    if (more) more = q_next(p, ahead, lb, m0, m1, k0, k0 + kKeyBlock);
+    if (more) {
+        kv_issue<D>(p, ahead, b, hk, lb, qs[1], gs[1], ss[1]);
+        ++n_after;
     }
     int buf = 0;
     while (have) {
-        // Buffer `buf` is complete, and every wave is done with the buffer of
-        // the tile before it, which takes the staged tile now.
+        // This wave's copies of buffer `buf` have landed; after the barrier
+        // every wave's have, and every wave is done with the buffer of the
+        // tile before, which takes the copies two tiles ahead.
+        wait_vmcnt(n_after * loads);
         __syncthreads();
         const int nb = buf == kRing - 1 ? 0 : buf + 1;
-        if (staged) {
-            kv_store<D>(p, stg, qs[nb], gs[nb], ss[nb]);
-            staged = q_next(p, ahead, lb, m0, m1, k0, k0 + kKeyBlock);
-            if (staged) kv_load<D>(p, stg, ahead, b, hk, lb);
+        if (more) more = q_next(p, ahead, lb, m0, m1, k0, k0 + kKeyBlock);
+        if (more) {
+            const int fb = buf == 0 ? kRing - 1 : buf - 1;
+            kv_issue<D>(p, ahead, b, hk, lb, qs[fb], gs[fb], ss[fb]);
+            ++n_after;
         }
         kv_compute<D>(p, qs[buf], gs[buf], ss[buf], kf, vf, dk, dv, cur, kw0, key_id, key_res, dpat);
         have = q_next(p, cur, lb, m0, m1, k0, k0 + kKeyBlock);
+        if (have) --n_after;
         buf = nb;
     }
     if (key < p.Lk) {
@@ -836,27 +885,14 @@ __device__ inline bool t_next(const BwdLaunch& p, TCursor& c, int t_lo, int t_hi
     }
 }
 
-template <int D, int NT>
-struct QStage {
-    Staged<D, NT> k, v;
-};
-
-template <int D, int NT>
-__device__ inline void q_load(const BwdLaunch& p, QStage<D, NT>& x, int t, i64 b, i64 hk) {
-    const i64 j0 = (i64)t * kTile;
-    const int nk = (int)min((i64)kTile, p.mask.kv_valid - j0);
-    stage_load<D, NT>(x.k, (const __bf16*)p.k + b * p.k_sB + j0 * p.k_sL + hk * p.k_sH, p.k_sL, nk);
-    stage_load<D, NT>(x.v, (const __bf16*)p.v + b * p.v_sB + j0 * p.v_sL + hk * p.v_sH, p.v_sL, nk);
-}
-
 // One 64-key tile against the wave's 32 rows, with two waves per SIMD (the
 // other wave's products cover this one's element-wise work): each 32-key
 // half runs its S^T and dP^T products (the two chains alternating), its dS
 // and its own dQ^T products in turn, so only one half's scores and dS are
 // live; LDS operand reads run two steps ahead.
 template <int D, bool XM>
-__device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const uint8_t* vt,
-                                     const uint4 (&qf)[D / 16], const uint4 (&gf)[D / 16], f32x16 (&dq)[D / 32],
+__device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const uint8_t* vt, const FragOffs<D>& fo,
+                                     const uint4 (&qf)[D / 16], const uint8_t* gw, f32x16 (&dq)[D / 32],
                                      int t, int full_lo, int full_hi, int lo, int hi, float lse2, float delt, i64 b,
                                      int row, int row_id, int row_res, unsigned dpat) {
     using C = Cfg<D>;
@@ -870,22 +906,37 @@ __device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const ui
         constexpr int kb = decltype(kbc)::value;
         f32x16 S = {}, G = {};
         uint4 pd[2];
-        auto ld = [&](const int i) __attribute__((always_inline)) {
-            if (i < NS) return (i & 1) ? frag_rows<D>(vt, kb, i >> 1) : frag_rows<D>(kt, kb, i >> 1);
-            const int m = i - NS;
-            return frag_cols<D>(kt, kb * 2 + m / C::NDB, m % C::NDB);
+        // step i: the A operand, and for the dP^T steps dO's fragment as B
+        struct Ops {
+            uint4 a, b;
         };
-        uint4 fa[NP];
+        auto ld = [&](const int i) __attribute__((always_inline)) {
+            Ops o;
+            o.b = uint4{0, 0, 0, 0};
+            if (i < NS) {
+                if (i & 1) {
+                    o.a = frag_rows_at<D>(vt, fo, kb, i >> 1);
+                    o.b = frag_rows_at<D>(gw, fo, 0, i >> 1);
+                } else {
+                    o.a = frag_rows_at<D>(kt, fo, kb, i >> 1);
+                }
+            } else {
+                const int m = i - NS;
+                o.a = frag_cols_at<D>(kt, fo, kb * 2 + m / C::NDB, m % C::NDB);
+            }
+            return o;
+        };
+        Ops fa[NP];
         static_for<AH>([&](auto ic) { fa[ic.value] = ld(ic.value); });
         static_for<NP>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             if constexpr (i + AH < NP) fa[i + AH] = ld(i + AH);
             if constexpr (i < NS) {
-                if constexpr (i & 1) G = mfma(fa[i], gf[i >> 1], G);
-                else S = mfma(fa[i], qf[i >> 1], S);
+                if constexpr (i & 1) G = mfma(fa[i].a, fa[i].b, G);
+                else S = mfma(fa[i].a, qf[i >> 1], S);
             } else {
                 constexpr int m = i - NS;
-                dq[m % C::NDB] = mfma(fa[i], pd[m / C::NDB], dq[m % C::NDB]);
+                dq[m % C::NDB] = mfma(fa[i].a, pd[m / C::NDB], dq[m % C::NDB]);
             }
             if constexpr (i == NS - 1) {
                 // dilated band: the half's keys congruent to row - kv_offset mod g
@@ -921,13 +972,54 @@ __device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const ui
     });
 }
 
+// 32 rows (rows past nvalid read as zero) copied by one wave into LDS in the
+// layout of tile_issue (the first half of a 64-row tile).
+template <int D>
+__device__ inline void rows_issue_wave(const __bf16* base, i64 sL, int nvalid, uint8_t* lds) {
+    constexpr int NCH = Cfg<D>::NCH, RUNS = 32 * D * 2 / 1024;
+    const int lane = threadIdx.x & 63;
+    const int bytes = uni(nvalid > 0 ? (int)(((i64)(nvalid - 1) * sL + D) * 2) : 0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kRsrcFlags);
+#pragma unroll
+    for (int run = 0; run < RUNS; ++run) {
+        const int slot = run * 64 + lane, r = slot / NCH, c = bswz<D>(r, slot % NCH);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + run * 1024), 16,
+                                                 (unsigned)(r * sL * 2 + c * 16), 0, 0, 0);
+    }
+}
+
+// The dQ kernel's walk over its key tiles: the tile being computed (cur),
+// the last one whose copies were issued (ahead), and how many tiles beyond
+// cur have copies in flight.
+struct DqWalk {
+    TCursor cur, ahead;
+    bool more;     // ahead is a tile of the walk
+    int n_after;   // tiles issued beyond cur
+    int t_lo, t_hi;
+    const __bf16* kbase;
+    const __bf16* vbase;
+};
+
+template <int D, int NW>
+__device__ inline void dq_issue(const BwdLaunch& p, const DqWalk& w, uint8_t* kl, uint8_t* vl) {
+    const i64 j0 = (i64)w.ahead.t * kTile;
+    const int nk = (int)max((i64)0, min((i64)kTile, p.mask.kv_valid - j0));
+    tile_issue<D, NW>(w.kbase + j0 * p.k_sL, p.k_sL, nk, lds_opaque(kl));
+    tile_issue<D, NW>(w.vbase + j0 * p.v_sL, p.v_sL, nk, lds_opaque(vl));
+}
+
 template <int D, int G, bool XM, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
     using C = Cfg<D>;
-    constexpr int NT = NW * 64, RB = NW * 32;  // work-items, rows per workgroup
-    __shared__ __attribute__((aligned(1024))) uint8_t ks[kRing][C::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t vs[kRing][C::TILE_BYTES];
-    __shared__ int red[4 * NW];
+    constexpr int RB = NW * 32;  // rows per workgroup
+    constexpr int LOADS = 2 * TileCopy<D, NW>::PER_WAVE;
+    static_assert(2 * LOADS <= 15, "wait_vmcnt covers at most 15 outstanding copies");
+    // The ring: three K/V tile pairs.  dO rows of the block (each wave reads
+    // its own 32 as an operand).  The interval reduction borrows the third
+    // ring buffer before its first copy.
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[3][2][C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t gs[RB * D * 2];
+    int* red = (int*)&ring[2][0][0];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hb = lane >> 5;
     const i64 nqb = (p.Lq + RB - 1) / RB;
@@ -955,14 +1047,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
                             ? (int)((((i64)row - p.mask.kv_offset) % p.mask.dilation + p.mask.dilation) % p.mask.dilation)
                             : 0;
     const unsigned dpat = (XM && p.mask.dilation > 1) ? dil_pattern(p.mask.dilation) : 0u;
-    // Q and dO rows of this lane as the B operand: d = ds*16 + hb*8 + 0..7.
-    uint4 qf[C::NDS], gf[C::NDS];
+    // Q rows of this lane as the B operand: d = ds*16 + hb*8 + 0..7.
+    uint4 qf[C::NDS];
     const __bf16* qp = (const __bf16*)p.q + b * p.q_sB + (i64)row * p.q_sL + h * p.q_sH;
-    const __bf16* gp = (const __bf16*)p.dout + b * p.do_sB + (i64)row * p.do_sL + h * p.do_sH;
 #pragma unroll
-    for (int ds = 0; ds < C::NDS; ++ds) {
-        qf[ds] = row_in ? *(const uint4*)(qp + ds * 16 + hb * 8) : uint4{0, 0, 0, 0};
-        gf[ds] = row_in ? *(const uint4*)(gp + ds * 16 + hb * 8) : uint4{0, 0, 0, 0};
+    for (int ds = 0; ds < C::NDS; ++ds) qf[ds] = row_in ? *(const uint4*)(qp + ds * 16 + hb * 8) : uint4{0, 0, 0, 0};
+    // The wave's 32 dO rows (past q_valid: zeros) into its part of gs; only
+    // this wave reads them, so its own wait below covers them.
+    uint8_t* gw = gs + wave * 32 * (D * 2);
+    {
+        const i64 r0 = qb * RB + wave * 32;
+        const int nrow = (int)max((i64)0, min((i64)32, p.mask.q_valid - r0));
+        rows_issue_wave<D>((const __bf16*)p.dout + b * p.do_sB + r0 * p.do_sL + h * p.do_sH, p.do_sL, nrow,
+                           lds_opaque(gw));
     }
     f32x16 dq[C::NDB];
 #pragma unroll
@@ -990,34 +1087,43 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
     const int t_lo = env_lo < env_hi ? env_lo / kTile : 0;
     const int t_hi = env_lo < env_hi ? (env_hi + kTile - 1) / kTile : 0;
 
-    // Same pipeline as the dK/dV kernel: loads two tiles ahead in registers,
-    // stores one tile ahead into a ring of three buffers.
-    TCursor cur{-1, 0};
-    bool have = t_next(p, cur, t_lo, t_hi);
-    QStage<D, NT> stg;
-    TCursor ahead = cur;
-    bool staged = false;
-    if (have) {
-        q_load<D, NT>(p, stg, cur.t, b, hk);
-        stage_store<D, NT>(stg.k, ks[0]);
-        stage_store<D, NT>(stg.v, vs[0]);
-        staged = t_next(p, ahead, t_lo, t_hi);
-        if (staged) q_load<D, NT>(p, stg, ahead.t, b, hk);
+    // Copies run two tiles ahead of the compute.  Each step: wait for this
+    // wave's copies of the tile, then at the barrier for every wave's (after
+    // which every wave is also done with the previous tile's buffer, the one
+    // the next copy overwrites); issue the copies two tiles ahead; compute.
+    DqWalk wk;
+    wk.t_lo = t_lo;
+    wk.t_hi = t_hi;
+    wk.kbase = (const __bf16*)p.k + b * p.k_sB + hk * p.k_sH;
+    wk.vbase = (const __bf16*)p.v + b * p.v_sB + hk * p.v_sH;
+    wk.cur = TCursor{-1, 0};
+    bool have = t_next(p, wk.cur, t_lo, t_hi);
+    wk.ahead = wk.cur;
+    wk.more = have;
+    wk.n_after = 0;
+    // (the barrier above: every wave has read red before ring[2] is copied to)
+    if (have) dq_issue<D, NW>(p, wk, ring[0][0], ring[0][1]);
+    if (wk.more) wk.more = t_next(p, wk.ahead, t_lo, t_hi);
+    if (wk.more) {
+        dq_issue<D, NW>(p, wk, ring[1][0], ring[1][1]);
+        ++wk.n_after;
     }
+    const FragOffs<D> fo = frag_offsets<D>();
     int buf = 0;
     while (have) {
+        wait_vmcnt(wk.n_after * LOADS);
         __syncthreads();
-        const int nb = buf == kRing - 1 ? 0 : buf + 1;
-        if (staged) {
-            stage_store<D, NT>(stg.k, ks[nb]);
-            stage_store<D, NT>(stg.v, vs[nb]);
-            staged = t_next(p, ahead, t_lo, t_hi);
-            if (staged) q_load<D, NT>(p, stg, ahead.t, b, hk);
+        if (wk.more) wk.more = t_next(p, wk.ahead, t_lo, t_hi);
+        if (wk.more) {
+            const int nb = buf == 0 ? 2 : buf - 1;
+            dq_issue<D, NW>(p, wk, ring[nb][0], ring[nb][1]);
+            ++wk.n_after;
         }
-        q_compute<D, XM>(p, ks[buf], vs[buf], qf, gf, dq, cur.t, full_lo, full_hi, lo, hi, lse2, delt, b, row,
-                         row_id, row_res, dpat);
-        have = t_next(p, cur, t_lo, t_hi);
-        buf = nb;
+        q_compute<D, XM>(p, ring[buf][0], ring[buf][1], fo, qf, gw, dq, wk.cur.t, full_lo, full_hi, lo, hi, lse2,
+                         delt, b, row, row_id, row_res, dpat);
+        have = t_next(p, wk.cur, t_lo, t_hi);
+        if (have) --wk.n_after;
+        buf = buf == 2 ? 0 : buf + 1;
     }
     if (row_ok) {
         const i64 es = G == BWA_F32 ? 4 : 2;

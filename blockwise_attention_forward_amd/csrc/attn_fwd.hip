@@ -889,32 +889,6 @@ __device__ inline void bf16_compute_tile(const uint8_t* kl, const uint8_t* vl, B
     st.l_run += h0.rs + h1.rs;
 }
 
-// Wait until at most n of this wave's vector-memory operations are in flight
-// (the tile copies are the only ones in the loop; n is wave-uniform).
-__device__ inline void wait_vm(int n) {
-    // s_waitcnt fields (gfx9): vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8].
-    if (n <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);
-    else if (n <= 4) __builtin_amdgcn_s_waitcnt(0x0F74);
-    else if (n <= 8) __builtin_amdgcn_s_waitcnt(0x0F78);
-    else __builtin_amdgcn_s_waitcnt(0x0F7C);
-}
-
-// Wait until at most n (0 .. 8) of this wave's vector-memory operations are
-// in flight; n is wave-uniform.
-__device__ inline void wait_vm_exact(int n) {
-    switch (n) {
-        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-        case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
-        case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-        case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
-        case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    }
-}
-
 // The copy ring: NBUF K/V tile buffers, each its own LDS object, visited in
 // a compile-time unrolled order.  Reads of buffer I can then be told apart
 // from the copies still landing in the other buffers, so they do not wait
@@ -941,8 +915,7 @@ __device__ __attribute__((always_inline)) inline bool bf16_step(const AttnLaunch
     const bool masked = cur.masked(walk.Lk);
     // This tile's copies are complete in every wave, and every wave is done
     // with the buffer the next copy goes to (the previous tile's).
-    if (XM && xm.kid) wait_vm_exact(n_after * (LOADS + 1));  // K, V and the key ids
-    else wait_vm(n_after * LOADS);
+    wait_vmcnt(n_after * (XM && xm.kid ? LOADS + 1 : LOADS));  // K, V (and the key ids)
     __syncthreads();
     if (more) more = ahead.next(walk);
     if (more) {
@@ -980,7 +953,7 @@ __device__ inline void bf16_walk(const AttnLaunch& p, Bf16State<D, NW>& st, cons
     using C = Bf16Cfg<D, NW>;
     constexpr int NB = C::NBUF;
     static_assert(NB == 2 || NB == 3, "ring of 2 or 3 buffers");
-    static_assert(2 * C::RUNS_PER_WAVE * (NB - 2) <= 12, "wait_vm covers at most 12 outstanding copies");
+    static_assert((2 * C::RUNS_PER_WAVE + 1) * (NB - 2) <= 15, "wait_vmcnt covers at most 15 outstanding copies");
     const i64 hk = (int)h / p.kv_group;  // key/value head of query head h
     const __bf16* kbase = (const __bf16*)p.k + b * p.k_sB + hk * p.k_sH;
     const __bf16* vbase = (const __bf16*)p.v + b * p.v_sB + hk * p.v_sH;

@@ -29,6 +29,48 @@ struct MaskDev {
     const int* ids_kv;  // [B][lk]
 };
 
+// Wait until at most n (0 .. 15, wave-uniform) of this wave's vector-memory
+// operations are in flight.  The count is exact: with copies of several tiles
+// in flight, waiting for "at most 4" when only 2 may remain would let a wave
+// pass the barrier before its part of the current tile has landed.
+// s_waitcnt fields (gfx9): vmcnt[3:0] and [15:14], expcnt[6:4],
+// lgkmcnt[11:8]; the other counters are left at their maxima.
+__device__ inline void wait_vmcnt(int n) {
+    switch (n) {
+        case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+        case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+        case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+        case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+        case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+        case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+        case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+        case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+        case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+        case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
+        case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
+        case 15: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+}
+
+// The LDS address of a copy into LDS (a buffer load with an LDS
+// destination) as a value that the compiler cannot trace to an LDS object.
+// Before an LDS read the compiler waits for every copy it cannot tell apart
+// from the read's object; a ring indexed at run time is one such object, so
+// the first read of a tile would wait for the copies of the tiles ahead,
+// issued just before.  With the address opaque it adds no such wait, and the
+// kernel orders each tile's copies before its reads itself: wait_vmcnt for
+// the wave's own copies, then the workgroup barrier.  (The empty asm keeps a
+// known buffer address from being folded back to its LDS object.)
+__device__ inline uint8_t* lds_opaque(void* p) {
+    unsigned a = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)p);
+    asm volatile("" : "+s"(a));
+    return (uint8_t*)(__attribute__((address_space(3))) uint8_t*)(uintptr_t)a;
+}
+
 // Keys visible to query row i of batch element b lie in one interval
 // [lo, hi): every term of the mask bounds them from below or above (padding,
 // segment, causal, prefix and window terms of the visibility rule in

@@ -304,7 +304,7 @@ struct TileCopy {
 };
 
 template <int D, int NW>
-__device__ inline void tile_issue(const __bf16* base, i64 sL, int nvalid, uint8_t* lds) {
+__device__ inline void tile_issue(const __bf16* base, i64 sL, int nvalid, int lds) {
     using T = TileCopy<D, NW>;
     constexpr int NCH = Cfg<D>::NCH;
     const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -315,10 +315,65 @@ __device__ inline void tile_issue(const __bf16* base, i64 sL, int nvalid, uint8_
         const int run = wave * T::PER_WAVE + it;
         if (T::RUNS % NW == 0 || run < T::RUNS) {
             const int slot = run * 64 + lane, r = slot / NCH, c = bswz<D>(r, slot % NCH);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + run * 1024), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)(lds + run * 1024), 16,
                                                      (unsigned)(r * sL * 2 + c * 16), 0, 0, 0);
         }
     }
+}
+
+// The 64-row tiles of one head of a tensor, copied into LDS one after
+// another: what every copy shares (the head's first row, the tile stride,
+// this lane's offsets within a tile) is computed once, so a copy costs a
+// multiply, a range and its loads.  Rows at or past `nrows` read as zero.
+template <int D, int NW>
+struct TileStream {
+    const uint8_t* head;
+    i64 tile_bytes;  // 64 rows
+    int row_bytes;
+    int nrows;
+    unsigned voff[TileCopy<D, NW>::PER_WAVE];
+};
+
+template <int D, int NW>
+__device__ inline void stream_init(TileStream<D, NW>& s, const __bf16* head, i64 sL, i64 nrows) {
+    using T = TileCopy<D, NW>;
+    constexpr int NCH = Cfg<D>::NCH;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    s.head = (const uint8_t*)head;
+    s.tile_bytes = sL * 2 * kTile;
+    s.row_bytes = (int)(sL * 2);
+    s.nrows = (int)nrows;
+#pragma unroll
+    for (int it = 0; it < T::PER_WAVE; ++it) {
+        const int slot = (wave * T::PER_WAVE + it) * 64 + lane, r = slot / NCH, c = bswz<D>(r, slot % NCH);
+        s.voff[it] = (unsigned)(r * s.row_bytes + c * 16);
+    }
+}
+
+template <int D, int NW>
+__device__ inline void stream_issue(const TileStream<D, NW>& s, int tile, int lds) {
+    using T = TileCopy<D, NW>;
+    const int wave = uni(threadIdx.x >> 6);
+    const int nvalid = min(max(s.nrows - tile * kTile, 0), kTile);
+    const int bytes = uni(nvalid > 0 ? (nvalid - 1) * s.row_bytes + D * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(s.head + tile * s.tile_bytes), 0, bytes, kRsrcFlags);
+#pragma unroll
+    for (int it = 0; it < T::PER_WAVE; ++it) {
+        const int run = wave * T::PER_WAVE + it;
+        if (T::RUNS % NW == 0 || run < T::RUNS)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)(lds + run * 1024), 16, s.voff[it], 0, 0, 0);
+    }
+}
+
+// 64 values of a per-row array (rows past `nrows` read as zero) copied by one
+// wave: lane i's 4 bytes land at byte 4i.
+__device__ inline void stat_issue(const float* head, int nrows, int tile, int lds) {
+    const int r0 = tile * kTile;
+    const int nr = min(max(nrows - r0, 0), kTile);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(head + r0), 0, uni(nr * 4), kRsrcFlags);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)lds, 4, (unsigned)((threadIdx.x & 63) * 4), 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -424,28 +479,39 @@ __device__ inline bool q_next(const BwdLaunch& p, QCursor& c, i64 lb, int m0, in
 // and dV through LDS at the end (rh 0 + rh 1, a fixed order).  Query tiles
 // go through two LDS buffers, each tile's loads issued one tile ahead.
 // ---------------------------------------------------------------------------
-// Copies of one query tile into LDS: its Q and dO rows (rows past q_valid
-// read as zero) and, by waves 0..3, the rows' LSE, delta and key interval
-// (64 values each; rows past Lq read as zero and see nothing).
+// The copies of the query tiles of one query head h of the grouped head hk:
+// its Q and dO rows (rows past q_valid read as zero) and the statistic that
+// wave w % 4 copies (LSE, delta, key interval lo, hi; rows past Lq read as
+// zero and see nothing).
+template <int D, int NW>
+struct QHead {
+    TileStream<D, NW> q, g;
+    const float* stat;
+    int gh;  // the query head within the group these are for
+};
+
+template <int D, int NW>
+__device__ inline void qhead_init(const BwdLaunch& p, QHead<D, NW>& x, int g, i64 b, i64 hk, i64 lb) {
+    const i64 h = hk * p.kv_group + g;
+    stream_init<D, NW>(x.q, (const __bf16*)p.q + b * p.q_sB + h * p.q_sH, p.q_sL, p.mask.q_valid);
+    stream_init<D, NW>(x.g, (const __bf16*)p.dout + b * p.do_sB + h * p.do_sH, p.do_sL, p.mask.q_valid);
+    const int w = uni(threadIdx.x >> 6) & 3;
+    const i64 li = (b * p.H + h) * p.Lq, ri = lb * p.Lq;
+    x.stat = w == 0 ? p.lse + li : w == 1 ? p.delta + li
+           : w == 2 ? (const float*)(p.row_lo + ri) : (const float*)(p.row_hi + ri);
+    x.gh = g;
+}
+
+// Copies of query tile c into LDS: Q and dO rows and, by waves 0..3, the
+// rows' statistics (LSE at st[0..63], delta, lo, hi after it).
 template <int D>
-__device__ inline void kv_issue8(const BwdLaunch& p, const QCursor& c, i64 b, i64 hk, i64 lb, uint8_t* qt,
-                                 uint8_t* gt, float* st) {
-    const i64 h = hk * p.kv_group + c.g;
-    const i64 r0 = (i64)c.m * kTile;
-    const int nq = (int)max((i64)0, min((i64)kTile, p.mask.q_valid - r0));
-    tile_issue<D, 8>((const __bf16*)p.q + b * p.q_sB + r0 * p.q_sL + h * p.q_sH, p.q_sL, nq, lds_opaque(qt));
-    tile_issue<D, 8>((const __bf16*)p.dout + b * p.do_sB + r0 * p.do_sL + h * p.do_sH, p.do_sL, nq,
-                     lds_opaque(gt));
-    const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    if (wave < 4) {
-        const int nr = (int)max((i64)0, min((i64)kTile, p.Lq - r0));
-        const i64 li = (b * p.H + h) * p.Lq + r0, ri = lb * p.Lq + r0;
-        const void* src = wave == 0 ? (const void*)(p.lse + li) : wave == 1 ? (const void*)(p.delta + li)
-                        : wave == 2 ? (const void*)(p.row_lo + ri) : (const void*)(p.row_hi + ri);
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, nr * 4, kRsrcFlags);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_opaque(st + wave * 64), 4,
-                                                 (unsigned)(lane * 4), 0, 0, 0);
-    }
+__device__ inline void kv_issue8(const BwdLaunch& p, QHead<D, 8>& x, const QCursor& c, i64 b, i64 hk, i64 lb,
+                                 int qt, int gt, int st) {
+    if (c.g != x.gh) qhead_init<D, 8>(p, x, c.g, b, hk, lb);
+    stream_issue<D, 8>(x.q, c.m, qt);
+    stream_issue<D, 8>(x.g, c.m, gt);
+    const int wave = uni(threadIdx.x >> 6);
+    if (wave < 4) stat_issue(x.stat, (int)p.Lq, c.m, st + wave * 256);
 }
 
 // Rows rh*32 .. rh*32+31 of one query tile against the wave's 32 keys (K and
@@ -482,6 +548,40 @@ __device__ inline void kv_compute8(const BwdLaunch& p, const uint8_t* qt, const 
         }
         return o;
     };
+    // P and dS of this lane's rows rh*32 + 8g + 4hb + e (slice g)
+    auto slice = [&](const int g) __attribute__((always_inline)) {
+        const int rb = rh * 32 + 8 * g + 4 * hb;
+        const f32x4 L = *(const f32x4*)(st + rb);
+        const f32x4 Dl = *(const f32x4*)(st + 64 + rb);
+        float pv[4], dv4[4];
+        if (masked) {
+            const i32x4 lo = *(const i32x4*)(st + 128 + rb);
+            const i32x4 hi = *(const i32x4*)(st + 192 + rb);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool vis = lo[e] <= key && key < hi[e];
+                const float x = pin(__builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * g + e], sc, -L[e] * kLog2e)));
+                const float d = pin(x * (G[4 * g + e] - Dl[e]));
+                pv[e] = vis ? x : 0.0f;
+                dv4[e] = vis ? d : 0.0f;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * g + e], sc, -L[e] * kLog2e));
+                dv4[e] = pv[e] * (G[4 * g + e] - Dl[e]);
+            }
+        }
+        const uint32_t a0 = pack_bf16x2(pv[0], pv[1]), a1 = pack_bf16x2(pv[2], pv[3]);
+        const uint32_t b0 = pack_bf16x2(dv4[0], dv4[1]), b1 = pack_bf16x2(dv4[2], dv4[3]);
+        if (g & 1) {
+            pp[g >> 1].z = a0; pp[g >> 1].w = a1;
+            pd[g >> 1].z = b0; pd[g >> 1].w = b1;
+        } else {
+            pp[g >> 1].x = a0; pp[g >> 1].y = a1;
+            pd[g >> 1].x = b0; pd[g >> 1].y = b1;
+        }
+    };
     Ops fa[NT];
     static_for<AH>([&](auto ic) { fa[ic.value] = ld(ic.value); });
     static_for<NT>([&](auto ic) {
@@ -495,43 +595,15 @@ __device__ inline void kv_compute8(const BwdLaunch& p, const uint8_t* qt, const 
             if constexpr (w) dk[db] = mfma(fa[i].a, pd[k2], dk[db]);
             else dv[db] = mfma(fa[i].a, pp[k2], dv[db]);
         }
+        // Slices 0 and 1 feed the first half of the update steps; slices 2
+        // and 3, run between those steps, the second.
         if constexpr (i == NS - 1) {
-            // P and dS of this lane's rows rh*32 + 8g + 4hb + e
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int rb = rh * 32 + 8 * g + 4 * hb;
-                const f32x4 L = *(const f32x4*)(st + rb);
-                const f32x4 Dl = *(const f32x4*)(st + 64 + rb);
-                float pv[4], dv4[4];
-                if (masked) {
-                    const i32x4 lo = *(const i32x4*)(st + 128 + rb);
-                    const i32x4 hi = *(const i32x4*)(st + 192 + rb);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const bool vis = lo[e] <= key && key < hi[e];
-                        const float x = pin(__builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * g + e], sc, -L[e] * kLog2e)));
-                        const float d = pin(x * (G[4 * g + e] - Dl[e]));
-                        pv[e] = vis ? x : 0.0f;
-                        dv4[e] = vis ? d : 0.0f;
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * g + e], sc, -L[e] * kLog2e));
-                        dv4[e] = pv[e] * (G[4 * g + e] - Dl[e]);
-                    }
-                }
-                const uint32_t a0 = pack_bf16x2(pv[0], pv[1]), a1 = pack_bf16x2(pv[2], pv[3]);
-                const uint32_t b0 = pack_bf16x2(dv4[0], dv4[1]), b1 = pack_bf16x2(dv4[2], dv4[3]);
-                if (g & 1) {
-                    pp[g >> 1].z = a0; pp[g >> 1].w = a1;
-                    pd[g >> 1].z = b0; pd[g >> 1].w = b1;
-                } else {
-                    pp[g >> 1].x = a0; pp[g >> 1].y = a1;
-                    pd[g >> 1].x = b0; pd[g >> 1].y = b1;
-                }
-            }
+            slice(0);
+            slice(1);
         }
+        if constexpr (i == NS + 1) slice(2);
+        if constexpr (i == NS + NM / 4) slice(3);  // before step NS + NM / 2, the first to use them
+        static_assert(NM / 4 > 1 && NM / 4 < NM / 2, "slices 2 and 3 fall between the first-half update steps");
         __builtin_amdgcn_sched_barrier(0);
     });
 }
@@ -574,7 +646,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv8(const BwdLaunch p) {
     const int m0 = ld_const(p.kfirst, lb * p.nkb + kb), m1 = ld_const(p.klast, lb * p.nkb + kb);
     QCursor cur{0, m0 - 1};
     bool have = m0 <= m1 && q_next(p, cur, lb, m0, m1, k0, k0 + kKeyBlock);
-    if (have) kv_issue8<D>(p, cur, b, hk, lb, qs[0], gs[0], ss[0]);
+    QHead<D, 8> qh;
+    qh.gh = -1;
+    if (have) kv_issue8<D>(p, qh, cur, b, hk, lb, lds_opaque(qs[0]), lds_opaque(gs[0]), lds_opaque(ss[0]));
     int buf = 0;
     while (have) {
         // This wave's copies of buffer `buf` (and of the key tiles) have
@@ -584,7 +658,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv8(const BwdLaunch p) {
         __syncthreads();
         QCursor nxt = cur;
         const bool more = q_next(p, nxt, lb, m0, m1, k0, k0 + kKeyBlock);
-        if (more) kv_issue8<D>(p, nxt, b, hk, lb, qs[buf ^ 1], gs[buf ^ 1], ss[buf ^ 1]);
+        if (more)
+            kv_issue8<D>(p, qh, nxt, b, hk, lb, lds_opaque(qs[buf ^ 1]), lds_opaque(gs[buf ^ 1]),
+                         lds_opaque(ss[buf ^ 1]));
         kv_compute8<D>(p, qs[buf], gs[buf], ss[buf], ks[kg >> 1], vs[kg >> 1], kg & 1, dk, dv, cur, lb, kw0, rh);
         cur = nxt;
         have = more;
@@ -633,34 +709,19 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv8(const BwdLaunch p) {
 // intervals and document ids, stream through LDS.  The element test needs
 // registers that the two-wave form above does not have to spare.
 // ---------------------------------------------------------------------------
-// Copies of one query tile into LDS: its Q and dO rows (rows past q_valid
-// read as zero), and by wave w statistic w of its rows (LSE, delta, key
-// interval lo, hi); with document ids every wave also copies the rows' ids
-// (the same bytes, so each wave's count of copies per tile is the same).
-// Rows past Lq read as zero and see nothing.
+// Copies of query tile c into LDS: Q and dO rows, statistic w by wave w
+// (LSE, delta, key interval lo, hi) and, with document ids, the rows' ids
+// by every wave (the same bytes, so each wave's count of copies per tile is
+// the same).
 template <int D>
-__device__ inline void kv_issue(const BwdLaunch& p, const QCursor& c, i64 b, i64 hk, i64 lb, uint8_t* qt,
-                                uint8_t* gt, float* st) {
-    const i64 h = hk * p.kv_group + c.g;
-    const i64 r0 = (i64)c.m * kTile;
-    const int nq = (int)max((i64)0, min((i64)kTile, p.mask.q_valid - r0));
-    tile_issue<D, 4>((const __bf16*)p.q + b * p.q_sB + r0 * p.q_sL + h * p.q_sH, p.q_sL, nq, lds_opaque(qt));
-    tile_issue<D, 4>((const __bf16*)p.dout + b * p.do_sB + r0 * p.do_sL + h * p.do_sH, p.do_sL, nq,
-                     lds_opaque(gt));
-    const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int nr = (int)max((i64)0, min((i64)kTile, p.Lq - r0));
-    const i64 li = (b * p.H + h) * p.Lq + r0, ri = lb * p.Lq + r0;
-    const void* src = wave == 0 ? (const void*)(p.lse + li) : wave == 1 ? (const void*)(p.delta + li)
-                    : wave == 2 ? (const void*)(p.row_lo + ri) : (const void*)(p.row_hi + ri);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, nr * 4, kRsrcFlags);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_opaque(st + wave * 64), 4, (unsigned)(lane * 4), 0,
-                                             0, 0);
-    if (p.mask.seg_mode == 3) {
-        const __amdgpu_buffer_rsrc_t is =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(p.mask.ids_q + b * p.mask.lq + r0), 0, nr * 4, kRsrcFlags);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(is, (lds_void*)lds_opaque(st + 256), 4, (unsigned)(lane * 4), 0, 0,
-                                                 0);
-    }
+__device__ inline void kv_issue(const BwdLaunch& p, QHead<D, 4>& x, const QCursor& c, i64 b, i64 hk, i64 lb,
+                                int qt, int gt, int st) {
+    if (c.g != x.gh) qhead_init<D, 4>(p, x, c.g, b, hk, lb);
+    stream_issue<D, 4>(x.q, c.m, qt);
+    stream_issue<D, 4>(x.g, c.m, gt);
+    stat_issue(x.stat, (int)p.Lq, c.m, st + uni(threadIdx.x >> 6) * 256);
+    if (p.mask.seg_mode == 3)
+        stat_issue((const float*)(p.mask.ids_q + b * p.mask.lq), (int)p.Lq, c.m, st + 1024);
 }
 
 // One 64-row query tile against the wave's 32 keys: 64 matrix-core steps in
@@ -802,10 +863,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
     QCursor ahead = cur;  // the last tile whose copies were issued
     bool more = have;
     int n_after = 0;      // tiles issued beyond cur
-    if (have) kv_issue<D>(p, cur, b, hk, lb, qs[0], gs[0], ss[0]);
+    QHead<D, 4> qh;
+    qh.gh = -1;
+    if (have) kv_issue<D>(p, qh, cur, b, hk, lb, lds_opaque(qs[0]), lds_opaque(gs[0]), lds_opaque(ss[0]));
     if (more) more = q_next(p, ahead, lb, m0, m1, k0, k0 + kKeyBlock);
     if (more) {
-        kv_issue<D>(p, ahead, b, hk, lb, qs[1], gs[1], ss[1]);
+        kv_issue<D>(p, qh, ahead, b, hk, lb, lds_opaque(qs[1]), lds_opaque(gs[1]), lds_opaque(ss[1]));
         ++n_after;
     }
     int buf = 0;
@@ -819,7 +882,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
         if (more) more = q_next(p, ahead, lb, m0, m1, k0, k0 + kKeyBlock);
         if (more) {
             const int fb = buf == 0 ? kRing - 1 : buf - 1;
-            kv_issue<D>(p, ahead, b, hk, lb, qs[fb], gs[fb], ss[fb]);
+            kv_issue<D>(p, qh, ahead, b, hk, lb, lds_opaque(qs[fb]), lds_opaque(gs[fb]), lds_opaque(ss[fb]));
             ++n_after;
         }
         kv_compute<D>(p, qs[buf], gs[buf], ss[buf], kf, vf, dk, dv, cur, kw0, key_id, key_res, dpat);
@@ -885,97 +948,112 @@ __device__ inline bool t_next(const BwdLaunch& p, TCursor& c, int t_lo, int t_hi
     }
 }
 
-// One 64-key tile against the wave's 32 rows, with two waves per SIMD (the
-// other wave's products cover this one's element-wise work): each 32-key
-// half runs its S^T and dP^T products (the two chains alternating), its dS
-// and its own dQ^T products in turn, so only one half's scores and dS are
-// live; LDS operand reads run two steps ahead.
+// One 64-key tile against the wave's 32 rows.  Per 32-key half kb: the S^T
+// and dP^T products (the two chains alternating), the element-wise dS, and
+// the dQ^T products.  The halves are interleaved so that each half's
+// element-wise work (in four slices of four keys) runs between matrix-core
+// products of the other phase instead of stalling the wave:
+//   steps [0, NS)            S^T, dP^T of half 0
+//   steps [NS, 2NS)          S^T, dP^T of half 1      + slices of half 0
+//   steps [2NS, 2NS+NH)      dQ^T of half 0           + slices of half 1
+//   steps [2NS+NH, 2NS+2NH)  dQ^T of half 1
+// (NS = 2 D/16, NH = 2 D/32).  LDS operand reads run three steps ahead (two
+// with element tests).
 template <int D, bool XM>
 __device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const uint8_t* vt, const FragOffs<D>& fo,
-                                     const uint4 (&qf)[D / 16], const uint8_t* gw, f32x16 (&dq)[D / 32],
-                                     int t, int full_lo, int full_hi, int lo, int hi, float lse2, float delt, i64 b,
-                                     int row, int row_id, int row_res, unsigned dpat) {
+                                 const uint4 (&qf)[D / 16], const uint8_t* gw, f32x16 (&dq)[D / 32], int t,
+                                 int full_lo, int full_hi, int lo, int hi, float lse2, float delt, i64 b, int row,
+                                 int row_id, int row_res, unsigned dpat) {
     using C = Cfg<D>;
-    constexpr int NS = 2 * C::NDS, NH = 2 * C::NDB, NP = NS + NH;  // steps per half
-    constexpr int AH = 2;                                            // read-ahead
+    constexpr int NS = 2 * C::NDS, NH = 2 * C::NDB, NT = 2 * NS + 2 * NH;
+    constexpr int AH = XM ? 2 : 3;  // read-ahead (the element tests leave registers for two)
     const int lane = threadIdx.x & 63, hb = lane >> 5;
     const int j0 = t * kTile;
     const bool masked = XM || !(full_lo <= j0 && j0 + kTile <= full_hi);
     const float sc = p.scale * kLog2e;
-    static_for<2>([&](auto kbc) {
-        constexpr int kb = decltype(kbc)::value;
-        f32x16 S = {}, G = {};
-        uint4 pd[2];
-        // step i: the A operand, and for the dP^T steps dO's fragment as B
-        struct Ops {
-            uint4 a, b;
-        };
-        auto ld = [&](const int i) __attribute__((always_inline)) {
-            Ops o;
-            o.b = uint4{0, 0, 0, 0};
-            if (i < NS) {
-                if (i & 1) {
-                    o.a = frag_rows_at<D>(vt, fo, kb, i >> 1);
-                    o.b = frag_rows_at<D>(gw, fo, 0, i >> 1);
-                } else {
-                    o.a = frag_rows_at<D>(kt, fo, kb, i >> 1);
-                }
-            } else {
-                const int m = i - NS;
-                o.a = frag_cols_at<D>(kt, fo, kb * 2 + m / C::NDB, m % C::NDB);
-            }
-            return o;
-        };
-        Ops fa[NP];
-        static_for<AH>([&](auto ic) { fa[ic.value] = ld(ic.value); });
-        static_for<NP>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            if constexpr (i + AH < NP) fa[i + AH] = ld(i + AH);
-            if constexpr (i < NS) {
-                if constexpr (i & 1) G = mfma(fa[i].a, fa[i].b, G);
-                else S = mfma(fa[i].a, qf[i >> 1], S);
-            } else {
-                constexpr int m = i - NS;
-                dq[m % C::NDB] = mfma(fa[i].a, pd[m / C::NDB], dq[m % C::NDB]);
-            }
-            if constexpr (i == NS - 1) {
-                // dilated band: the half's keys congruent to row - kv_offset mod g
-                unsigned kbits = ~0u;
-                if (XM && masked && p.mask.dilation > 1) kbits = dil_bits(row_res, j0 + kb * 32, p.mask.dilation, dpat);
+    // Without element tests dP^T accumulates onto the row's -delta, so it
+    // ends as dP - delta (one subtraction per element less; the element-test
+    // form keeps the registers that takes and subtracts).
+    const float g0 = XM ? 0.0f : -delt, dsub = XM ? delt : 0.0f;
+    f32x16 S[2] = {f32x16{}, f32x16{}}, G[2];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    float dsv[4];
-                    int kid[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                    if (XM && masked && p.mask.seg_mode == 3) key_ids8(p, b, j0 + kb * 32 + 8 * g, kid);
+    for (int i = 0; i < 16; ++i) { G[0][i] = g0; G[1][i] = g0; }
+    uint4 pd[2][2];  // bf16 dS^T per half and 16-key step
+    // dilated band: the keys of half kb congruent to row - kv_offset mod g
+    unsigned kbits[2] = {~0u, ~0u};
+    if (XM && masked && p.mask.dilation > 1) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * g + e], sc, -lse2));
-                        float d = pin(x * (G[4 * g + e] - delt));
-                        if (masked) {
-                            const int key = j0 + kb * 32 + 8 * g + 4 * hb + e;
-                            bool vis = lo <= key && key < hi;
-                            if (XM) {
-                                vis = vis && ((kbits >> (8 * g + 4 * hb + e)) & 1u);
-                                if (p.mask.seg_mode == 3) vis = vis && row_id == (hb ? kid[4 + e] : kid[e]);
-                            }
-                            d = vis ? d : 0.0f;
-                        }
-                        dsv[e] = d;
-                    }
-                    const uint32_t a0 = pack_bf16x2(dsv[0], dsv[1]), a1 = pack_bf16x2(dsv[2], dsv[3]);
-                    if (g & 1) { pd[g >> 1].z = a0; pd[g >> 1].w = a1; }
-                    else { pd[g >> 1].x = a0; pd[g >> 1].y = a1; }
-                }
+        for (int kb = 0; kb < 2; ++kb) kbits[kb] = dil_bits(row_res, j0 + kb * 32, p.mask.dilation, dpat);
+    }
+    // step i: the A operand, and for the dP^T steps dO's fragment as B
+    struct Ops {
+        uint4 a, b;
+    };
+    auto ld = [&](const int i) __attribute__((always_inline)) {
+        Ops o;
+        o.b = uint4{0, 0, 0, 0};
+        if (i < 2 * NS) {
+            const int kb = i / NS, j = i % NS;
+            if (j & 1) {
+                o.a = frag_rows_at<D>(vt, fo, kb, j >> 1);
+                o.b = frag_rows_at<D>(gw, fo, 0, j >> 1);
+            } else {
+                o.a = frag_rows_at<D>(kt, fo, kb, j >> 1);
             }
-            __builtin_amdgcn_sched_barrier(0);
-        });
+        } else {
+            const int m = i - 2 * NS, kb = m / NH, j = m % NH;
+            o.a = frag_cols_at<D>(kt, fo, kb * 2 + j / C::NDB, j % C::NDB);
+        }
+        return o;
+    };
+    // dS^T of keys j0 + kb*32 + 8g + 4hb + e (e = 0..3) for this lane's row
+    auto slice = [&](const int kb, const int g) __attribute__((always_inline)) {
+        float dsv[4];
+        int kid[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (XM && masked && p.mask.seg_mode == 3) key_ids8(p, b, j0 + kb * 32 + 8 * g, kid);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][4 * g + e], sc, -lse2));
+            float d = pin(x * (XM ? G[kb][4 * g + e] - dsub : G[kb][4 * g + e]));
+            if (masked) {
+                const int key = j0 + kb * 32 + 8 * g + 4 * hb + e;
+                bool vis = lo <= key && key < hi;
+                if (XM) {
+                    vis = vis && ((kbits[kb] >> (8 * g + 4 * hb + e)) & 1u);
+                    if (p.mask.seg_mode == 3) vis = vis && row_id == (hb ? kid[4 + e] : kid[e]);
+                }
+                d = vis ? d : 0.0f;
+            }
+            dsv[e] = d;
+        }
+        const uint32_t a0 = pack_bf16x2(dsv[0], dsv[1]), a1 = pack_bf16x2(dsv[2], dsv[3]);
+        if (g & 1) { pd[kb][g >> 1].z = a0; pd[kb][g >> 1].w = a1; }
+        else { pd[kb][g >> 1].x = a0; pd[kb][g >> 1].y = a1; }
+    };
+    Ops fa[NT];
+    static_for<AH>([&](auto ic) { fa[ic.value] = ld(ic.value); });
+    static_for<NT>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + AH < NT) fa[i + AH] = ld(i + AH);
+        if constexpr (i < 2 * NS) {
+            constexpr int kb = i / NS, j = i % NS;
+            if constexpr (j & 1) G[kb] = mfma(fa[i].a, fa[i].b, G[kb]);
+            else S[kb] = mfma(fa[i].a, qf[j >> 1], S[kb]);
+        } else {
+            constexpr int m = i - 2 * NS, kb = m / NH, j = m % NH;
+            dq[j % C::NDB] = mfma(fa[i].a, pd[kb][j / C::NDB], dq[j % C::NDB]);
+        }
+        if constexpr (i >= NS && i < 2 * NS && (i - NS) % (NS / 4) == NS / 4 - 1) slice(0, (i - NS) / (NS / 4));
+        if constexpr (i >= 2 * NS && i < 2 * NS + NH && (i - 2 * NS) % (NH / 4) == NH / 4 - 1)
+            slice(1, (i - 2 * NS) / (NH / 4));
+        __builtin_amdgcn_sched_barrier(0);
     });
 }
 
 // 32 rows (rows past nvalid read as zero) copied by one wave into LDS in the
 // layout of tile_issue (the first half of a 64-row tile).
 template <int D>
-__device__ inline void rows_issue_wave(const __bf16* base, i64 sL, int nvalid, uint8_t* lds) {
+__device__ inline void rows_issue_wave(const __bf16* base, i64 sL, int nvalid, int lds) {
     constexpr int NCH = Cfg<D>::NCH, RUNS = 32 * D * 2 / 1024;
     const int lane = threadIdx.x & 63;
     const int bytes = uni(nvalid > 0 ? (int)(((i64)(nvalid - 1) * sL + D) * 2) : 0);
@@ -983,7 +1061,7 @@ __device__ inline void rows_issue_wave(const __bf16* base, i64 sL, int nvalid, u
 #pragma unroll
     for (int run = 0; run < RUNS; ++run) {
         const int slot = run * 64 + lane, r = slot / NCH, c = bswz<D>(r, slot % NCH);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + run * 1024), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)(lds + run * 1024), 16,
                                                  (unsigned)(r * sL * 2 + c * 16), 0, 0, 0);
     }
 }
@@ -996,16 +1074,16 @@ struct DqWalk {
     bool more;     // ahead is a tile of the walk
     int n_after;   // tiles issued beyond cur
     int t_lo, t_hi;
-    const __bf16* kbase;
-    const __bf16* vbase;
 };
 
+// Copies of key tile t of the key/value head (K and V rows from kbase, vbase).
 template <int D, int NW>
-__device__ inline void dq_issue(const BwdLaunch& p, const DqWalk& w, uint8_t* kl, uint8_t* vl) {
-    const i64 j0 = (i64)w.ahead.t * kTile;
+__device__ inline void dq_issue(const BwdLaunch& p, const __bf16* kbase, const __bf16* vbase, int t, int kl,
+                                int vl) {
+    const i64 j0 = (i64)t * kTile;
     const int nk = (int)max((i64)0, min((i64)kTile, p.mask.kv_valid - j0));
-    tile_issue<D, NW>(w.kbase + j0 * p.k_sL, p.k_sL, nk, lds_opaque(kl));
-    tile_issue<D, NW>(w.vbase + j0 * p.v_sL, p.v_sL, nk, lds_opaque(vl));
+    tile_issue<D, NW>(kbase + j0 * p.k_sL, p.k_sL, nk, kl);
+    tile_issue<D, NW>(vbase + j0 * p.v_sL, p.v_sL, nk, vl);
 }
 
 template <int D, int G, bool XM, int NW>
@@ -1094,18 +1172,18 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
     DqWalk wk;
     wk.t_lo = t_lo;
     wk.t_hi = t_hi;
-    wk.kbase = (const __bf16*)p.k + b * p.k_sB + hk * p.k_sH;
-    wk.vbase = (const __bf16*)p.v + b * p.v_sB + hk * p.v_sH;
+    const __bf16* kbase = (const __bf16*)p.k + b * p.k_sB + hk * p.k_sH;
+    const __bf16* vbase = (const __bf16*)p.v + b * p.v_sB + hk * p.v_sH;
     wk.cur = TCursor{-1, 0};
     bool have = t_next(p, wk.cur, t_lo, t_hi);
     wk.ahead = wk.cur;
     wk.more = have;
     wk.n_after = 0;
     // (the barrier above: every wave has read red before ring[2] is copied to)
-    if (have) dq_issue<D, NW>(p, wk, ring[0][0], ring[0][1]);
+    if (have) dq_issue<D, NW>(p, kbase, vbase, wk.ahead.t, lds_opaque(ring[0][0]), lds_opaque(ring[0][1]));
     if (wk.more) wk.more = t_next(p, wk.ahead, t_lo, t_hi);
     if (wk.more) {
-        dq_issue<D, NW>(p, wk, ring[1][0], ring[1][1]);
+        dq_issue<D, NW>(p, kbase, vbase, wk.ahead.t, lds_opaque(ring[1][0]), lds_opaque(ring[1][1]));
         ++wk.n_after;
     }
     const FragOffs<D> fo = frag_offsets<D>();
@@ -1116,7 +1194,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
         if (wk.more) wk.more = t_next(p, wk.ahead, t_lo, t_hi);
         if (wk.more) {
             const int nb = buf == 0 ? 2 : buf - 1;
-            dq_issue<D, NW>(p, wk, ring[nb][0], ring[nb][1]);
+            dq_issue<D, NW>(p, kbase, vbase, wk.ahead.t, lds_opaque(ring[nb][0]), lds_opaque(ring[nb][1]));
             ++wk.n_after;
         }
         q_compute<D, XM>(p, ring[buf][0], ring[buf][1], fo, qf, gw, dq, wk.cur.t, full_lo, full_hi, lo, hi, lse2,

@@ -56,8 +56,9 @@ __device__ inline void wait_vmcnt(int n) {
     }
 }
 
-// The LDS address of a copy into LDS (a buffer load with an LDS
-// destination) as a value that the compiler cannot trace to an LDS object.
+// The LDS address (byte offset) of a copy into LDS (a buffer load with an
+// LDS destination) as a value that the compiler cannot trace to an LDS
+// object.
 // Before an LDS read the compiler waits for every copy it cannot tell apart
 // from the read's object; a ring indexed at run time is one such object, so
 // the first read of a tile would wait for the copies of the tiles ahead,
@@ -65,10 +66,10 @@ __device__ inline void wait_vmcnt(int n) {
 // kernel orders each tile's copies before its reads itself: wait_vmcnt for
 // the wave's own copies, then the workgroup barrier.  (The empty asm keeps a
 // known buffer address from being folded back to its LDS object.)
-__device__ inline uint8_t* lds_opaque(void* p) {
-    unsigned a = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)p);
+__device__ inline int lds_opaque(const void* p) {
+    int a = __builtin_amdgcn_readfirstlane((int)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p);
     asm volatile("" : "+s"(a));
-    return (uint8_t*)(__attribute__((address_space(3))) uint8_t*)(uintptr_t)a;
+    return a;
 }
 
 // Keys visible to query row i of batch element b lie in one interval

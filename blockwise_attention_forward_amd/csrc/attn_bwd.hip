@@ -948,105 +948,98 @@ __device__ inline bool t_next(const BwdLaunch& p, TCursor& c, int t_lo, int t_hi
     }
 }
 
-// One 64-key tile against the wave's 32 rows.  Per 32-key half kb: the S^T
-// and dP^T products (the two chains alternating), the element-wise dS, and
-// the dQ^T products.  The halves are interleaved so that each half's
-// element-wise work (in four slices of four keys) runs between matrix-core
-// products of the other phase instead of stalling the wave:
-//   steps [0, NS)            S^T, dP^T of half 0
-//   steps [NS, 2NS)          S^T, dP^T of half 1      + slices of half 0
-//   steps [2NS, 2NS+NH)      dQ^T of half 0           + slices of half 1
-//   steps [2NS+NH, 2NS+2NH)  dQ^T of half 1
-// (NS = 2 D/16, NH = 2 D/32).  LDS operand reads run three steps ahead (two
-// with element tests).
+// One 64-key tile against the wave's 32 rows, with two waves per SIMD (the
+// other wave's products cover this one's element-wise work): each 32-key
+// half runs its S^T and dP^T products (the two chains alternating), its dS
+// and its own dQ^T products in turn, so only one half's scores and dS are
+// live.  LDS operand reads run three steps ahead (two with element tests,
+// whose registers that takes).  Interleaving one half's element-wise work
+// with the other half's products measured slower (the two halves' scores
+// then share the registers).
 template <int D, bool XM>
 __device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const uint8_t* vt, const FragOffs<D>& fo,
-                                 const uint4 (&qf)[D / 16], const uint8_t* gw, f32x16 (&dq)[D / 32], int t,
-                                 int full_lo, int full_hi, int lo, int hi, float lse2, float delt, i64 b, int row,
-                                 int row_id, int row_res, unsigned dpat) {
+                                     const uint4 (&qf)[D / 16], const uint8_t* gw, f32x16 (&dq)[D / 32],
+                                     int t, int full_lo, int full_hi, int lo, int hi, float lse2, float delt, i64 b,
+                                     int row, int row_id, int row_res, unsigned dpat) {
     using C = Cfg<D>;
-    constexpr int NS = 2 * C::NDS, NH = 2 * C::NDB, NT = 2 * NS + 2 * NH;
-    constexpr int AH = XM ? 2 : 3;  // read-ahead (the element tests leave registers for two)
+    constexpr int NS = 2 * C::NDS, NH = 2 * C::NDB, NP = NS + NH;  // steps per half
+    constexpr int AH = XM ? 2 : 3;                                  // read-ahead
     const int lane = threadIdx.x & 63, hb = lane >> 5;
     const int j0 = t * kTile;
     const bool masked = XM || !(full_lo <= j0 && j0 + kTile <= full_hi);
     const float sc = p.scale * kLog2e;
-    // Without element tests dP^T accumulates onto the row's -delta, so it
-    // ends as dP - delta (one subtraction per element less; the element-test
-    // form keeps the registers that takes and subtracts).
-    const float g0 = XM ? 0.0f : -delt, dsub = XM ? delt : 0.0f;
-    f32x16 S[2] = {f32x16{}, f32x16{}}, G[2];
+    static_for<2>([&](auto kbc) {
+        constexpr int kb = decltype(kbc)::value;
+        // Without element tests dP^T accumulates onto the row's -delta, so it
+        // ends as dP - delta (one subtraction per element less).
+        const float g0 = XM ? 0.0f : -delt, dsub = XM ? delt : 0.0f;
+        f32x16 S = {}, G;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { G[0][i] = g0; G[1][i] = g0; }
-    uint4 pd[2][2];  // bf16 dS^T per half and 16-key step
-    // dilated band: the keys of half kb congruent to row - kv_offset mod g
-    unsigned kbits[2] = {~0u, ~0u};
-    if (XM && masked && p.mask.dilation > 1) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) kbits[kb] = dil_bits(row_res, j0 + kb * 32, p.mask.dilation, dpat);
-    }
-    // step i: the A operand, and for the dP^T steps dO's fragment as B
-    struct Ops {
-        uint4 a, b;
-    };
-    auto ld = [&](const int i) __attribute__((always_inline)) {
-        Ops o;
-        o.b = uint4{0, 0, 0, 0};
-        if (i < 2 * NS) {
-            const int kb = i / NS, j = i % NS;
-            if (j & 1) {
-                o.a = frag_rows_at<D>(vt, fo, kb, j >> 1);
-                o.b = frag_rows_at<D>(gw, fo, 0, j >> 1);
-            } else {
-                o.a = frag_rows_at<D>(kt, fo, kb, j >> 1);
-            }
-        } else {
-            const int m = i - 2 * NS, kb = m / NH, j = m % NH;
-            o.a = frag_cols_at<D>(kt, fo, kb * 2 + j / C::NDB, j % C::NDB);
-        }
-        return o;
-    };
-    // dS^T of keys j0 + kb*32 + 8g + 4hb + e (e = 0..3) for this lane's row
-    auto slice = [&](const int kb, const int g) __attribute__((always_inline)) {
-        float dsv[4];
-        int kid[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (XM && masked && p.mask.seg_mode == 3) key_ids8(p, b, j0 + kb * 32 + 8 * g, kid);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][4 * g + e], sc, -lse2));
-            float d = pin(x * (XM ? G[kb][4 * g + e] - dsub : G[kb][4 * g + e]));
-            if (masked) {
-                const int key = j0 + kb * 32 + 8 * g + 4 * hb + e;
-                bool vis = lo <= key && key < hi;
-                if (XM) {
-                    vis = vis && ((kbits[kb] >> (8 * g + 4 * hb + e)) & 1u);
-                    if (p.mask.seg_mode == 3) vis = vis && row_id == (hb ? kid[4 + e] : kid[e]);
+        for (int i = 0; i < 16; ++i) G[i] = g0;
+        uint4 pd[2];
+        // step i: the A operand, and for the dP^T steps dO's fragment as B
+        struct Ops {
+            uint4 a, b;
+        };
+        auto ld = [&](const int i) __attribute__((always_inline)) {
+            Ops o;
+            o.b = uint4{0, 0, 0, 0};
+            if (i < NS) {
+                if (i & 1) {
+                    o.a = frag_rows_at<D>(vt, fo, kb, i >> 1);
+                    o.b = frag_rows_at<D>(gw, fo, 0, i >> 1);
+                } else {
+                    o.a = frag_rows_at<D>(kt, fo, kb, i >> 1);
                 }
-                d = vis ? d : 0.0f;
+            } else {
+                const int m = i - NS;
+                o.a = frag_cols_at<D>(kt, fo, kb * 2 + m / C::NDB, m % C::NDB);
             }
-            dsv[e] = d;
-        }
-        const uint32_t a0 = pack_bf16x2(dsv[0], dsv[1]), a1 = pack_bf16x2(dsv[2], dsv[3]);
-        if (g & 1) { pd[kb][g >> 1].z = a0; pd[kb][g >> 1].w = a1; }
-        else { pd[kb][g >> 1].x = a0; pd[kb][g >> 1].y = a1; }
-    };
-    Ops fa[NT];
-    static_for<AH>([&](auto ic) { fa[ic.value] = ld(ic.value); });
-    static_for<NT>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        if constexpr (i + AH < NT) fa[i + AH] = ld(i + AH);
-        if constexpr (i < 2 * NS) {
-            constexpr int kb = i / NS, j = i % NS;
-            if constexpr (j & 1) G[kb] = mfma(fa[i].a, fa[i].b, G[kb]);
-            else S[kb] = mfma(fa[i].a, qf[j >> 1], S[kb]);
-        } else {
-            constexpr int m = i - 2 * NS, kb = m / NH, j = m % NH;
-            dq[j % C::NDB] = mfma(fa[i].a, pd[kb][j / C::NDB], dq[j % C::NDB]);
-        }
-        if constexpr (i >= NS && i < 2 * NS && (i - NS) % (NS / 4) == NS / 4 - 1) slice(0, (i - NS) / (NS / 4));
-        if constexpr (i >= 2 * NS && i < 2 * NS + NH && (i - 2 * NS) % (NH / 4) == NH / 4 - 1)
-            slice(1, (i - 2 * NS) / (NH / 4));
-        __builtin_amdgcn_sched_barrier(0);
+            return o;
+        };
+        Ops fa[NP];
+        static_for<AH>([&](auto ic) { fa[ic.value] = ld(ic.value); });
+        static_for<NP>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (i + AH < NP) fa[i + AH] = ld(i + AH);
+            if constexpr (i < NS) {
+                if constexpr (i & 1) G = mfma(fa[i].a, fa[i].b, G);
+                else S = mfma(fa[i].a, qf[i >> 1], S);
+            } else {
+                constexpr int m = i - NS;
+                dq[m % C::NDB] = mfma(fa[i].a, pd[m / C::NDB], dq[m % C::NDB]);
+            }
+            if constexpr (i == NS - 1) {
+                // dilated band: the half's keys congruent to row - kv_offset mod g
+                unsigned kbits = ~0u;
+                if (XM && masked && p.mask.dilation > 1) kbits = dil_bits(row_res, j0 + kb * 32, p.mask.dilation, dpat);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float dsv[4];
+                    int kid[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                    if (XM && masked && p.mask.seg_mode == 3) key_ids8(p, b, j0 + kb * 32 + 8 * g, kid);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * g + e], sc, -lse2));
+                        float d = pin(x * (XM ? G[4 * g + e] - dsub : G[4 * g + e]));
+                        if (masked) {
+                            const int key = j0 + kb * 32 + 8 * g + 4 * hb + e;
+                            bool vis = lo <= key && key < hi;
+                            if (XM) {
+                                vis = vis && ((kbits >> (8 * g + 4 * hb + e)) & 1u);
+                                if (p.mask.seg_mode == 3) vis = vis && row_id == (hb ? kid[4 + e] : kid[e]);
+                            }
+                            d = vis ? d : 0.0f;
+                        }
+                        dsv[e] = d;
+                    }
+                    const uint32_t a0 = pack_bf16x2(dsv[0], dsv[1]), a1 = pack_bf16x2(dsv[2], dsv[3]);
+                    if (g & 1) { pd[g >> 1].z = a0; pd[g >> 1].w = a1; }
+                    else { pd[g >> 1].x = a0; pd[g >> 1].y = a1; }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
     });
 }
 

@@ -101,6 +101,30 @@ def test_masks_against_oracle(mi, D, dtype):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+# Masks whose rows see many keys: the plain bf16 launch runs whole blocks
+# (rows with few keys, as in the suite above, run half blocks).
+LONG_ROW_MASKS = [
+    {},
+    {"causal": True, "kv_offset": 300 - 9000},
+    {"causal": True, "kv_offset": 300 - 9000, "window": 5000, "dilation": 3},
+    {"window": 2500, "kv_offset": 4000},
+]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mi", range(len(LONG_ROW_MASKS)))
+def test_whole_block_launch_long_rows(mi, D):
+    mask = LONG_ROW_MASKS[mi]
+    B, H, Lq, Lk = 1, 2, 300, 9000
+    q = _rand((B, Lq, H, D), 40 + mi, torch.bfloat16)
+    k = _rand((B, Lk, H, D), 50 + mi, torch.bfloat16)
+    v = _rand((B, Lk, H, D), 60 + mi, torch.bfloat16)
+    scale = 1 / math.sqrt(D)
+    o_ref, l_ref = oracle_attention(q, k, v, mask, scale)
+    o, l = bw.bwa_attn_fwd(q, k, v, mask, scale=scale)
+    assert_close(o, l, o_ref, l_ref, torch.bfloat16, f"whole blocks {mask}")
+
+
 @pytest.mark.parametrize("Lq,Lk", [(1, 1), (5, 700), (700, 5), (129, 64), (64, 129)])
 def test_shapes(Lq, Lk):
     B, H, D = 1, 2, 128

@@ -93,13 +93,15 @@ class Timer:
 
 
 def _source_sha(fname="attn_fwd.hip"):
-    """Hash of a kernel source file without comments and blank lines."""
-    p = os.path.join(ROOT, "blockwise_attention_forward_amd", "csrc", fname)
+    """Hash of a kernel source file and the shared device header it includes,
+    without comments and blank lines."""
     code = []
-    for line in open(p, encoding="utf-8"):
-        line = line.split("//", 1)[0].rstrip()
-        if line:
-            code.append(line)
+    for f in (fname, "internal.h"):
+        p = os.path.join(ROOT, "blockwise_attention_forward_amd", "csrc", f)
+        for line in open(p, encoding="utf-8"):
+            line = line.split("//", 1)[0].rstrip()
+            if line:
+                code.append(line)
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
@@ -116,6 +118,28 @@ def _traffic(kernel_key, fname="attn_fwd.hip"):
     if not rec or rec.get("source_sha") != _source_sha(fname):
         return None
     return rec.get("bytes_per_launch")
+
+
+def _warm_up(torch, step, args):
+    """Untimed steps before the timed ones.  Unless --warmup fixes the count,
+    run at least 3 and keep going until 300 ms have passed: the device's
+    clocks take that long to settle under sustained load, and a call of a
+    fraction of a millisecond would otherwise be timed on a cold device.
+    Unless --steps fixes it, the timed count is then at least 20 steps and
+    enough for about 200 ms.  Sets args.warmup and args.steps to the counts
+    used."""
+    t = time.perf_counter()
+    n = 0
+    while (n < args.warmup) if args.warmup is not None else (n < 3 or time.perf_counter() - t < 0.3):
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t) * 1e3 / max(n, 1)
+    args.warmup = n
+    if args.steps is None:
+        args.steps = int(min(5000, max(20, math.ceil(200.0 / max(ms, 1e-3)))))
 
 
 def _launcher(torch, bw, launch, q, lk, units):
@@ -355,6 +379,24 @@ def _measured_ceilings(torch):
         b.record()
         torch.cuda.synchronize()
         out["mfma_lds_bf16_TFLOPs"] = round(256 * 8 * iters * 8 * 32768.0 * 3 / (a.elapsed_time(b) * 1e-3) / 1e12, 1)
+        # LDS operand bytes per product against matrix-core rate: the share of
+        # the nominal peak with n 16-byte reads and m pairs of transposing
+        # 8-byte reads per two products (the forward reads (1, 1), dK/dV (2, 1))
+        m = lib.bwa_probe_mfma_lds_mix
+        m.restype = ctypes.c_int32
+        m.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        mix = {}
+        mi = iters // 10
+        for nb, nt in ((2, 0), (0, 2), (1, 1), (2, 1), (4, 0), (3, 1), (6, 0)):
+            assert m(nb, nt, mi // 10, 256, lsink.data_ptr(), stream) == 0
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            assert m(nb, nt, mi, 256, lsink.data_ptr(), stream) == 0
+            b.record()
+            torch.cuda.synchronize()
+            tf = 256 * 8 * mi * 8 * 32768.0 / (a.elapsed_time(b) * 1e-3) / 1e12
+            mix[f"{(nb + nt) / 2:g}KB_per_product_b128x{nb}_trpair_x{nt}"] = round(100.0 * tf / PEAK_BF16_TFLOPS, 1)
+        out["mfma_lds_mix_pct_of_peak"] = mix
         # streaming probes: the merge's mix (4 bytes read per byte written)
         # and a read-only pass (the bound's mix), 1 GiB of reads each
         g = lib.bwa_probe_stream
@@ -407,8 +449,10 @@ def _blas_threads():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: at least 20, and enough for about 200 ms)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: at least 3, and until 300 ms have passed)")
     ap.add_argument("--workload", default="dit_share",
                     choices=["dit_share", "varlen", "window", "long_causal", "long_causal_packed",
                              "prefix_lm", "dilated_sliding_window", "document", "two_sided_window"],
@@ -448,9 +492,7 @@ def main():
         sys.exit(2)
     W = setup_dit_share(torch, bw, synth, args.launch)
     timer = Timer(torch)
-    for _ in range(args.warmup):
-        W["step"]()
-    torch.cuda.synchronize()
+    _warm_up(torch, W["step"], args)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record()
@@ -475,7 +517,7 @@ def main():
 
     # the step with the hops chained by the carried partial (no merge launch)
     t3 = Timer(torch)
-    for _ in range(args.warmup):
+    for _ in range(min(args.warmup, 3)):  # the device is warm by now
         W["step_carry"]()
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -593,9 +635,7 @@ def run_single(args, torch, bw, synth):
     if args.which == "bwd":
         W = setup_backward(torch, bw, synth, W)
     timer = Timer(torch)
-    for _ in range(args.warmup):
-        W["step"]()
-    torch.cuda.synchronize()
+    _warm_up(torch, W["step"], args)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
     for _ in range(args.steps):

@@ -45,6 +45,19 @@ int32_t bwa_probe_mfma_bf16(int32_t iters, int32_t blocks, float* sink, uint64_t
 int32_t bwa_probe_mfma_lds_bf16(int32_t iters, int32_t blocks, float* sink, void* stream);
 
 /*
+ * The same with a chosen mix of LDS operand reads per pair of products:
+ * n_b128 reads of 16 bytes per lane (1 KB each) and n_tr pairs of
+ * transposing 8-byte reads (ds_read_b64_tr_b16, 1 KB per pair), combined into
+ * the A operand of both products of the pair; each wavefront runs `iters`
+ * iterations of 4 pairs.  Work = blocks * 8 * iters * 8 * 32768 FLOP.  The
+ * mixes built are (n_b128, n_tr) = (2, 0), (0, 2), (1, 1), (2, 1), (4, 0),
+ * (3, 1) and (6, 0).  Returns 0, 1 for bad arguments or a mix not built, or
+ * 8 when the launch fails.
+ */
+int32_t bwa_probe_mfma_lds_mix(int32_t n_b128, int32_t n_tr, int32_t iters, int32_t blocks, float* sink,
+                               void* stream);
+
+/*
  * HBM streaming probe: the bandwidth the device sustains for a mix of
  * reads and writes.  src (device, 16-byte aligned) holds `ratio` streams of
  * `chunks` 16-byte chunks each; every chunk is read once with non-temporal

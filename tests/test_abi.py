@@ -47,12 +47,18 @@ def test_probe_library_exports_and_rejects_bad_arguments():
         pytest.skip("libbwa_probe.so not built")
     lib = ctypes.CDLL(PROBE_LIB)
     names = _declared(PROBE_HEADER)
-    assert names == ["bwa_probe_mfma_bf16", "bwa_probe_mfma_lds_bf16", "bwa_probe_stream"]
+    assert names == ["bwa_probe_mfma_bf16", "bwa_probe_mfma_lds_bf16", "bwa_probe_mfma_lds_mix", "bwa_probe_stream"]
     h = lib.bwa_probe_mfma_lds_bf16
     h.restype = ctypes.c_int32
     h.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     assert h(0, 1, ctypes.c_void_p(16), None) == 1 and h(1, 0, ctypes.c_void_p(16), None) == 1
     assert h(1, 1, None, None) == 1
+    m = lib.bwa_probe_mfma_lds_mix
+    m.restype = ctypes.c_int32
+    m.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    assert m(1, 1, 0, 1, ctypes.c_void_p(16), None) == 1 and m(1, 1, 1, 0, ctypes.c_void_p(16), None) == 1
+    assert m(1, 1, 1, 1, None, None) == 1
+    assert m(5, 0, 1, 1, ctypes.c_void_p(16), None) == 1  # a mix that is not built
     g = lib.bwa_probe_stream
     g.restype = ctypes.c_int32
     g.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,

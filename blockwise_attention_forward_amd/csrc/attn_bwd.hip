@@ -268,6 +268,16 @@ __device__ inline int wave_max(int x) {
     return x;
 }
 
+// Filter bit of a document id (a multiplicative hash onto 32 bits): two
+// tiles whose filters share no bit hold no row and key of one document.
+__device__ inline unsigned doc_bit(int id) { return 1u << (((unsigned)id * 0x9E3779B1u) >> 27); }
+
+__device__ inline unsigned wave_or(unsigned x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x |= (unsigned)__shfl_xor((int)x, o);
+    return x;
+}
+
 // Store 16 values of a 32x32 result tile held as C[d][n] (n = this lane's
 // row or key): d = db*32 + 8*g + 4*hb + 0..3 for g = 0..3.
 template <int G>
@@ -413,6 +423,10 @@ __global__ __launch_bounds__(64) void bwd_qtiles_kernel(const BwdLaunch p) {
     const int env_lo = wave_min(ne ? lo : kBig), env_hi = wave_max(ne ? hi : 0);
     const int full_lo = wave_max(ne ? lo : kBig), full_hi = wave_min(ne ? hi : -1);
     if (lane == 0) p.qsum[t] = int4{env_lo, env_hi, full_lo, full_hi};
+    if (p.mask.seg_mode == 3) {
+        const unsigned f = wave_or(ne ? doc_bit(p.mask.ids_q[lb * p.mask.lq + row]) : 0u);
+        if (lane == 0) p.qbloom[t] = f;
+    }
     if (env_lo < env_hi) {
         const int n0 = env_lo / kKeyBlock, n1 = (env_hi - 1) / kKeyBlock;
         for (int n = n0 + lane; n <= n1; n += 64) {
@@ -420,6 +434,16 @@ __global__ __launch_bounds__(64) void bwd_qtiles_kernel(const BwdLaunch p) {
             atomicMax(&p.klast[lb * p.nkb + n], (int)m);
         }
     }
+}
+
+// Document ids: one wave per 64-key tile, the filter of its keys' ids below
+// kv_valid.
+__global__ __launch_bounds__(64) void bwd_ktiles_kernel(const BwdLaunch p) {
+    const i64 t = blockIdx.x;  // over list_batch * nkt
+    const i64 lb = t / p.nkt, n = t % p.nkt;
+    const i64 key = n * kTile + threadIdx.x;
+    const unsigned f = wave_or(key < p.mask.kv_valid ? doc_bit(p.mask.ids_kv[lb * p.mask.lk + key]) : 0u);
+    if (threadIdx.x == 0) p.kbloom[t] = f;
 }
 
 // delta[b,h,i] = dO_i . O_i in fp32: D/8 lanes per row, 8 elements each.
@@ -458,16 +482,27 @@ struct QCursor {
     int g, m;  // query head within the group, query tile
 };
 
-// Next (g, m) after c whose rows' envelope meets keys [k0, k1).
-__device__ inline bool q_next(const BwdLaunch& p, QCursor& c, i64 lb, int m0, int m1, int k0, int k1) {
+// Next (g, m) after c whose rows' envelope meets keys [k0, k1) and, with
+// document ids, whose filter meets the key block's filter kf.
+template <bool DOC>
+__device__ inline bool q_next(const BwdLaunch& p, QCursor& c, i64 lb, int m0, int m1, int k0, int k1, unsigned kf) {
     for (;;) {
         if (++c.m > m1) {
             c.m = m0;
             if (++c.g >= p.kv_group) return false;
         }
         const i32x4 s = ld_const((const i32x4*)p.qsum, lb * p.nqt + c.m);
-        if (s[0] < k1 && s[1] > k0) return true;
+        if (s[0] < k1 && s[1] > k0 && (!DOC || (ld_const(p.qbloom, lb * p.nqt + c.m) & kf) != 0))
+            return true;
     }
+}
+
+// The filter of the document ids of keys [k0, k0 + 128).
+__device__ inline unsigned key_block_filter(const BwdLaunch& p, i64 lb, int k0) {
+    const i64 t = k0 / kTile;
+    unsigned f = ld_const(p.kbloom, lb * p.nkt + t);
+    if (t + 1 < p.nkt) f |= ld_const(p.kbloom, lb * p.nkt + t + 1);
+    return f;
 }
 
 // ---------------------------------------------------------------------------
@@ -644,8 +679,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv8(const BwdLaunch p) {
     for (int d = 0; d < C::NDB; ++d) { dk[d] = f32x16{}; dv[d] = f32x16{}; }
 
     const int m0 = ld_const(p.kfirst, lb * p.nkb + kb), m1 = ld_const(p.klast, lb * p.nkb + kb);
+    const unsigned kfb = ~0u;  // no document ids here
     QCursor cur{0, m0 - 1};
-    bool have = m0 <= m1 && q_next(p, cur, lb, m0, m1, k0, k0 + kKeyBlock);
+    bool have = m0 <= m1 && q_next<false>(p, cur, lb, m0, m1, k0, k0 + kKeyBlock, kfb);
     QHead<D, 8> qh;
     qh.gh = -1;
     if (have) kv_issue8<D>(p, qh, cur, b, hk, lb, lds_opaque(qs[0]), lds_opaque(gs[0]), lds_opaque(ss[0]));
@@ -657,7 +693,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv8(const BwdLaunch p) {
         wait_loads();
         __syncthreads();
         QCursor nxt = cur;
-        const bool more = q_next(p, nxt, lb, m0, m1, k0, k0 + kKeyBlock);
+        const bool more = q_next<false>(p, nxt, lb, m0, m1, k0, k0 + kKeyBlock, kfb);
         if (more)
             kv_issue8<D>(p, qh, nxt, b, hk, lb, lds_opaque(qs[buf ^ 1]), lds_opaque(gs[buf ^ 1]),
                          lds_opaque(ss[buf ^ 1]));
@@ -715,12 +751,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv8(const BwdLaunch p) {
 // the same).
 template <int D>
 __device__ inline void kv_issue(const BwdLaunch& p, QHead<D, 4>& x, const QCursor& c, i64 b, i64 hk, i64 lb,
-                                int qt, int gt, int st) {
+                                int qt, int gt, int st, bool doc) {
     if (c.g != x.gh) qhead_init<D, 4>(p, x, c.g, b, hk, lb);
     stream_issue<D, 4>(x.q, c.m, qt);
     stream_issue<D, 4>(x.g, c.m, gt);
     stat_issue(x.stat, (int)p.Lq, c.m, st + uni(threadIdx.x >> 6) * 256);
-    if (p.mask.seg_mode == 3)
+    if (doc)
         stat_issue((const float*)(p.mask.ids_q + b * p.mask.lq), (int)p.Lq, c.m, st + 1024);
 }
 
@@ -735,7 +771,7 @@ __device__ inline void kv_issue(const BwdLaunch& p, QHead<D, 4>& x, const QCurso
 // (NS = 2 D/16 score steps, NM = 4 D/32 update steps per chunk).  S and dP
 // alternate between their two accumulation chains; LDS operand reads run
 // kAhead steps ahead of their use.
-template <int D>
+template <int D, bool DOC>
 __device__ inline void kv_compute(const BwdLaunch& p, const uint8_t* qt, const uint8_t* gt, const float* st,
                                   const uint4 (&kf)[D / 16], const uint4 (&vf)[D / 16], f32x16 (&dk)[D / 32],
                                   f32x16 (&dv)[D / 32], const QCursor& c, int kw0, int key_id, int key_res,
@@ -772,12 +808,12 @@ __device__ inline void kv_compute(const BwdLaunch& p, const uint8_t* qt, const u
         const i32x4 lo = *(const i32x4*)(st + 128 + rb);
         const i32x4 hi = *(const i32x4*)(st + 192 + rb);
         i32x4 rid = {0, 0, 0, 0};
-        if (p.mask.seg_mode == 3) rid = *(const i32x4*)(st + 256 + rb);
+        if (DOC) rid = *(const i32x4*)(st + 256 + rb);
         float pv[4], dv4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             bool vis = lo[e] <= key && key < hi[e] && ((rbits[rc] >> (8 * g + 4 * hb + e)) & 1u);
-            if (p.mask.seg_mode == 3) vis = vis && rid[e] == key_id;
+            if (DOC) vis = vis && rid[e] == key_id;
             const float x = pin(__builtin_amdgcn_exp2f(__builtin_fmaf(S[rc][4 * g + e], sc, -L[e] * kLog2e)));
             const float d = pin(x * (G[rc][4 * g + e] - Dl[e]));
             pv[e] = vis ? x : 0.0f;
@@ -816,7 +852,8 @@ __device__ inline void kv_compute(const BwdLaunch& p, const uint8_t* qt, const u
     });
 }
 
-template <int D, int G>
+// DOC: document ids (the tile filters apply).
+template <int D, int G, bool DOC>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
     using C = Cfg<D>;
     // Three tile buffers; a tile's copies into LDS are issued two tiles
@@ -846,29 +883,31 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
     f32x16 dk[C::NDB], dv[C::NDB];
 #pragma unroll
     for (int d = 0; d < C::NDB; ++d) { dk[d] = f32x16{}; dv[d] = f32x16{}; }
-    const int key_id = (p.mask.seg_mode == 3 && key < p.Lk) ? p.mask.ids_kv[b * p.mask.lk + key] : -1;
+    const int key_id = (DOC && key < p.Lk) ? p.mask.ids_kv[b * p.mask.lk + key] : -1;
     // (key + kv_offset) mod g: the rows congruent to it see the key
     const int key_res = p.mask.dilation > 1
                             ? (int)((((i64)key + p.mask.kv_offset) % p.mask.dilation + p.mask.dilation) % p.mask.dilation)
                             : 0;
     const unsigned dpat = p.mask.dilation > 1 ? dil_pattern(p.mask.dilation) : 0u;
+    const unsigned kfw = DOC && kw0 / kTile < p.nkt ? ld_const(p.kbloom, lb * p.nkt + kw0 / kTile) : 0u;
     wait_loads();
 
     const int m0 = ld_const(p.kfirst, lb * p.nkb + kb), m1 = ld_const(p.klast, lb * p.nkb + kb);
+    const unsigned kfb = DOC ? key_block_filter(p, lb, k0) : ~0u;
     QCursor cur{0, m0 - 1};
-    bool have = m0 <= m1 && q_next(p, cur, lb, m0, m1, k0, k0 + kKeyBlock);
+    bool have = m0 <= m1 && q_next<DOC>(p, cur, lb, m0, m1, k0, k0 + kKeyBlock, kfb);
     // Prologue: copies of the first two tiles.
     constexpr int LOADS = 2 * TileCopy<D, 4>::PER_WAVE + 1;  // per wave and tile, plus the document ids
-    const int loads = LOADS + (p.mask.seg_mode == 3 ? 1 : 0);
+    const int loads = LOADS + (DOC ? 1 : 0);
     QCursor ahead = cur;  // the last tile whose copies were issued
     bool more = have;
     int n_after = 0;      // tiles issued beyond cur
     QHead<D, 4> qh;
     qh.gh = -1;
-    if (have) kv_issue<D>(p, qh, cur, b, hk, lb, lds_opaque(qs[0]), lds_opaque(gs[0]), lds_opaque(ss[0]));
-    if (more) more = q_next(p, ahead, lb, m0, m1, k0, k0 + kKeyBlock);
+    if (have) kv_issue<D>(p, qh, cur, b, hk, lb, lds_opaque(qs[0]), lds_opaque(gs[0]), lds_opaque(ss[0]), DOC);
+    if (more) more = q_next<DOC>(p, ahead, lb, m0, m1, k0, k0 + kKeyBlock, kfb);
     if (more) {
-        kv_issue<D>(p, qh, ahead, b, hk, lb, lds_opaque(qs[1]), lds_opaque(gs[1]), lds_opaque(ss[1]));
+        kv_issue<D>(p, qh, ahead, b, hk, lb, lds_opaque(qs[1]), lds_opaque(gs[1]), lds_opaque(ss[1]), DOC);
         ++n_after;
     }
     int buf = 0;
@@ -879,14 +918,17 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
         wait_vmcnt(n_after * loads);
         __syncthreads();
         const int nb = buf == kRing - 1 ? 0 : buf + 1;
-        if (more) more = q_next(p, ahead, lb, m0, m1, k0, k0 + kKeyBlock);
+        if (more) more = q_next<DOC>(p, ahead, lb, m0, m1, k0, k0 + kKeyBlock, kfb);
         if (more) {
             const int fb = buf == 0 ? kRing - 1 : buf - 1;
-            kv_issue<D>(p, qh, ahead, b, hk, lb, lds_opaque(qs[fb]), lds_opaque(gs[fb]), lds_opaque(ss[fb]));
+            kv_issue<D>(p, qh, ahead, b, hk, lb, lds_opaque(qs[fb]), lds_opaque(gs[fb]), lds_opaque(ss[fb]), DOC);
             ++n_after;
         }
-        kv_compute<D>(p, qs[buf], gs[buf], ss[buf], kf, vf, dk, dv, cur, kw0, key_id, key_res, dpat);
-        have = q_next(p, cur, lb, m0, m1, k0, k0 + kKeyBlock);
+        // With document ids a wave skips a tile whose filter misses its keys' (a
+        // 32-key half of one key tile: that tile's filter).
+        if (!DOC || (ld_const(p.qbloom, lb * p.nqt + cur.m) & kfw) != 0)
+            kv_compute<D, DOC>(p, qs[buf], gs[buf], ss[buf], kf, vf, dk, dv, cur, kw0, key_id, key_res, dpat);
+        have = q_next<DOC>(p, cur, lb, m0, m1, k0, k0 + kKeyBlock, kfb);
         if (have) --n_after;
         buf = nb;
     }
@@ -925,7 +967,7 @@ __device__ inline int order_tile(const BwdLaunch& p, int r) {
     }
 }
 
-__device__ inline bool t_next(const BwdLaunch& p, TCursor& c, int t_lo, int t_hi) {
+__device__ __attribute__((always_inline)) inline bool t_step(const BwdLaunch& p, TCursor& c, int t_lo, int t_hi) {
     if (p.order == BWA_ORDER_ASC) {
         if (c.r < 0) c.r = t_lo - 1;
         if (++c.r >= t_hi) return false;
@@ -948,6 +990,17 @@ __device__ inline bool t_next(const BwdLaunch& p, TCursor& c, int t_lo, int t_hi
     }
 }
 
+// The next key tile of the walk whose filter, with document ids, meets the
+// filter qf of the block's rows.
+template <bool DOC>
+__device__ inline bool t_next(const BwdLaunch& p, TCursor& c, int t_lo, int t_hi, i64 lb, unsigned qf) {
+    if (!DOC) return t_step(p, c, t_lo, t_hi);
+    for (;;) {
+        if (!t_step(p, c, t_lo, t_hi)) return false;
+        if ((ld_const(p.kbloom, lb * p.nkt + c.t) & qf) != 0) return true;
+    }
+}
+
 // One 64-key tile against the wave's 32 rows, with two waves per SIMD (the
 // other wave's products cover this one's element-wise work): each 32-key
 // half runs its S^T and dP^T products (the two chains alternating), its dS
@@ -956,7 +1009,7 @@ __device__ inline bool t_next(const BwdLaunch& p, TCursor& c, int t_lo, int t_hi
 // whose registers that takes).  Interleaving one half's element-wise work
 // with the other half's products measured slower (the two halves' scores
 // then share the registers).
-template <int D, bool XM>
+template <int D, bool XM, bool DOC>
 __device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const uint8_t* vt, const FragOffs<D>& fo,
                                      const uint4 (&qf)[D / 16], const uint8_t* gw, f32x16 (&dq)[D / 32],
                                      int t, int full_lo, int full_hi, int lo, int hi, float lse2, float delt, i64 b,
@@ -1017,7 +1070,7 @@ __device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const ui
                 for (int g = 0; g < 4; ++g) {
                     float dsv[4];
                     int kid[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                    if (XM && masked && p.mask.seg_mode == 3) key_ids8(p, b, j0 + kb * 32 + 8 * g, kid);
+                    if (DOC && masked) key_ids8(p, b, j0 + kb * 32 + 8 * g, kid);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * g + e], sc, -lse2));
@@ -1027,7 +1080,7 @@ __device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const ui
                             bool vis = lo <= key && key < hi;
                             if (XM) {
                                 vis = vis && ((kbits >> (8 * g + 4 * hb + e)) & 1u);
-                                if (p.mask.seg_mode == 3) vis = vis && row_id == (hb ? kid[4 + e] : kid[e]);
+                                if (DOC) vis = vis && row_id == (hb ? kid[4 + e] : kid[e]);
                             }
                             d = vis ? d : 0.0f;
                         }
@@ -1079,7 +1132,9 @@ __device__ inline void dq_issue(const BwdLaunch& p, const __bf16* kbase, const _
     tile_issue<D, NW>(vbase + j0 * p.v_sL, p.v_sL, nk, vl);
 }
 
-template <int D, int G, bool XM, int NW>
+// XM: element tests; DOC: document ids (with XM; the tile filters apply).
+// (XM without DOC: a dilated band.)
+template <int D, int G, bool XM, int NW, bool DOC>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
     using C = Cfg<D>;
     constexpr int RB = NW * 32;  // rows per workgroup
@@ -1112,7 +1167,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
         lse2 = p.lse[li] * kLog2e;
         delt = p.delta[li];
     }
-    const int row_id = (XM && p.mask.seg_mode == 3 && row_ok) ? p.mask.ids_q[b * p.mask.lq + row] : -1;
+    const int row_id = (DOC && row_ok) ? p.mask.ids_q[b * p.mask.lq + row] : -1;
     // (row - kv_offset) mod g: the keys congruent to it are seen
     const int row_res = (XM && p.mask.dilation > 1)
                             ? (int)((((i64)row - p.mask.kv_offset) % p.mask.dilation + p.mask.dilation) % p.mask.dilation)
@@ -1162,19 +1217,31 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
     // wave's copies of the tile, then at the barrier for every wave's (after
     // which every wave is also done with the previous tile's buffer, the one
     // the next copy overwrites); issue the copies two tiles ahead; compute.
+    // Document ids: the filters of the block's rows and of this wave's rows
+    // (a 32-row half of one query tile: that tile's filter).
+    unsigned qfb = ~0u, qfw = ~0u;
+    if (DOC) {
+        const i64 m0 = qb * RB / kTile;
+        qfb = 0u;
+#pragma unroll
+        for (int i = 0; i < RB / kTile; ++i)
+            if (m0 + i < p.nqt) qfb |= ld_const(p.qbloom, lb * p.nqt + m0 + i);
+        const i64 mw = (qb * RB + wave * 32) / kTile;
+        qfw = mw < p.nqt ? ld_const(p.qbloom, lb * p.nqt + mw) : 0u;
+    }
     DqWalk wk;
     wk.t_lo = t_lo;
     wk.t_hi = t_hi;
     const __bf16* kbase = (const __bf16*)p.k + b * p.k_sB + hk * p.k_sH;
     const __bf16* vbase = (const __bf16*)p.v + b * p.v_sB + hk * p.v_sH;
     wk.cur = TCursor{-1, 0};
-    bool have = t_next(p, wk.cur, t_lo, t_hi);
+    bool have = t_next<DOC>(p, wk.cur, t_lo, t_hi, lb, qfb);
     wk.ahead = wk.cur;
     wk.more = have;
     wk.n_after = 0;
     // (the barrier above: every wave has read red before ring[2] is copied to)
     if (have) dq_issue<D, NW>(p, kbase, vbase, wk.ahead.t, lds_opaque(ring[0][0]), lds_opaque(ring[0][1]));
-    if (wk.more) wk.more = t_next(p, wk.ahead, t_lo, t_hi);
+    if (wk.more) wk.more = t_next<DOC>(p, wk.ahead, t_lo, t_hi, lb, qfb);
     if (wk.more) {
         dq_issue<D, NW>(p, kbase, vbase, wk.ahead.t, lds_opaque(ring[1][0]), lds_opaque(ring[1][1]));
         ++wk.n_after;
@@ -1184,15 +1251,16 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
     while (have) {
         wait_vmcnt(wk.n_after * LOADS);
         __syncthreads();
-        if (wk.more) wk.more = t_next(p, wk.ahead, t_lo, t_hi);
+        if (wk.more) wk.more = t_next<DOC>(p, wk.ahead, t_lo, t_hi, lb, qfb);
         if (wk.more) {
             const int nb = buf == 0 ? 2 : buf - 1;
             dq_issue<D, NW>(p, kbase, vbase, wk.ahead.t, lds_opaque(ring[nb][0]), lds_opaque(ring[nb][1]));
             ++wk.n_after;
         }
-        q_compute<D, XM>(p, ring[buf][0], ring[buf][1], fo, qf, gw, dq, wk.cur.t, full_lo, full_hi, lo, hi, lse2,
-                         delt, b, row, row_id, row_res, dpat);
-        have = t_next(p, wk.cur, t_lo, t_hi);
+        if (!DOC || (ld_const(p.kbloom, lb * p.nkt + wk.cur.t) & qfw) != 0)
+            q_compute<D, XM, DOC>(p, ring[buf][0], ring[buf][1], fo, qf, gw, dq, wk.cur.t, full_lo, full_hi, lo, hi,
+                             lse2, delt, b, row, row_id, row_res, dpat);
+        have = t_next<DOC>(p, wk.cur, t_lo, t_hi, lb, qfb);
         if (have) --wk.n_after;
         buf = buf == 2 ? 0 : buf + 1;
     }
@@ -1206,11 +1274,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
 
 template <int D, int G>
 hipError_t launch_dg(const BwdLaunch& a, hipStream_t stream) {
-    const bool xm = a.mask.dilation > 1 || a.mask.seg_mode == 3;
+    const bool doc = a.mask.seg_mode == 3, xm = a.mask.dilation > 1 || doc;
     const i64 nkb_total = (i64)a.B * a.Hk * a.nkb;
     if (nkb_total > 0) {
         // element masks: one wave per SIMD; interval masks: two
-        if (xm) hipLaunchKernelGGL((attn_bwd_dkdv<D, G>), dim3((unsigned)nkb_total), dim3(256), 0, stream, a);
+        if (doc) hipLaunchKernelGGL((attn_bwd_dkdv<D, G, true>), dim3((unsigned)nkb_total), dim3(256), 0, stream, a);
+        else if (xm) hipLaunchKernelGGL((attn_bwd_dkdv<D, G, false>), dim3((unsigned)nkb_total), dim3(256), 0, stream, a);
         else hipLaunchKernelGGL((attn_bwd_dkdv8<D, G>), dim3((unsigned)nkb_total), dim3(512), 0, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1218,10 +1287,12 @@ hipError_t launch_dg(const BwdLaunch& a, hipStream_t stream) {
     constexpr int NW = kDqWaves;
     const i64 nqb_total = (i64)a.B * a.H * ((a.Lq + 32 * NW - 1) / (32 * NW));
     if (nqb_total > 0) {
-        if (xm)
-            hipLaunchKernelGGL((attn_bwd_dq<D, G, true, NW>), dim3((unsigned)nqb_total), dim3(64 * NW), 0, stream, a);
+        if (doc)
+            hipLaunchKernelGGL((attn_bwd_dq<D, G, true, NW, true>), dim3((unsigned)nqb_total), dim3(64 * NW), 0, stream, a);
+        else if (xm)
+            hipLaunchKernelGGL((attn_bwd_dq<D, G, true, NW, false>), dim3((unsigned)nqb_total), dim3(64 * NW), 0, stream, a);
         else
-            hipLaunchKernelGGL((attn_bwd_dq<D, G, false, NW>), dim3((unsigned)nqb_total), dim3(64 * NW), 0, stream, a);
+            hipLaunchKernelGGL((attn_bwd_dq<D, G, false, NW, false>), dim3((unsigned)nqb_total), dim3(64 * NW), 0, stream, a);
     }
     return hipGetLastError();
 }
@@ -1233,6 +1304,8 @@ hipError_t launch_d(const BwdLaunch& a, hipStream_t stream) {
     if (rows > 0) hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, a);
     if (a.list_batch * a.nqt > 0)
         hipLaunchKernelGGL(bwd_qtiles_kernel, dim3((unsigned)(a.list_batch * a.nqt)), dim3(64), 0, stream, a);
+    if (a.mask.seg_mode == 3 && a.list_batch * a.nkt > 0)
+        hipLaunchKernelGGL(bwd_ktiles_kernel, dim3((unsigned)(a.list_batch * a.nkt)), dim3(64), 0, stream, a);
     const i64 drows = (i64)a.B * a.Lq * a.H;
     if (drows > 0) {
         const i64 blocks = (drows * (D / 8) + 255) / 256;
@@ -1254,8 +1327,9 @@ static i64 pad256(i64 x) { return (x + 255) / 256 * 256; }
 
 i64 bwd_workspace_bytes(i64 B, i64 H, i64 Lq, i64 Lk, i64 list_batch) {
     const i64 nqt = (Lq + kTile - 1) / kTile, nkb = (Lk + kKeyBlock - 1) / kKeyBlock;
+    const i64 nkt = (Lk + kTile - 1) / kTile;
     return pad256(B * H * Lq * 4) + 2 * pad256(list_batch * Lq * 4) + pad256(list_batch * nqt * 16) +
-           2 * pad256(list_batch * nkb * 4);
+           2 * pad256(list_batch * nkb * 4) + pad256(list_batch * nqt * 4) + pad256(list_batch * nkt * 4);
 }
 
 void bwd_workspace_layout(BwdLaunch& a, void* ws) {
@@ -1268,7 +1342,9 @@ void bwd_workspace_layout(BwdLaunch& a, void* ws) {
     a.row_hi = (int*)w; w += pad256(a.list_batch * a.Lq * 4);
     a.qsum = (int4*)w; w += pad256(a.list_batch * a.nqt * 16);
     a.kfirst = (int*)w; w += pad256(a.list_batch * a.nkb * 4);
-    a.klast = (int*)w;
+    a.klast = (int*)w; w += pad256(a.list_batch * a.nkb * 4);
+    a.qbloom = (unsigned*)w; w += pad256(a.list_batch * a.nqt * 4);
+    a.kbloom = (unsigned*)w;
 }
 
 }  // namespace bwa

@@ -245,6 +245,12 @@ struct BwdLaunch {
     float* delta;       // [B][H][Lq]
     int* row_lo; int* row_hi;  // [list_batch][Lq]
     int4* qsum;         // [list_batch][nqt]: envelope lo, hi; common part lo, hi
+    // Document ids only: 32-bit filters of the ids of each 64-row query tile's
+    // rows that see keys, and of each 64-key tile's keys below kv_valid
+    // (bit hash(id) set); a tile pair whose filters share no bit has no
+    // (row, key) pair of one document.
+    unsigned* qbloom;  // [list_batch][nqt]
+    unsigned* kbloom;  // [list_batch][nkt]
     int* kfirst; int* klast;   // [list_batch][nkb]: query tiles meeting the key block
     i64 list_batch, nqt, nkb, nkt;
     MaskDev mask;

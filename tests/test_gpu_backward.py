@@ -149,6 +149,33 @@ def test_edge_sizes(Lq, Lk):
             assert torch.count_nonzero(dq) == 0 and torch.count_nonzero(dk) == 0 and torch.count_nonzero(dv) == 0
 
 
+def _doc_runs(L, seed, max_run, n_ids):
+    """Document ids in runs of 1..max_run tokens, each run's id drawn from
+    n_ids values (a document's runs are not contiguous)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ids = []
+    while len(ids) < L:
+        ids += [int(rng.integers(0, n_ids))] * int(rng.integers(1, max_run + 1))
+    return np.array(ids[:L], dtype=np.int32)
+
+
+@pytest.mark.parametrize("max_run,n_ids", [(100, 12), (40, 1000), (160, 3)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_document_tile_filters(max_run, n_ids, D):
+    # Runs longer and shorter than a 32-row wave, a 64-row tile and a 128-key
+    # block, with few or many distinct ids (many: 64-bit filters collide), so
+    # that waves, tiles and key blocks skip some tiles and keep the others;
+    # q_valid and kv_valid cut the last runs.  Every element against the oracle.
+    B, L, H = 2, 700, 2
+    q, k, v, do = _inputs(B, L, L, H, H, D, 61 + D + max_run)
+    ids = np.stack([_doc_runs(L, 7 + b + max_run, max_run, n_ids) for b in range(B)])
+    for extra in ({}, {"causal": True, "q_valid": 650, "kv_valid": 600}):
+        mask = {"segment_ids_q": ids, "segment_ids_kv": ids, "documents": True, **extra}
+        dq, dk, dv = _run(q, k, v, do, mask, D ** -0.5)
+        torch.cuda.synchronize()
+        _check_full(q, k, v, do, mask, D ** -0.5, dq, dk, dv, True, False, f"docs {max_run}/{n_ids} {extra}")
+
+
 def test_padding_garbage_does_not_leak():
     # rows past q_valid and keys past kv_valid hold NaN: they must not reach
     # any gradient (they are read as zeros and masked)

@@ -63,6 +63,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -272,6 +273,8 @@ __device__ inline int wave_max(int x) {
 // tiles whose filters share no bit hold no row and key of one document.
 __device__ inline unsigned doc_bit(int id) { return 1u << (((unsigned)id * 0x9E3779B1u) >> 27); }
 
+typedef unsigned long long u64;
+
 __device__ inline unsigned wave_or(unsigned x) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) x |= (unsigned)__shfl_xor((int)x, o);
@@ -424,8 +427,16 @@ __global__ __launch_bounds__(64) void bwd_qtiles_kernel(const BwdLaunch p) {
     const int full_lo = wave_max(ne ? lo : kBig), full_hi = wave_min(ne ? hi : -1);
     if (lane == 0) p.qsum[t] = int4{env_lo, env_hi, full_lo, full_hi};
     if (p.mask.seg_mode == 3) {
-        const unsigned f = wave_or(ne ? doc_bit(p.mask.ids_q[lb * p.mask.lq + row]) : 0u);
-        if (lane == 0) p.qbloom[t] = f;
+        const int id = ne ? p.mask.ids_q[lb * p.mask.lq + row] : 0;
+        const unsigned f = wave_or(ne ? doc_bit(id) : 0u);
+        const u64 seen = __builtin_amdgcn_ballot_w64(ne);
+        const int id0 = __shfl(id, seen ? __builtin_ctzll(seen) : 0);
+        const bool one = seen != 0 && __builtin_amdgcn_ballot_w64(ne && id != id0) == 0;
+        if (lane == 0) {
+            p.qbloom[t] = f;
+            p.qdoc[2 * t] = one ? 1 : 0;
+            p.qdoc[2 * t + 1] = one ? id0 : 0;
+        }
     }
     if (env_lo < env_hi) {
         const int n0 = env_lo / kKeyBlock, n1 = (env_hi - 1) / kKeyBlock;
@@ -442,8 +453,17 @@ __global__ __launch_bounds__(64) void bwd_ktiles_kernel(const BwdLaunch p) {
     const i64 t = blockIdx.x;  // over list_batch * nkt
     const i64 lb = t / p.nkt, n = t % p.nkt;
     const i64 key = n * kTile + threadIdx.x;
-    const unsigned f = wave_or(key < p.mask.kv_valid ? doc_bit(p.mask.ids_kv[lb * p.mask.lk + key]) : 0u);
-    if (threadIdx.x == 0) p.kbloom[t] = f;
+    const bool in = key < p.mask.kv_valid;
+    const int id = in ? p.mask.ids_kv[lb * p.mask.lk + key] : 0;
+    const unsigned f = wave_or(in ? doc_bit(id) : 0u);
+    const u64 seen = __builtin_amdgcn_ballot_w64(in);
+    const int id0 = __shfl(id, 0);
+    const bool one = seen != 0 && __builtin_amdgcn_ballot_w64(in && id != id0) == 0;
+    if (threadIdx.x == 0) {
+        p.kbloom[t] = f;
+        p.kdoc[2 * t] = one ? 1 : 0;
+        p.kdoc[2 * t + 1] = one ? id0 : 0;
+    }
 }
 
 // delta[b,h,i] = dO_i . O_i in fp32: D/8 lanes per row, 8 elements each.
@@ -775,7 +795,7 @@ template <int D, bool DOC>
 __device__ inline void kv_compute(const BwdLaunch& p, const uint8_t* qt, const uint8_t* gt, const float* st,
                                   const uint4 (&kf)[D / 16], const uint4 (&vf)[D / 16], f32x16 (&dk)[D / 32],
                                   f32x16 (&dv)[D / 32], const QCursor& c, int kw0, int key_id, int key_res,
-                                  unsigned dpat) {
+                                  unsigned dpat, bool masked) {
     using C = Cfg<D>;
     constexpr int NS = 2 * C::NDS, NM = 4 * C::NDB, NT = 2 * NS + 2 * NM;
     const int lane = threadIdx.x & 63, l32 = lane & 31, hb = lane >> 5;
@@ -797,7 +817,7 @@ __device__ inline void kv_compute(const BwdLaunch& p, const uint8_t* qt, const u
     // dilated band the rows that see the key are those congruent to
     // key + kv_offset modulo g: a bit per row of the 32-row chunk.
     unsigned rbits[2] = {~0u, ~0u};
-    if (p.mask.dilation > 1) {
+    if (masked && p.mask.dilation > 1) {
 #pragma unroll
         for (int rc = 0; rc < 2; ++rc) rbits[rc] = dil_bits(key_res, c.m * kTile + rc * 32, p.mask.dilation, dpat);
     }
@@ -805,19 +825,27 @@ __device__ inline void kv_compute(const BwdLaunch& p, const uint8_t* qt, const u
         const int rb = rc * 32 + 8 * g + 4 * hb;
         const f32x4 L = *(const f32x4*)(st + rb);
         const f32x4 Dl = *(const f32x4*)(st + 64 + rb);
-        const i32x4 lo = *(const i32x4*)(st + 128 + rb);
-        const i32x4 hi = *(const i32x4*)(st + 192 + rb);
-        i32x4 rid = {0, 0, 0, 0};
-        if (DOC) rid = *(const i32x4*)(st + 256 + rb);
         float pv[4], dv4[4];
+        if (masked) {
+            const i32x4 lo = *(const i32x4*)(st + 128 + rb);
+            const i32x4 hi = *(const i32x4*)(st + 192 + rb);
+            i32x4 rid = {0, 0, 0, 0};
+            if (DOC) rid = *(const i32x4*)(st + 256 + rb);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            bool vis = lo[e] <= key && key < hi[e] && ((rbits[rc] >> (8 * g + 4 * hb + e)) & 1u);
-            if (DOC) vis = vis && rid[e] == key_id;
-            const float x = pin(__builtin_amdgcn_exp2f(__builtin_fmaf(S[rc][4 * g + e], sc, -L[e] * kLog2e)));
-            const float d = pin(x * (G[rc][4 * g + e] - Dl[e]));
-            pv[e] = vis ? x : 0.0f;
-            dv4[e] = vis ? d : 0.0f;
+            for (int e = 0; e < 4; ++e) {
+                bool vis = lo[e] <= key && key < hi[e] && ((rbits[rc] >> (8 * g + 4 * hb + e)) & 1u);
+                if (DOC) vis = vis && rid[e] == key_id;
+                const float x = pin(__builtin_amdgcn_exp2f(__builtin_fmaf(S[rc][4 * g + e], sc, -L[e] * kLog2e)));
+                const float d = pin(x * (G[rc][4 * g + e] - Dl[e]));
+                pv[e] = vis ? x : 0.0f;
+                dv4[e] = vis ? d : 0.0f;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rc][4 * g + e], sc, -L[e] * kLog2e));
+                dv4[e] = pv[e] * (G[rc][4 * g + e] - Dl[e]);
+            }
         }
         const uint32_t a0 = pack_bf16x2(pv[0], pv[1]), a1 = pack_bf16x2(pv[2], pv[3]);
         const uint32_t b0 = pack_bf16x2(dv4[0], dv4[1]), b1 = pack_bf16x2(dv4[2], dv4[3]);
@@ -890,6 +918,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
                             : 0;
     const unsigned dpat = p.mask.dilation > 1 ? dil_pattern(p.mask.dilation) : 0u;
     const unsigned kfw = DOC && kw0 / kTile < p.nkt ? ld_const(p.kbloom, lb * p.nkt + kw0 / kTile) : 0u;
+    // whether the wave's keys below kv_valid share one document id (kid_w)
+    const int kid_w = uni(key_id);
+    const bool kone = DOC && __builtin_amdgcn_ballot_w64(key_in && key_id != kid_w) == 0;
     wait_loads();
 
     const int m0 = ld_const(p.kfirst, lb * p.nkb + kb), m1 = ld_const(p.klast, lb * p.nkb + kb);
@@ -926,8 +957,17 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdLaunch p) {
         }
         // With document ids a wave skips a tile whose filter misses its keys' (a
         // 32-key half of one key tile: that tile's filter).
-        if (!DOC || (ld_const(p.qbloom, lb * p.nqt + cur.m) & kfw) != 0)
-            kv_compute<D, DOC>(p, qs[buf], gs[buf], ss[buf], kf, vf, dk, dv, cur, kw0, key_id, key_res, dpat);
+        if (!DOC || (ld_const(p.qbloom, lb * p.nqt + cur.m) & kfw) != 0) {
+            // Document ids: rows all of the document of the wave's keys, every
+            // row's interval holding the keys: no element test.
+            bool masked = true;
+            if (DOC && kone && p.mask.dilation <= 1) {
+                const i32x2 qd = ld_const((const i32x2*)p.qdoc, lb * p.nqt + cur.m);
+                const i32x4 sm = ld_const((const i32x4*)p.qsum, lb * p.nqt + cur.m);
+                masked = !(qd[0] && qd[1] == kid_w && sm[2] <= kw0 && kw0 + 32 <= sm[3]);
+            }
+            kv_compute<D, DOC>(p, qs[buf], gs[buf], ss[buf], kf, vf, dk, dv, cur, kw0, key_id, key_res, dpat, masked);
+        }
         have = q_next<DOC>(p, cur, lb, m0, m1, k0, k0 + kKeyBlock, kfb);
         if (have) --n_after;
         buf = nb;
@@ -967,7 +1007,7 @@ __device__ inline int order_tile(const BwdLaunch& p, int r) {
     }
 }
 
-__device__ __attribute__((always_inline)) inline bool t_step(const BwdLaunch& p, TCursor& c, int t_lo, int t_hi) {
+__device__ inline bool t_next(const BwdLaunch& p, TCursor& c, int t_lo, int t_hi) {
     if (p.order == BWA_ORDER_ASC) {
         if (c.r < 0) c.r = t_lo - 1;
         if (++c.r >= t_hi) return false;
@@ -992,13 +1032,17 @@ __device__ __attribute__((always_inline)) inline bool t_step(const BwdLaunch& p,
 
 // The next key tile of the walk whose filter, with document ids, meets the
 // filter qf of the block's rows.
-template <bool DOC>
-__device__ inline bool t_next(const BwdLaunch& p, TCursor& c, int t_lo, int t_hi, i64 lb, unsigned qf) {
-    if (!DOC) return t_step(p, c, t_lo, t_hi);
+__device__ inline bool t_next_doc(const BwdLaunch& p, TCursor& c, int t_lo, int t_hi, i64 lb, unsigned qf) {
     for (;;) {
-        if (!t_step(p, c, t_lo, t_hi)) return false;
+        if (!t_next(p, c, t_lo, t_hi)) return false;
         if ((ld_const(p.kbloom, lb * p.nkt + c.t) & qf) != 0) return true;
     }
+}
+
+template <bool DOC>
+__device__ inline bool walk_next(const BwdLaunch& p, TCursor& c, int t_lo, int t_hi, i64 lb, unsigned qf) {
+    if constexpr (DOC) return t_next_doc(p, c, t_lo, t_hi, lb, qf);
+    else return t_next(p, c, t_lo, t_hi);
 }
 
 // One 64-key tile against the wave's 32 rows, with two waves per SIMD (the
@@ -1013,13 +1057,14 @@ template <int D, bool XM, bool DOC>
 __device__ inline void q_compute(const BwdLaunch& p, const uint8_t* kt, const uint8_t* vt, const FragOffs<D>& fo,
                                      const uint4 (&qf)[D / 16], const uint8_t* gw, f32x16 (&dq)[D / 32],
                                      int t, int full_lo, int full_hi, int lo, int hi, float lse2, float delt, i64 b,
-                                     int row, int row_id, int row_res, unsigned dpat) {
+                                     int row, int row_id, int row_res, unsigned dpat, bool plain) {
     using C = Cfg<D>;
     constexpr int NS = 2 * C::NDS, NH = 2 * C::NDB, NP = NS + NH;  // steps per half
     constexpr int AH = XM ? 2 : 3;                                  // read-ahead
     const int lane = threadIdx.x & 63, hb = lane >> 5;
     const int j0 = t * kTile;
-    const bool masked = XM || !(full_lo <= j0 && j0 + kTile <= full_hi);
+    // plain: an element-test tile whose every element is visible (one document)
+    const bool masked = (XM && !plain) || !(full_lo <= j0 && j0 + kTile <= full_hi);
     const float sc = p.scale * kLog2e;
     static_for<2>([&](auto kbc) {
         constexpr int kb = decltype(kbc)::value;
@@ -1229,19 +1274,22 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
         const i64 mw = (qb * RB + wave * 32) / kTile;
         qfw = mw < p.nqt ? ld_const(p.qbloom, lb * p.nqt + mw) : 0u;
     }
+    // whether the wave's rows below q_valid share one document id (rid_w)
+    const int rid_w = uni(row_id);
+    const bool rone = DOC && __builtin_amdgcn_ballot_w64(row_in && row_id != rid_w) == 0;
     DqWalk wk;
     wk.t_lo = t_lo;
     wk.t_hi = t_hi;
     const __bf16* kbase = (const __bf16*)p.k + b * p.k_sB + hk * p.k_sH;
     const __bf16* vbase = (const __bf16*)p.v + b * p.v_sB + hk * p.v_sH;
     wk.cur = TCursor{-1, 0};
-    bool have = t_next<DOC>(p, wk.cur, t_lo, t_hi, lb, qfb);
+    bool have = walk_next<DOC>(p, wk.cur, t_lo, t_hi, lb, qfb);
     wk.ahead = wk.cur;
     wk.more = have;
     wk.n_after = 0;
     // (the barrier above: every wave has read red before ring[2] is copied to)
     if (have) dq_issue<D, NW>(p, kbase, vbase, wk.ahead.t, lds_opaque(ring[0][0]), lds_opaque(ring[0][1]));
-    if (wk.more) wk.more = t_next<DOC>(p, wk.ahead, t_lo, t_hi, lb, qfb);
+    if (wk.more) wk.more = walk_next<DOC>(p, wk.ahead, t_lo, t_hi, lb, qfb);
     if (wk.more) {
         dq_issue<D, NW>(p, kbase, vbase, wk.ahead.t, lds_opaque(ring[1][0]), lds_opaque(ring[1][1]));
         ++wk.n_after;
@@ -1251,16 +1299,29 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
     while (have) {
         wait_vmcnt(wk.n_after * LOADS);
         __syncthreads();
-        if (wk.more) wk.more = t_next<DOC>(p, wk.ahead, t_lo, t_hi, lb, qfb);
+        if (wk.more) wk.more = walk_next<DOC>(p, wk.ahead, t_lo, t_hi, lb, qfb);
         if (wk.more) {
             const int nb = buf == 0 ? 2 : buf - 1;
             dq_issue<D, NW>(p, kbase, vbase, wk.ahead.t, lds_opaque(ring[nb][0]), lds_opaque(ring[nb][1]));
             ++wk.n_after;
         }
-        if (!DOC || (ld_const(p.kbloom, lb * p.nkt + wk.cur.t) & qfw) != 0)
+        if constexpr (DOC) {
+            if ((ld_const(p.kbloom, lb * p.nkt + wk.cur.t) & qfw) != 0) {
+                // keys all of the document of the wave's rows (and, tested
+                // inside, every row's interval holding them): no element test
+                bool plain = false;
+                if (rone && p.mask.dilation <= 1) {
+                    const i32x2 kd = ld_const((const i32x2*)p.kdoc, lb * p.nkt + wk.cur.t);
+                    plain = kd[0] && kd[1] == rid_w;
+                }
+                q_compute<D, XM, DOC>(p, ring[buf][0], ring[buf][1], fo, qf, gw, dq, wk.cur.t, full_lo, full_hi, lo,
+                                      hi, lse2, delt, b, row, row_id, row_res, dpat, plain);
+            }
+        } else {
             q_compute<D, XM, DOC>(p, ring[buf][0], ring[buf][1], fo, qf, gw, dq, wk.cur.t, full_lo, full_hi, lo, hi,
-                             lse2, delt, b, row, row_id, row_res, dpat);
-        have = t_next<DOC>(p, wk.cur, t_lo, t_hi, lb, qfb);
+                                  lse2, delt, b, row, row_id, row_res, dpat, false);
+        }
+        have = walk_next<DOC>(p, wk.cur, t_lo, t_hi, lb, qfb);
         if (have) --wk.n_after;
         buf = buf == 2 ? 0 : buf + 1;
     }
@@ -1329,7 +1390,8 @@ i64 bwd_workspace_bytes(i64 B, i64 H, i64 Lq, i64 Lk, i64 list_batch) {
     const i64 nqt = (Lq + kTile - 1) / kTile, nkb = (Lk + kKeyBlock - 1) / kKeyBlock;
     const i64 nkt = (Lk + kTile - 1) / kTile;
     return pad256(B * H * Lq * 4) + 2 * pad256(list_batch * Lq * 4) + pad256(list_batch * nqt * 16) +
-           2 * pad256(list_batch * nkb * 4) + pad256(list_batch * nqt * 4) + pad256(list_batch * nkt * 4);
+           2 * pad256(list_batch * nkb * 4) + pad256(list_batch * nqt * 4) + pad256(list_batch * nkt * 4) +
+           pad256(list_batch * nqt * 8) + pad256(list_batch * nkt * 8);
 }
 
 void bwd_workspace_layout(BwdLaunch& a, void* ws) {
@@ -1344,7 +1406,9 @@ void bwd_workspace_layout(BwdLaunch& a, void* ws) {
     a.kfirst = (int*)w; w += pad256(a.list_batch * a.nkb * 4);
     a.klast = (int*)w; w += pad256(a.list_batch * a.nkb * 4);
     a.qbloom = (unsigned*)w; w += pad256(a.list_batch * a.nqt * 4);
-    a.kbloom = (unsigned*)w;
+    a.kbloom = (unsigned*)w; w += pad256(a.list_batch * a.nkt * 4);
+    a.qdoc = (int*)w; w += pad256(a.list_batch * a.nqt * 8);
+    a.kdoc = (int*)w;
 }
 
 }  // namespace bwa

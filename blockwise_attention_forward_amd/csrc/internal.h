@@ -251,6 +251,10 @@ struct BwdLaunch {
     // (row, key) pair of one document.
     unsigned* qbloom;  // [list_batch][nqt]
     unsigned* kbloom;  // [list_batch][nkt]
+    // and {1, id} when every row of the query tile that sees keys (every key
+    // of the key tile below kv_valid) has document id `id`, else {0, 0}
+    int* qdoc;         // [list_batch][nqt][2]
+    int* kdoc;         // [list_batch][nkt][2]
     int* kfirst; int* klast;   // [list_batch][nkb]: query tiles meeting the key block
     i64 list_batch, nqt, nkb, nkt;
     MaskDev mask;

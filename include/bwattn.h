@@ -440,8 +440,9 @@ int32_t bwa_attn_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor*
  * Workspace of bwa_attn_bwd for B, H query heads, Lq, Lk and mask (host
  * only, no launch).  *bytes = pad(B*H*Lq*4) + 2 pad(c*Lq*4)
  * + pad(c*ceil(Lq/64)*16) + 2 pad(c*ceil(Lk/128)*4) + pad(c*ceil(Lq/64)*4)
- * + pad(c*ceil(Lk/64)*4), pad = round up to 256, c = B with per-token
- * segment ids, else 1 (the last two hold document-id filters).  *n_kv_tiles (optional) = the
+ * + pad(c*ceil(Lk/64)*4) + pad(c*ceil(Lq/64)*8) + pad(c*ceil(Lk/64)*8),
+ * pad = round up to 256, c = B with per-token segment ids, else 1 (the last
+ * four hold document-id summaries of the query and key tiles).  *n_kv_tiles (optional) = the
  * number of 64-key tiles, the length of a BWA_ORDER_CUSTOM permutation.
  */
 int32_t bwa_attn_bwd_workspace(const bwa_mask* mask, int64_t B, int64_t H, int64_t Lq, int64_t Lk,

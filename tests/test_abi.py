@@ -348,17 +348,19 @@ def test_bwd_workspace_size():
     pad = lambda x: (x + 255) // 256 * 256  # noqa: E731
     # delta [B, H, Lq] fp32, row intervals [c, Lq] x 2, query-tile summaries
     # [c, ceil(Lq/64)] x 16 bytes, key-block ranges [c, ceil(Lk/128)] x 2,
-    # document-id filters [c, ceil(Lq/64)] and [c, ceil(Lk/64)] x 4 bytes
+    # document-id filters [c, ceil(Lq/64)] and [c, ceil(Lk/64)] x 4 bytes and
+    # the tiles' single ids [c, ceil(Lq/64)] and [c, ceil(Lk/64)] x 8 bytes
     m = _mask(causal=1, window=512)
     assert f(ctypes.byref(m), 2, 16, 4096, 8192, ctypes.byref(n), ctypes.byref(t)) == 0
     assert n.value == (pad(2 * 16 * 4096 * 4) + 2 * pad(4096 * 4) + pad(64 * 16) + 2 * pad(64 * 4) + pad(64 * 4)
-                       + pad(128 * 4))
+                       + pad(128 * 4) + pad(64 * 8) + pad(128 * 8))
     assert t.value == 128
     # per-token segment ids: one copy per batch element
     m = _mask(segment_ids_q=0x40000)
     assert f(ctypes.byref(m), 3, 2, 1000, 1000, ctypes.byref(n), None) == 0
     assert n.value == (pad(3 * 2 * 1000 * 4) + 2 * pad(3 * 1000 * 4) + pad(3 * 16 * 16) + 2 * pad(3 * 8 * 4)
-                       + pad(3 * 16 * 4) + pad(3 * 16 * 4))
+                       + pad(3 * 16 * 4) + pad(3 * 16 * 4)
+                       + pad(3 * 16 * 8) + pad(3 * 16 * 8))
     assert f(ctypes.byref(m), 3, 2, 1000, 1000, None, None) == 1
     assert f(ctypes.byref(_mask()), -1, 2, 10, 10, ctypes.byref(n), None) == 2
     assert f(ctypes.byref(_mask(causal=2)), 1, 2, 10, 10, ctypes.byref(n), None) == 5

@@ -176,6 +176,23 @@ def test_document_tile_filters(max_run, n_ids, D):
         _check_full(q, k, v, do, mask, D ** -0.5, dq, dk, dv, True, False, f"docs {max_run}/{n_ids} {extra}")
 
 
+def test_document_filters_in_every_order():
+    # the filtered key-tile walk of dQ in each order: dK and dV do not depend
+    # on it, dQ against the oracle
+    B, L, H, D = 1, 900, 2, 64
+    q, k, v, do = _inputs(B, L, L, H, H, D, 77)
+    ids = _doc_runs(L, 78, 90, 6)[None]
+    mask = {"segment_ids_q": ids, "segment_ids_kv": ids, "documents": True}
+    n = (L + 63) // 64
+    perm = torch.tensor(np.random.Generator(np.random.PCG64(79)).permutation(n), dtype=torch.int32, device=DEV)
+    base = _run(q, k, v, do, mask, D ** -0.5)
+    for order, kv in ((bw.BWA_ORDER_DESC, None), (bw.BWA_ORDER_OUTSIDE_IN, None), (bw.BWA_ORDER_CUSTOM, perm)):
+        dq, dk, dv = _run(q, k, v, do, mask, D ** -0.5, order=order, kv_order=kv)
+        torch.cuda.synchronize()
+        assert torch.equal(dk, base[1]) and torch.equal(dv, base[2]), order
+        _check_full(q, k, v, do, mask, D ** -0.5, dq, dk, dv, True, False, f"docs order {order}")
+
+
 def test_padding_garbage_does_not_leak():
     # rows past q_valid and keys past kv_valid hold NaN: they must not reach
     # any gradient (they are read as zeros and masked)

@@ -557,6 +557,14 @@ __device__ inline void qhead_init(const BwdLaunch& p, QHead<D, NW>& x, int g, i6
     x.gh = g;
 }
 
+// The LDS of an 8-wave workgroup of the dK/dV or dQ kernel, as two arrays
+// (the roles of each part are given with the kernels): ring, three pairs of
+// 64-row tiles, and side, four tiles.
+template <int D>
+using LdsRing = uint8_t[3][2][Cfg<D>::TILE_BYTES];
+template <int D>
+using LdsSide = uint8_t[4 * Cfg<D>::TILE_BYTES];
+
 // Copies of query tile c into LDS: Q and dO rows and, by waves 0..3, the
 // rows' statistics (LSE at st[0..63], delta, lo, hi after it).
 template <int D>
@@ -663,21 +671,21 @@ __device__ inline void kv_compute8(const BwdLaunch& p, const uint8_t* qt, const 
     });
 }
 
+// One dK/dV block of 128 keys (`logical` = (b * Hk + hk) * nkb + key block).
+// LDS: side holds K (two 64-row tiles) then V of the 128 keys; ring[x][0]
+// and ring[x][1] the Q and dO tiles of buffer x (x = 0, 1); ring[2] the rows'
+// statistics of both buffers.  At the end four 32 KB regions (the K, the V,
+// and the two Q / dO buffers) hold the row-half-1 waves' partial dK and dV,
+// one region per key group.
 template <int D, int G>
-__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv8(const BwdLaunch p) {
+__device__ __attribute__((always_inline)) inline void dkdv8_block(const BwdLaunch& p, i64 logical, LdsRing<D>& ring,
+                                                                  LdsSide<D>& side) {
     using C = Cfg<D>;
-    // K and V of the 128 keys (two 64-row tiles each), Q / dO tiles (two
-    // buffers) and the rows' statistics.  At the end the four arrays hold the
-    // row-half-1 waves' partial dK and dV, one array per key group.
-    __shared__ __attribute__((aligned(1024))) uint8_t ks[2][C::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t vs[2][C::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t qs[2][C::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t gs[2][C::TILE_BYTES];
-    __shared__ __attribute__((aligned(256))) float ss[2][256];  // LSE, delta, lo, hi of 64 rows
+    constexpr int T = C::TILE_BYTES;
+    float* const ss0 = (float*)&ring[2][0][0];  // LSE, delta, lo, hi of 64 rows, per buffer (256 floats)
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31;
     const int kg = wave & 3, rh = wave >> 2;  // key group, row half (waves w and w+4 share a SIMD)
-    const i64 logical = xcd_remap(blockIdx.x, gridDim.x);
     const i64 bhk = logical / p.nkb, kb = logical % p.nkb;
     const i64 b = bhk / p.Hk, hk = bhk % p.Hk;
     const i64 lb = p.list_batch == 1 ? 0 : b;
@@ -690,9 +698,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv8(const BwdLaunch p) {
         const int j0 = k0 + 64 * half;
         const int nk = (int)max((i64)0, min((i64)kTile, p.mask.kv_valid - j0));
         tile_issue<D, 8>((const __bf16*)p.k + b * p.k_sB + (i64)j0 * p.k_sL + hk * p.k_sH, p.k_sL, nk,
-                         lds_opaque(ks[half]));
+                         lds_opaque(&side[half * T]));
         tile_issue<D, 8>((const __bf16*)p.v + b * p.v_sB + (i64)j0 * p.v_sL + hk * p.v_sH, p.v_sL, nk,
-                         lds_opaque(vs[half]));
+                         lds_opaque(&side[(2 + half) * T]));
     }
     f32x16 dk[C::NDB], dv[C::NDB];
 #pragma unroll
@@ -704,7 +712,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv8(const BwdLaunch p) {
     bool have = m0 <= m1 && q_next<false>(p, cur, lb, m0, m1, k0, k0 + kKeyBlock, kfb);
     QHead<D, 8> qh;
     qh.gh = -1;
-    if (have) kv_issue8<D>(p, qh, cur, b, hk, lb, lds_opaque(qs[0]), lds_opaque(gs[0]), lds_opaque(ss[0]));
+    if (have) kv_issue8<D>(p, qh, cur, b, hk, lb, lds_opaque(ring[0][0]), lds_opaque(ring[0][1]), lds_opaque(ss0));
     int buf = 0;
     while (have) {
         // This wave's copies of buffer `buf` (and of the key tiles) have
@@ -715,9 +723,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv8(const BwdLaunch p) {
         QCursor nxt = cur;
         const bool more = q_next<false>(p, nxt, lb, m0, m1, k0, k0 + kKeyBlock, kfb);
         if (more)
-            kv_issue8<D>(p, qh, nxt, b, hk, lb, lds_opaque(qs[buf ^ 1]), lds_opaque(gs[buf ^ 1]),
-                         lds_opaque(ss[buf ^ 1]));
-        kv_compute8<D>(p, qs[buf], gs[buf], ss[buf], ks[kg >> 1], vs[kg >> 1], kg & 1, dk, dv, cur, lb, kw0, rh);
+            kv_issue8<D>(p, qh, nxt, b, hk, lb, lds_opaque(ring[buf ^ 1][0]), lds_opaque(ring[buf ^ 1][1]),
+                         lds_opaque(ss0 + (buf ^ 1) * 256));
+        kv_compute8<D>(p, ring[buf][0], ring[buf][1], ss0 + buf * 256, &side[(kg >> 1) * T], &side[(2 + (kg >> 1)) * T],
+                       kg & 1, dk, dv, cur, lb, kw0, rh);
         cur = nxt;
         have = more;
         buf ^= 1;
@@ -725,7 +734,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv8(const BwdLaunch p) {
     // The row-half-1 wave of each key group hands its partial sums to the
     // row-half-0 wave: lane-major, 8 D/32 x 16 floats per lane (32 KB).
     __syncthreads();
-    float* red = (float*)(kg == 0 ? &ks[0][0] : kg == 1 ? &vs[0][0] : kg == 2 ? &qs[0][0] : &gs[0][0]);
+    float* red = (float*)(kg < 2 ? &side[kg * 2 * T] : &ring[kg - 2][0][0]);
     if (rh == 1) {
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
@@ -1179,22 +1188,23 @@ __device__ inline void dq_issue(const BwdLaunch& p, const __bf16* kbase, const _
 
 // XM: element tests; DOC: document ids (with XM; the tile filters apply).
 // (XM without DOC: a dilated band.)
+// One dQ block of 256 rows (`logical` = (b * H + h) * nqb + position, the
+// blocks with the most key tiles first).  LDS: ring[i] holds the K and V
+// tiles of ring buffer i; side the block's dO rows (each wave reads its own
+// 32 as an operand).  The interval reduction borrows the third ring buffer
+// before its first copy.
 template <int D, int G, bool XM, int NW, bool DOC>
-__global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
+__device__ __attribute__((always_inline)) inline void dq_block(const BwdLaunch& p, i64 logical, LdsRing<D>& ring,
+                                                               LdsSide<D>& gs) {
     using C = Cfg<D>;
     constexpr int RB = NW * 32;  // rows per workgroup
     constexpr int LOADS = 2 * TileCopy<D, NW>::PER_WAVE;
     static_assert(2 * LOADS <= 15, "wait_vmcnt covers at most 15 outstanding copies");
-    // The ring: three K/V tile pairs.  dO rows of the block (each wave reads
-    // its own 32 as an operand).  The interval reduction borrows the third
-    // ring buffer before its first copy.
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[3][2][C::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t gs[RB * D * 2];
+    static_assert(RB * D * 2 <= (int)sizeof(LdsSide<D>), "the block's dO rows fit the side array");
     int* red = (int*)&ring[2][0][0];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hb = lane >> 5;
     const i64 nqb = (p.Lq + RB - 1) / RB;
-    const i64 logical = xcd_remap(blockIdx.x, gridDim.x);
     const i64 bh = logical / nqb;
     const i64 qb = nqb - 1 - logical % nqb;  // the blocks with the most key tiles first
     const i64 b = bh / p.H, h = bh % p.H, hk = h / p.kv_group;
@@ -1333,27 +1343,63 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
     }
 }
 
+// dQ for masks with element terms (dilated bands, document ids).
+template <int D, int G, bool XM, int NW, bool DOC>
+__global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq(const BwdLaunch p) {
+    __shared__ __attribute__((aligned(1024))) LdsRing<D> ring;
+    __shared__ __attribute__((aligned(1024))) LdsSide<D> side;
+    dq_block<D, G, XM, NW, DOC>(p, xcd_remap(blockIdx.x, gridDim.x), ring, side);
+}
+
+// dK/dV and dQ of masks without element terms in one launch, as 8-wave
+// workgroups on one LDS layout.  Per key/value head group (b, hk), in order:
+// the dQ blocks of its query heads, then its dK/dV blocks; each XCD takes a
+// contiguous range of that order, so a workgroup that finishes early takes
+// the next block of either kind (two launches leave compute units idle at the
+// end of the first when its blocks differ in length, as a window's do), and
+// both kinds of one head group share the XCD's L2.
+template <int D, int G>
+__global__ __launch_bounds__(512, 1) void attn_bwd_fused(const BwdLaunch p) {
+    __shared__ __attribute__((aligned(1024))) LdsRing<D> ring;
+    __shared__ __attribute__((aligned(1024))) LdsSide<D> side;
+    const i64 nqb = (p.Lq + 255) / 256;
+    const i64 nq = (i64)p.kv_group * nqb, per = nq + p.nkb;
+    const i64 logical = xcd_remap(blockIdx.x, gridDim.x);
+    const i64 g = logical / per, r = logical % per;  // g = b * Hk + hk
+    if (r < nq) {
+        const i64 b = g / p.Hk, hk = g % p.Hk, h = hk * p.kv_group + r / nqb;
+        dq_block<D, G, false, 8, false>(p, (b * p.H + h) * nqb + r % nqb, ring, side);
+    } else {
+        dkdv8_block<D, G>(p, g * p.nkb + (r - nq), ring, side);
+    }
+}
+
 template <int D, int G>
 hipError_t launch_dg(const BwdLaunch& a, hipStream_t stream) {
     const bool doc = a.mask.seg_mode == 3, xm = a.mask.dilation > 1 || doc;
+    constexpr int NW = kDqWaves;
+    static_assert(NW == 8, "the fused launch runs 8-wave dQ blocks");
+    const i64 nqb = (a.Lq + 32 * NW - 1) / (32 * NW);
+    if (!xm) {
+        // interval masks: dK/dV and dQ blocks in one launch, two waves per SIMD
+        const i64 n = (i64)a.B * a.Hk * ((i64)a.kv_group * nqb + a.nkb);
+        if (n > 0) hipLaunchKernelGGL((attn_bwd_fused<D, G>), dim3((unsigned)n), dim3(512), 0, stream, a);
+        return hipGetLastError();
+    }
+    // element masks: dK/dV with one wave per SIMD, then dQ
     const i64 nkb_total = (i64)a.B * a.Hk * a.nkb;
     if (nkb_total > 0) {
-        // element masks: one wave per SIMD; interval masks: two
         if (doc) hipLaunchKernelGGL((attn_bwd_dkdv<D, G, true>), dim3((unsigned)nkb_total), dim3(256), 0, stream, a);
-        else if (xm) hipLaunchKernelGGL((attn_bwd_dkdv<D, G, false>), dim3((unsigned)nkb_total), dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((attn_bwd_dkdv8<D, G>), dim3((unsigned)nkb_total), dim3(512), 0, stream, a);
+        else hipLaunchKernelGGL((attn_bwd_dkdv<D, G, false>), dim3((unsigned)nkb_total), dim3(256), 0, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    constexpr int NW = kDqWaves;
-    const i64 nqb_total = (i64)a.B * a.H * ((a.Lq + 32 * NW - 1) / (32 * NW));
+    const i64 nqb_total = (i64)a.B * a.H * nqb;
     if (nqb_total > 0) {
         if (doc)
             hipLaunchKernelGGL((attn_bwd_dq<D, G, true, NW, true>), dim3((unsigned)nqb_total), dim3(64 * NW), 0, stream, a);
-        else if (xm)
-            hipLaunchKernelGGL((attn_bwd_dq<D, G, true, NW, false>), dim3((unsigned)nqb_total), dim3(64 * NW), 0, stream, a);
         else
-            hipLaunchKernelGGL((attn_bwd_dq<D, G, false, NW, false>), dim3((unsigned)nqb_total), dim3(64 * NW), 0, stream, a);
+            hipLaunchKernelGGL((attn_bwd_dq<D, G, true, NW, false>), dim3((unsigned)nqb_total), dim3(64 * NW), 0, stream, a);
     }
     return hipGetLastError();
 }

@@ -282,6 +282,51 @@ static int32_t resolve_cus(int32_t n_cus, int32_t* out) {
     return BWA_OK;
 }
 
+// A dilated band (causal, window W, dilation g, kv_offset a multiple of g) is
+// g independent causal windows: row i = r + g a sees key j exactly when
+// j = r + g c with c <= a + kv_offset / g and a + kv_offset / g - c <
+// ceil(W / g).  When the lengths, kv_offset and the valid counts are
+// multiples of g, each batch element runs as one launch whose batch index is
+// the residue r, on strided views of q, k, v, o and lse: every key it
+// computes is visible, where the band's own walk computes g keys per visible
+// one.  Other dilated calls (and fixed-m modes, carried partials and
+// segments) take the element-test kernels.
+static bool dilated_as_windows(const bwa::AttnLaunch& a) {
+    const bwa::MaskDev& m = a.mask;
+    const i64 g = m.dilation;
+    return g > 1 && m.seg_mode == 0 && m.prefix == 0 && m.causal && m.window > 0 && a.mode == BWA_MODE_ONLINE &&
+           !a.lse_prev && !a.split_next && a.Lq % g == 0 && a.Lk % g == 0 && m.kv_offset % g == 0 &&
+           m.q_valid % g == 0 && m.kv_valid % g == 0;
+}
+
+static hipError_t launch_dilated(const bwa::AttnLaunch& a, int32_t bq, hipStream_t stream) {
+    const i64 g = a.mask.dilation;
+    const i64 ei = a.in_dtype == BWA_BF16 ? 2 : 4, eo = a.out_dtype == BWA_BF16 ? 2 : 4;
+    for (i64 b = 0; b < a.B; ++b) {
+        bwa::AttnLaunch s = a;
+        s.B = (int)g;
+        s.Lq = a.Lq / g;
+        s.Lk = a.Lk / g;
+        s.q = (const char*)a.q + b * a.q_sB * ei; s.q_sB = a.q_sL; s.q_sL = a.q_sL * g;
+        s.k = (const char*)a.k + b * a.k_sB * ei; s.k_sB = a.k_sL; s.k_sL = a.k_sL * g;
+        s.v = (const char*)a.v + b * a.v_sB * ei; s.v_sB = a.v_sL; s.v_sL = a.v_sL * g;
+        s.o = (char*)a.o + b * a.o_sB * eo; s.o_sB = a.o_sL; s.o_sL = a.o_sL * g;
+        s.lse = a.lse + b * a.lse_sB; s.lse_sB = a.lse_sL; s.lse_sL = a.lse_sL * g;
+        s.mask.lq = s.Lq;
+        s.mask.lk = s.Lk;
+        s.mask.kv_offset = a.mask.kv_offset / g;
+        s.mask.q_valid = a.mask.q_valid / g;
+        s.mask.kv_valid = a.mask.kv_valid / g;
+        s.mask.window = (int)((a.mask.window + g - 1) / g);
+        s.mask.dilation = 1;
+        s.have_blocks = 0;  // the walk follows the window inline
+        s.n_qblocks = (s.Lq + bq - 1) / bq;
+        const hipError_t e = bwa::launch_attn_fwd(s, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 static int32_t attn_fwd_impl(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v, const bwa_mask* mask,
                              const bwa_blocks* blocks, float scale, int32_t mode, const float* m,
                              const uint8_t* gate, const bwa_tensor* o_prev, const float* lse_prev, bwa_tensor* o,
@@ -345,6 +390,7 @@ static int32_t attn_fwd_impl(const bwa_tensor* q, const bwa_tensor* k, const bwa
     a.v_sB = v->sB; a.v_sL = v->sL; a.v_sH = v->sH;
     a.o = o->ptr; a.o_sB = o->sB; a.o_sL = o->sL; a.o_sH = o->sH;
     a.lse = lse;
+    a.lse_sB = H * Lq; a.lse_sH = Lq; a.lse_sL = 1;
     a.B = (int)B; a.H = (int)H; a.D = (int)q->D;
     a.kv_group = H > 0 ? (int)(H / k->H) : 1;
     a.Lq = Lq; a.Lk = Lk;
@@ -384,6 +430,7 @@ static int32_t attn_fwd_impl(const bwa_tensor* q, const bwa_tensor* k, const bwa
             bwa::split_workspace_layout(a, bal->ws, sp, bq, (int)q->D);
         }
     }
+    if (dilated_as_windows(a)) return hip_status(launch_dilated(a, bq, (hipStream_t)stream), "attn_fwd launch");
     return hip_status(bwa::launch_attn_fwd(a, (hipStream_t)stream), "attn_fwd launch");
 }
 

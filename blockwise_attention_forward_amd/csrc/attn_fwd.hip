@@ -500,12 +500,12 @@ __device__ inline void store_out(const AttnLaunch& p, f32x16 (&acc)[D / 32], flo
                                  float m_fixed, i64 b, i64 h, i64 row) {
     const bool row_ok = row < p.Lq;
     const i64 r = row_ok ? row : 0;
-    const i64 li = (b * p.H + h) * p.Lq + r;
+    const i64 li = (b * p.H + h) * p.Lq + r;  // the carried LSE: [B][H][Lq]
     void* o_row = OUT == BWA_F32 ? (void*)((float*)p.o + b * p.o_sB + r * p.o_sL + h * p.o_sH)
                                  : (void*)((__bf16*)p.o + b * p.o_sB + r * p.o_sL + h * p.o_sH);
     const float* prev_o = p.lse_prev ? p.o_prev + b * p.op_sB + r * p.op_sL + h * p.op_sH : nullptr;
-    store_rows<D, OUT, BODY>(p, acc, m_run, l_run, m_fixed, row_ok, o_row, p.lse + li, prev_o,
-                             p.lse_prev ? p.lse_prev + li : nullptr);
+    store_rows<D, OUT, BODY>(p, acc, m_run, l_run, m_fixed, row_ok, o_row, p.lse + b * p.lse_sB + h * p.lse_sH + r * p.lse_sL,
+                             prev_o, p.lse_prev ? p.lse_prev + li : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -1330,7 +1330,7 @@ __global__ __launch_bounds__(NW * 64) void merge_pieces_kernel(const AttnLaunch 
             *(uint2*)((__bf16*)p.o + off + 4 * i) = v;
         }
     }
-    if (part == 0) p.lse[li] = lse;
+    if (part == 0) p.lse[b * p.lse_sB + h * p.lse_sH + row * p.lse_sL] = lse;
 }
 
 // ---------------------------------------------------------------------------

@@ -130,7 +130,7 @@ struct AttnLaunch {
     const void* q; const void* k; const void* v;
     i64 q_sB, q_sL, q_sH, k_sB, k_sL, k_sH, v_sB, v_sL, v_sH;
     void* o; i64 o_sB, o_sL, o_sH;
-    float* lse;
+    float* lse; i64 lse_sB, lse_sH, lse_sL;  // lse[b * lse_sB + h * lse_sH + row * lse_sL]
     int B, H, D;
     int kv_group;  // query heads per key/value head (h reads key/value head h / kv_group)
     i64 Lq, Lk;

@@ -111,6 +111,36 @@ LONG_ROW_MASKS = [
 ]
 
 
+# Dilated bands whose lengths, kv_offset and valid counts are multiples of the
+# dilation g run as g strided causal windows (one launch per batch element,
+# the residue class as its batch index); the others walk the band with the
+# element test.  (g, window, Lq, Lk, kv_offset, q_valid, kv_valid)
+DILATED_SPLIT = [
+    (2, 100, 768, 768, 0, 768, 768),
+    (3, 257, 768, 960, -192, 720, 900),
+    (4, 1024, 768, 768, 0, 768, 768),
+    (4, 301, 512, 1024, -512, 512, 1000),
+    (5, 64, 640, 640, 0, 600, 640),
+    (4, 130, 768, 768, 2, 768, 768),  # kv_offset not a multiple of g: the element test
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("ci", range(len(DILATED_SPLIT)))
+def test_dilated_band_as_strided_windows(ci, D, dtype):
+    g, w, Lq, Lk, off, qv, kvv = DILATED_SPLIT[ci]
+    B, H, Hk = 2, 4, 2
+    mask = {"causal": True, "window": w, "dilation": g, "kv_offset": off, "q_valid": qv, "kv_valid": kvv}
+    q = _rand((B, Lq, H, D), 40 + ci, dtype)
+    k = _rand((B, Lk, Hk, D), 50 + ci, dtype)
+    v = _rand((B, Lk, Hk, D), 60 + ci, dtype)
+    scale = 1 / math.sqrt(D)
+    o_ref, l_ref = oracle_attention(q, k, v, mask, scale)
+    o, lse = bw.bwa_attn_fwd(q, k, v, mask, scale=scale)
+    assert_close(o, lse, o_ref, l_ref, dtype, f"dilated {DILATED_SPLIT[ci]}")
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("mi", range(len(LONG_ROW_MASKS)))
 def test_whole_block_launch_long_rows(mi, D):

@@ -15,7 +15,9 @@ merge of the two hop partials into the bf16 output.
 
 value      = counted attention FLOPs per step / step time (TFLOP/s), FLOPs
              counted on a 128x128 tile grid over non-skipped tiles, 4*D per
-             visible (row, key) pair of those tiles.
+             visible (row, key) pair of those tiles.  (A dilated band whose
+             sizes are multiples of its dilation g runs as g strided causal
+             windows; it is counted on their grids.)
 roofline   = the dominant kernel (the gated attention launch of one hop):
              algorithmic FLOPs per launch / its mean launch time (HIP events on
              the launch stream), against the bf16 dense matrix-core peak.
@@ -297,11 +299,25 @@ def setup_single(torch, bw, synth, name, launch="auto"):
     mask = bw.Mask.of(d["mask"], "cuda")
     bq, _ = bw.bwa_attn_tile(q.dtype, D)
     blocks = bw.bwa_block_mask_build(mask, B, Lq, Lk, bq, 128)
-    count_lists = bw.bwa_block_mask_build(mask, B, Lq, Lk, 128, 128)
+    m = d["mask"]
+    g = int(m.get("dilation", 0) or 0)
+    off, qv, kvv = int(m.get("kv_offset", 0)), int(m.get("q_valid", Lq)), int(m.get("kv_valid", Lk))
+    if g > 1 and all(x % g == 0 for x in (Lq, Lk, off, qv, kvv)):
+        # A dilated band of this shape runs as g strided causal windows (one
+        # per residue class): count the unmasked blocks of those windows, the
+        # work the call does, not the blocks of the band (which would count
+        # the g - 1 keys in g that the band hides).
+        sub = dict(causal=True, window=-(-int(m["window"]) // g), kv_offset=off // g, q_valid=qv // g,
+                   kv_valid=kvv // g)
+        count_lists = bw.bwa_block_mask_build(sub, B, Lq // g, Lk // g, 128, 128)
+        torch.cuda.synchronize()
+        flops = g * _counted_flops(count_lists, D, H, Lq // g, Lk // g)
+    else:
+        count_lists = bw.bwa_block_mask_build(mask, B, Lq, Lk, 128, 128)
+        torch.cuda.synchronize()
+        flops = _counted_flops(count_lists, D, H, Lq, Lk)
     o = torch.empty_like(q)
     lse = torch.empty(B, H, Lq, device="cuda")
-    torch.cuda.synchronize()
-    flops = _counted_flops(count_lists, D, H, Lq, Lk)
     attn, _, launch_info = _launcher(torch, bw, launch, q, Lk, B * H * ((Lq + bq - 1) // bq))
 
     def step(timer=None):

@@ -291,12 +291,28 @@ static int32_t resolve_cus(int32_t n_cus, int32_t* out) {
 // computes is visible, where the band's own walk computes g keys per visible
 // one.  Other dilated calls (and fixed-m modes, carried partials and
 // segments) take the element-test kernels.
-static bool dilated_as_windows(const bwa::AttnLaunch& a) {
-    const bwa::MaskDev& m = a.mask;
+static bool band_splits(const bwa::MaskDev& m, i64 Lq, i64 Lk) {
     const i64 g = m.dilation;
-    return g > 1 && m.seg_mode == 0 && m.prefix == 0 && m.causal && m.window > 0 && a.mode == BWA_MODE_ONLINE &&
-           !a.lse_prev && !a.split_next && a.Lq % g == 0 && a.Lk % g == 0 && m.kv_offset % g == 0 &&
-           m.q_valid % g == 0 && m.kv_valid % g == 0;
+    return g > 1 && m.seg_mode == 0 && m.prefix == 0 && m.causal && m.window > 0 && Lq % g == 0 && Lk % g == 0 &&
+           m.kv_offset % g == 0 && m.q_valid % g == 0 && m.kv_valid % g == 0;
+}
+
+// The mask of each residue class's window.
+static bwa::MaskDev band_window(const bwa::MaskDev& m, i64 Lq, i64 Lk) {
+    const i64 g = m.dilation;
+    bwa::MaskDev s = m;
+    s.lq = Lq / g;
+    s.lk = Lk / g;
+    s.kv_offset = m.kv_offset / g;
+    s.q_valid = m.q_valid / g;
+    s.kv_valid = m.kv_valid / g;
+    s.window = (int)((m.window + g - 1) / g);
+    s.dilation = 1;
+    return s;
+}
+
+static bool dilated_as_windows(const bwa::AttnLaunch& a) {
+    return band_splits(a.mask, a.Lq, a.Lk) && a.mode == BWA_MODE_ONLINE && !a.lse_prev && !a.split_next;
 }
 
 static hipError_t launch_dilated(const bwa::AttnLaunch& a, int32_t bq, hipStream_t stream) {
@@ -312,13 +328,7 @@ static hipError_t launch_dilated(const bwa::AttnLaunch& a, int32_t bq, hipStream
         s.v = (const char*)a.v + b * a.v_sB * ei; s.v_sB = a.v_sL; s.v_sL = a.v_sL * g;
         s.o = (char*)a.o + b * a.o_sB * eo; s.o_sB = a.o_sL; s.o_sL = a.o_sL * g;
         s.lse = a.lse + b * a.lse_sB; s.lse_sB = a.lse_sL; s.lse_sL = a.lse_sL * g;
-        s.mask.lq = s.Lq;
-        s.mask.lk = s.Lk;
-        s.mask.kv_offset = a.mask.kv_offset / g;
-        s.mask.q_valid = a.mask.q_valid / g;
-        s.mask.kv_valid = a.mask.kv_valid / g;
-        s.mask.window = (int)((a.mask.window + g - 1) / g);
-        s.mask.dilation = 1;
+        s.mask = band_window(a.mask, a.Lq, a.Lk);
         s.have_blocks = 0;  // the walk follows the window inline
         s.n_qblocks = (s.Lq + bq - 1) / bq;
         const hipError_t e = bwa::launch_attn_fwd(s, stream);
@@ -518,6 +528,17 @@ int32_t bwa_attn_fwd_balanced_carry(const bwa_tensor* q, const bwa_tensor* k, co
     return attn_fwd_impl(q, k, v, mask, blocks, scale, mode, m, gate, o_prev, lse_prev, o, lse, stream, &bal);
 }
 
+// The backward pass of a dilated band that splits into strided windows (as
+// the forward does; order ascending): one pass per batch element over g
+// residue classes, with the element's LSE gathered into the workspace in the
+// windows' row order first.  Its workspace: the windows' own, after the
+// gathered LSE.
+static i64 bwd_split_bytes(const bwa::MaskDev& m, i64 H, i64 Lq, i64 Lk) {
+    if (!band_splits(m, Lq, Lk)) return 0;
+    const i64 g = m.dilation;
+    return (H * Lq * 4 + 255) / 256 * 256 + bwa::bwd_workspace_bytes(g, H, Lq / g, Lk / g, 1);
+}
+
 int32_t bwa_attn_bwd_workspace(const bwa_mask* mask, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t* bytes,
                                int64_t* n_kv_tiles) {
     if (!bytes) return fail(BWA_ERR_NULL_ARG, "bytes output is NULL");
@@ -527,9 +548,39 @@ int32_t bwa_attn_bwd_workspace(const bwa_mask* mask, int64_t B, int64_t H, int64
     int32_t st = resolve_mask(mask, B, Lq, Lk, md);
     if (st) return st;
     const i64 lb = md.seg_mode >= 2 ? B : 1;
-    *bytes = bwa::bwd_workspace_bytes(B, H, Lq, Lk, lb);
+    *bytes = std::max(bwa::bwd_workspace_bytes(B, H, Lq, Lk, lb), bwd_split_bytes(md, H, Lq, Lk));
     if (n_kv_tiles) *n_kv_tiles = (Lk + 63) / 64;
     return ok();
+}
+
+static hipError_t launch_bwd_split(const bwa::BwdLaunch& a, void* workspace, hipStream_t stream) {
+    const i64 g = a.mask.dilation;
+    const i64 eg = a.grad_dtype == BWA_BF16 ? 2 : 4, eo = a.o_dtype == BWA_BF16 ? 2 : 4;
+    float* lse_w = (float*)workspace;
+    void* ws = (char*)workspace + (a.H * a.Lq * 4 + 255) / 256 * 256;
+    for (i64 b = 0; b < a.B; ++b) {
+        hipError_t e = bwa::launch_lse_gather(a.lse + b * a.H * a.Lq, lse_w, a.H, a.Lq, (int)g, stream);
+        if (e != hipSuccess) return e;
+        bwa::BwdLaunch s = a;
+        s.B = (int)g;
+        s.Lq = a.Lq / g;
+        s.Lk = a.Lk / g;
+        s.q = (const char*)a.q + b * a.q_sB * 2; s.q_sB = a.q_sL; s.q_sL = a.q_sL * g;
+        s.k = (const char*)a.k + b * a.k_sB * 2; s.k_sB = a.k_sL; s.k_sL = a.k_sL * g;
+        s.v = (const char*)a.v + b * a.v_sB * 2; s.v_sB = a.v_sL; s.v_sL = a.v_sL * g;
+        s.o = (const char*)a.o + b * a.o_sB * eo; s.o_sB = a.o_sL; s.o_sL = a.o_sL * g;
+        s.dout = (const char*)a.dout + b * a.do_sB * 2; s.do_sB = a.do_sL; s.do_sL = a.do_sL * g;
+        s.dq = (char*)a.dq + b * a.dq_sB * eg; s.dq_sB = a.dq_sL; s.dq_sL = a.dq_sL * g;
+        s.dk = (char*)a.dk + b * a.dk_sB * eg; s.dk_sB = a.dk_sL; s.dk_sL = a.dk_sL * g;
+        s.dv = (char*)a.dv + b * a.dv_sB * eg; s.dv_sB = a.dv_sL; s.dv_sL = a.dv_sL * g;
+        s.lse = lse_w;
+        s.mask = band_window(a.mask, a.Lq, a.Lk);
+        s.list_batch = 1;
+        bwa::bwd_workspace_layout(s, ws);
+        e = bwa::launch_attn_bwd(s, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 int32_t bwa_attn_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v, const bwa_tensor* o,
@@ -570,7 +621,8 @@ int32_t bwa_attn_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor*
         B * H * Lq * (q->D / 8) >= ((i64)1 << 32) - 256)
         return fail(BWA_ERR_UNSUPPORTED, "grid too large");
     a.list_batch = a.mask.seg_mode >= 2 ? B : 1;
-    const i64 need = bwa::bwd_workspace_bytes(B, H, Lq, Lk, a.list_batch);
+    const bool split = order == BWA_ORDER_ASC && band_splits(a.mask, Lq, Lk);
+    const i64 need = split ? bwd_split_bytes(a.mask, H, Lq, Lk) : bwa::bwd_workspace_bytes(B, H, Lq, Lk, a.list_batch);
     if (!workspace) return fail(BWA_ERR_NULL_ARG, "workspace is NULL");
     if ((uintptr_t)workspace % 256) return fail(BWA_ERR_BAD_STRIDE, "workspace not 256-byte aligned");
     if (workspace_bytes < need)
@@ -594,6 +646,7 @@ int32_t bwa_attn_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor*
     a.scale = scale;
     a.order = order;
     a.perm = order == BWA_ORDER_CUSTOM ? kv_order : nullptr;
+    if (split) return hip_status(launch_bwd_split(a, workspace, (hipStream_t)stream), "attn_bwd launch");
     bwa::bwd_workspace_layout(a, workspace);
     return hip_status(bwa::launch_attn_bwd(a, (hipStream_t)stream), "attn_bwd launch");
 }

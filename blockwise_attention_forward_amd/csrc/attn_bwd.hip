@@ -1430,6 +1430,21 @@ hipError_t launch_attn_bwd(const BwdLaunch& a, hipStream_t stream) {
     return a.D == 64 ? launch_d<64>(a, stream) : launch_d<128>(a, stream);
 }
 
+namespace {
+__global__ __launch_bounds__(256) void lse_gather_kernel(const float* src, float* dst, i64 H, i64 Lq, int g) {
+    const i64 i = (i64)blockIdx.x * 256 + threadIdx.x;  // over H * Lq, in dst order
+    if (i >= H * Lq) return;
+    const i64 n = Lq / g, r = i / (H * n), rest = i % (H * n), h = rest / n, a = rest % n;
+    dst[i] = src[h * Lq + r + (i64)g * a];
+}
+}  // namespace
+
+hipError_t launch_lse_gather(const float* src, float* dst, i64 H, i64 Lq, int g, hipStream_t stream) {
+    const i64 n = H * Lq;
+    if (n > 0) hipLaunchKernelGGL(lse_gather_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, src, dst, H, Lq, g);
+    return hipGetLastError();
+}
+
 static i64 pad256(i64 x) { return (x + 255) / 256 * 256; }
 
 i64 bwd_workspace_bytes(i64 B, i64 H, i64 Lq, i64 Lk, i64 list_batch) {

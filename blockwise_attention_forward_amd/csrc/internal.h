@@ -260,6 +260,9 @@ struct BwdLaunch {
     MaskDev mask;
 };
 hipError_t launch_attn_bwd(const BwdLaunch& a, hipStream_t stream);
+// dst[(r * H + h) * (Lq / g) + a] = src[h * Lq + r + g * a]: one batch
+// element's LSE [H][Lq] in the row order of its g residue classes.
+hipError_t launch_lse_gather(const float* src, float* dst, i64 H, i64 Lq, int g, hipStream_t stream);
 i64 bwd_workspace_bytes(i64 B, i64 H, i64 Lq, i64 Lk, i64 list_batch);
 void bwd_workspace_layout(BwdLaunch& a, void* ws);
 

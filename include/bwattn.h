@@ -114,6 +114,12 @@ typedef struct bwa_tensor {
  * A row with no visible key gets O = 0 and LSE = -inf.  (The [DKORDER]
  * tables name sliding_window, prefix_lm, dilated_sliding_window and
  * document masks without defining them; these are the plainest readings.)
+ * A dilated band is g causal windows of ceil(W / g) keys over the residue
+ * classes of rows and keys; when Lq, Lk, kv_offset, q_valid and kv_valid are
+ * multiples of g and there are no segments, bwa_attn_fwd (online mode,
+ * without a carried partial) and bwa_attn_bwd (ascending order) compute it
+ * that way, on strided views, so that they compute visible keys only; the
+ * results agree with the band's own walk to rounding.
  *
  * Segments come either from cumulative lengths (cu_seqlens_q/kv, shared by
  * every batch element; segment s covers [cu[s], cu[s+1]); positions covered
@@ -442,7 +448,11 @@ int32_t bwa_attn_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor*
  * + pad(c*ceil(Lq/64)*16) + 2 pad(c*ceil(Lk/128)*4) + pad(c*ceil(Lq/64)*4)
  * + pad(c*ceil(Lk/64)*4) + pad(c*ceil(Lq/64)*8) + pad(c*ceil(Lk/64)*8),
  * pad = round up to 256, c = B with per-token segment ids, else 1 (the last
- * four hold document-id summaries of the query and key tiles).  *n_kv_tiles (optional) = the
+ * four hold document-id summaries of the query and key tiles).  For a
+ * dilated band computed as strided windows (see the mask description),
+ * *bytes is the larger of that and pad(H*Lq*4) plus the same formula for B =
+ * g, Lq / g, Lk / g, c = 1 (one batch element's LSE in the windows' row order,
+ * then the windows' own workspace).  *n_kv_tiles (optional) = the
  * number of 64-key tiles, the length of a BWA_ORDER_CUSTOM permutation.
  */
 int32_t bwa_attn_bwd_workspace(const bwa_mask* mask, int64_t B, int64_t H, int64_t Lq, int64_t Lk,

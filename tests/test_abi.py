@@ -362,6 +362,16 @@ def test_bwd_workspace_size():
                        + pad(3 * 16 * 4) + pad(3 * 16 * 4)
                        + pad(3 * 16 * 8) + pad(3 * 16 * 8))
     assert f(ctypes.byref(m), 3, 2, 1000, 1000, None, None) == 1
+    # a dilated band that runs as g strided windows: the larger of the two
+    full = lambda B, H, Lq, Lk: (pad(B * H * Lq * 4) + 2 * pad(Lq * 4) + pad(-(-Lq // 64) * 16)  # noqa: E731
+                                 + 2 * pad(-(-Lk // 128) * 4) + pad(-(-Lq // 64) * 4) + pad(-(-Lk // 64) * 4)
+                                 + pad(-(-Lq // 64) * 8) + pad(-(-Lk // 64) * 8))
+    m = _mask(causal=1, window=1024, dilation=4)
+    assert f(ctypes.byref(m), 2, 16, 8192, 8192, ctypes.byref(n), None) == 0
+    assert n.value == max(full(2, 16, 8192, 8192), pad(16 * 8192 * 4) + full(4, 16, 2048, 2048))
+    m = _mask(causal=1, window=1024, dilation=4, kv_offset=2)  # not a multiple of g: the band's own
+    assert f(ctypes.byref(m), 2, 16, 8192, 8192, ctypes.byref(n), None) == 0
+    assert n.value == full(2, 16, 8192, 8192)
     assert f(ctypes.byref(_mask()), -1, 2, 10, 10, ctypes.byref(n), None) == 2
     assert f(ctypes.byref(_mask(causal=2)), 1, 2, 10, 10, ctypes.byref(n), None) == 5
 

@@ -22,7 +22,7 @@ import torch
 import oracle
 import synth
 from helpers import assert_grad_close, bwd_bounds, mask_for_batch, np64
-from test_gpu_kernels import MASKS
+from test_gpu_kernels import DILATED_SPLIT, MASKS
 
 pytestmark = pytest.mark.gpu
 
@@ -191,6 +191,20 @@ def test_document_filters_in_every_order():
         torch.cuda.synchronize()
         assert torch.equal(dk, base[1]) and torch.equal(dv, base[2]), order
         _check_full(q, k, v, do, mask, D ** -0.5, dq, dk, dv, True, False, f"docs order {order}")
+
+
+@pytest.mark.parametrize("ci", range(len(DILATED_SPLIT)))
+def test_dilated_band_as_strided_windows(ci):
+    # ascending order runs a band whose sizes are multiples of g as g strided
+    # windows; descending order walks the band itself: both against the oracle
+    g, w, Lq, Lk, off, qv, kvv = DILATED_SPLIT[ci]
+    B, H, Hk, D = 2, 4, 2, 64
+    q, k, v, do = _inputs(B, Lq, Lk, H, Hk, D, 90 + ci)
+    mask = {"causal": True, "window": w, "dilation": g, "kv_offset": off, "q_valid": qv, "kv_valid": kvv}
+    for order in (bw.BWA_ORDER_ASC, bw.BWA_ORDER_DESC):
+        dq, dk, dv = _run(q, k, v, do, mask, D ** -0.5, order=order)
+        torch.cuda.synchronize()
+        _check_full(q, k, v, do, mask, D ** -0.5, dq, dk, dv, True, False, f"dilated {DILATED_SPLIT[ci]} {order}")
 
 
 def test_padding_garbage_does_not_leak():

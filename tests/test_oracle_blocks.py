@@ -160,3 +160,25 @@ def test_workload_counts():
     assert k4.shape == (296, 296) and np.all(k4 == FULL)
     np.testing.assert_allclose(oracle.counted_flops(k4, 37800, 37800, 128, 128, 128) * 20,
                                4 * 128 * 37800.0 ** 2 * 20)
+
+
+@pytest.mark.parametrize("g,W,Lq,Lk,off,qv,kvv", [
+    (2, 7, 24, 24, 0, 24, 24),
+    (3, 10, 24, 36, -12, 21, 33),
+    (4, 16, 32, 32, 4, 28, 32),
+    (5, 3, 40, 20, 20, 40, 15),
+    (4, 1, 16, 16, 0, 16, 16),
+])
+def test_dilated_band_is_strided_windows(g, W, Lq, Lk, off, qv, kvv):
+    # The library computes a dilated band whose sizes are multiples of g as g
+    # causal windows of ceil(W / g) keys over the residue classes r: rows
+    # r + g a, keys r + g c, kv_offset / g.  The band's visibility must equal
+    # the union of those windows' (brute force on the oracle's definition).
+    band = {"causal": True, "window": W, "dilation": g, "kv_offset": off, "q_valid": qv, "kv_valid": kvv}
+    full = oracle.visibility(np.arange(Lq), Lk, band, Lq)
+    sub = {"causal": True, "window": -(-W // g), "kv_offset": off // g, "q_valid": qv // g, "kv_valid": kvv // g}
+    win = oracle.visibility(np.arange(Lq // g), Lk // g, sub, Lq // g)
+    split = np.zeros_like(full)
+    for r in range(g):
+        split[r::g, r::g] = win
+    assert np.array_equal(full, split)

@@ -275,8 +275,12 @@ def setup_dit_share(torch, bw, synth, launch="auto"):
                 sample_oracle=sample_oracle, hops=len(ks), launch=launch_info["launch"])
 
 
-def setup_single(torch, bw, synth, name, launch="auto"):
-    """One attention call of a masked workload (run lists + attention)."""
+def setup_single(torch, bw, synth, name, launch="auto", mode="online"):
+    """One attention call of a masked workload (run lists + attention).
+
+    mode "gated": the bound and gate of "Fixed-m softmax for 2D-ring x Ulysses
+    attention (WAN 2.2)" (description) are computed in the step, and the call
+    runs fixed-m on the heads that pass the gate, online on the rest."""
     if name == "varlen":
         d = synth.make_varlen("cuda")
         desc = ("varlen: H3 packed request, B=1 H=24 D=128 bf16, 33,024 tokens, cu_seqlens [0, 33002, 33024], "
@@ -320,10 +324,24 @@ def setup_single(torch, bw, synth, name, launch="auto"):
     lse = torch.empty(B, H, Lq, device="cuda")
     attn, _, launch_info = _launcher(torch, bw, launch, q, Lk, B * H * ((Lq + bq - 1) // bq))
 
+    gated = mode == "gated"
+    if gated:
+        tau = 106.5
+        bound_out = (torch.empty(B, H, device="cuda"), torch.empty(B, H, device="cuda"),
+                     torch.empty(B, H, Lq, device="cuda"), torch.empty(B, H, dtype=torch.uint8, device="cuda"))
+
     def step(timer=None):
         bw.bwa_block_mask_build(mask, B, Lq, Lk, bq, 128, out=blocks)
-        tok = timer.start("hop") if timer else None
-        attn(q, k, v, mask, blocks=blocks, scale=scale, o=o, lse=lse)
+        if gated:
+            tb = timer.start("bound") if timer else None
+            _, _, mm, gate = bw.bwa_fixed_m_bound(q, [k], scale, tau, kv_valid=[kvv], q_valid=qv, out=bound_out)
+            if timer:
+                timer.stop(tb)
+            tok = timer.start("hop") if timer else None
+            attn(q, k, v, mask, blocks=blocks, scale=scale, mode=bw.BWA_MODE_GATED, m=mm, gate=gate, o=o, lse=lse)
+        else:
+            tok = timer.start("hop") if timer else None
+            attn(q, k, v, mask, blocks=blocks, scale=scale, o=o, lse=lse)
         if timer:
             timer.stop(tok)
 
@@ -343,6 +361,13 @@ def setup_single(torch, bw, synth, name, launch="auto"):
         return fl, dt, f"head 0, {len(rows)} seeded query rows against their visible keys, fp64"
 
     info = dict(workload=desc, B=B, H=H, D=D, Lq=Lq, Lk=Lk, **launch_info)
+    if gated:
+        step()
+        torch.cuda.synchronize()
+        info.update(mode=f"gated: fixed-m (gate {tau}) on heads that pass, online on the rest; bound in the step",
+                    heads_fixed_m=int(bound_out[3].sum().item()))
+    else:
+        info.update(mode="online")
     return dict(step=step, flops_step=flops, flops_dominant=flops, dominant="hop", info=info,
                 sample_oracle=sample_oracle, data=d)
 
@@ -477,6 +502,8 @@ def main():
                     help="attention launch; auto: balanced from 4 rounds of query blocks per compute unit up")
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
                     help="bwd: time the backward pass of a single-call workload")
+    ap.add_argument("--mode", default="online", choices=["online", "gated"],
+                    help="single-call workloads: online softmax, or the fixed-m bound and gate with online fallback")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 3 plain elementwise copies of MIB MiB (scale for HBM byte counters)")
@@ -501,6 +528,9 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    if args.which == "bwd" and args.mode == "gated":
+        print("--mode gated applies to the forward pass", file=sys.stderr)
+        sys.exit(2)
     if args.workload != "dit_share":
         return run_single(args, torch, bw, synth)
     if args.which == "bwd":
@@ -647,7 +677,7 @@ def setup_backward(torch, bw, synth, W):
 
 def run_single(args, torch, bw, synth):
     """A masked workload: one attention call per step (bf16 in and out)."""
-    W = setup_single(torch, bw, synth, args.workload, args.launch)
+    W = setup_single(torch, bw, synth, args.workload, args.launch, args.mode)
     if args.which == "bwd":
         W = setup_backward(torch, bw, synth, W)
     timer = Timer(torch)
@@ -676,6 +706,7 @@ def run_single(args, torch, bw, synth):
         "dtype": "bf16", "data": "synthetic", "config": W["info"],
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         ("ms_backward" if bwd else "ms_attention"): round(ms_hop, 4),
+        **({"ms_bound": round(timer.mean_ms("bound"), 4)} if args.mode == "gated" and not bwd else {}),
         "counted_TFLOP": round(W["flops_step"] / 1e12, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

@@ -277,6 +277,24 @@ def test_varlen_balanced():
     assert_close(*gpu_rows(o, l, rows), o_ref, l_ref, BF16, "varlen balanced")
 
 
+def test_varlen_gated_balanced():
+    # The packed request with the fixed-m bound and gate (bench --mode gated):
+    # the alignment rows stay zero with LSE -inf, the rest matches the oracle.
+    w = synth.make_varlen(DEV)
+    q, k, v, mask, scale = w["q"], w["k"], w["v"], w["mask"], w["scale"]
+    B, L, H, D = q.shape
+    kmax, mmax, m, gate = bw.bwa_fixed_m_bound(q, [k], scale, 106.5, q_valid=mask["q_valid"])
+    assert gate.all().item()
+    bq, _ = bw.bwa_attn_tile(BF16, D)
+    blocks = bw.bwa_block_mask_build(mask, 1, L, L, bq, 128)
+    o, l = bw.bwa_attn_fwd_balanced(q, k, v, mask, blocks=blocks, scale=scale, mode=bw.BWA_MODE_GATED, m=m,
+                                    gate=gate)
+    assert torch.all(o[:, 33002:] == 0) and torch.all(torch.isneginf(l[:, :, 33002:]))
+    rows = synth.sample_rows(L, 512, seed=30, must=[0, 127, 128, 33001, 33002, 33023])
+    o_ref, l_ref = oracle_attention(q, k, v, mask, scale, rows)
+    assert_close(*gpu_rows(o, l, rows), o_ref, l_ref, BF16, "varlen gated")
+
+
 def _hops_carry(d, mode, m=None, gate=None, balanced=False):
     """The hops chained by the carried partial: hop 0 writes fp32, the last hop the bf16 result."""
     q = d["q"]
@@ -392,6 +410,25 @@ def test_long_causal_single_segment(long):
     rows = synth.sample_rows(L, 512, seed=26, must=[0, 1, 255, 256, L - 1])
     o_ref, l_ref = oracle_attention(q, k, v, plain, scale, rows)
     assert_close(*gpu_rows(o0, l0, rows), o_ref, l_ref, BF16, "1M causal")
+
+
+@pytest.mark.timeout(900)
+def test_long_causal_gated_balanced(long):
+    # The fixed-m bound and gate on the 1M causal workload, the balanced launch
+    # (the bench's --mode gated): every head passes the gate on these inputs
+    # and runs the fixed-m body; the result is the oracle's within tolerance.
+    q, k, v, scale = long["q"], long["k"], long["v"], long["scale"]
+    L = q.shape[1]
+    mask = {"causal": True}
+    kmax, mmax, m, gate = bw.bwa_fixed_m_bound(q, [k], scale, 106.5)
+    assert gate.all().item()
+    bq, _ = bw.bwa_attn_tile(BF16, 128)
+    blocks = bw.bwa_block_mask_build(mask, 1, L, L, bq, 128)
+    o, l = bw.bwa_attn_fwd_balanced(q, k, v, mask, blocks=blocks, scale=scale, mode=bw.BWA_MODE_GATED, m=m,
+                                    gate=gate)
+    rows = synth.sample_rows(L, 512, seed=29, must=[0, 1, 255, 256, L - 1])
+    o_ref, l_ref = oracle_attention(q, k, v, mask, scale, rows)
+    assert_close(*gpu_rows(o, l, rows), o_ref, l_ref, BF16, "1M causal gated")
 
 
 @pytest.mark.timeout(900)

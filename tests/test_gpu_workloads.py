@@ -143,6 +143,29 @@ def test_page_masks(kind, Lq, Lk):
     assert_close(*gpu_rows(o, l, rows), o_ref, l_ref, BF16, f"{kind} {Lq}x{Lk}")
 
 
+@pytest.mark.parametrize("kind", synth.PAGE_MASKS)
+def test_page_masks_gated(kind):
+    # The page masks with the fixed-m bound and gate (bench --mode gated), plain
+    # launch: every head passes on these inputs; the fixed-m body with the
+    # element tests (dilated bands walk their band here, not the strided
+    # windows) matches the oracle, and the gated launch gives the fixed-m bits.
+    Lq = Lk = 4096
+    w = synth.make_page_mask(kind, Lq, Lk, DEV)
+    q, k, v, mask, scale = w["q"], w["k"], w["v"], w["mask"], w["scale"]
+    m0 = mask_for_batch(mask, 0)
+    qv, kvv = int(mask.get("q_valid", Lq)), int(mask.get("kv_valid", Lk))
+    kmax, mmax, m, gate = bw.bwa_fixed_m_bound(q, [k], scale, 106.5, kv_valid=[kvv], q_valid=qv)
+    assert gate.all().item()
+    bq, _ = bw.bwa_attn_tile(BF16, 128)
+    blocks = bw.bwa_block_mask_build(mask, 1, Lq, Lk, bq, 128)
+    o, l = bw.bwa_attn_fwd(q, k, v, mask, blocks=blocks, scale=scale, mode=bw.BWA_MODE_GATED, m=m, gate=gate)
+    o2, l2 = bw.bwa_attn_fwd(q, k, v, mask, blocks=blocks, scale=scale, mode=bw.BWA_MODE_FIXED_M, m=m)
+    assert torch.equal(o, o2) and torch.equal(l, l2)
+    rows = synth.sample_rows(Lq, 256, seed=31, must=[0, 1, 63, 64, Lq // 4 - 1, Lq // 4, Lq - 1])
+    o_ref, l_ref = oracle_attention(q, k, v, m0, scale, rows)
+    assert_close(*gpu_rows(o, l, rows), o_ref, l_ref, BF16, f"{kind} gated")
+
+
 @pytest.fixture(scope="module")
 def dit():
     return synth.make_dit_share(DEV)

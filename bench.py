@@ -508,6 +508,12 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 3 plain elementwise copies of MIB MiB (scale for HBM byte counters)")
     args = ap.parse_args()
+    if args.which == "bwd" and args.mode == "gated":
+        print("--mode gated applies to the forward pass", file=sys.stderr)
+        sys.exit(2)
+    if args.workload == "dit_share" and args.mode == "gated":
+        print("the dit_share step is gated already (--mode applies to the single-call workloads)", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share only (one MI355X); multi-GPU runs are not part of "
               "this build: run with --gpus 1", file=sys.stderr)
@@ -528,9 +534,6 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    if args.which == "bwd" and args.mode == "gated":
-        print("--mode gated applies to the forward pass", file=sys.stderr)
-        sys.exit(2)
     if args.workload != "dit_share":
         return run_single(args, torch, bw, synth)
     if args.which == "bwd":

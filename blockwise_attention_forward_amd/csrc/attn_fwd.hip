@@ -551,6 +551,11 @@ template <int D, int NW>
 struct Bf16State {
     using C = Bf16Cfg<D, NW>;
     uint4 qf[C::NDS];
+    // Lane byte offsets of the fragment reads inside a tile (computed once per
+    // block, see lds_lane_offsets): K fragment of step ds in key block 0, and
+    // the first transposing V^T read of d block db.
+    int koff[C::NDS];
+    int voff[C::NDB];
     f32x16 acc[C::NDB];
     float m_run, l_run, m_fixed, m_l2, scale_l2;
     int lo, hi;
@@ -596,6 +601,33 @@ template <int D> __device__ inline int k_swz(int r, int c) {
 }
 template <int D> __device__ inline int v_swz(int r, int c) {
     return D == 128 ? c ^ ((r & 3) << 2) : c ^ (((r >> 1) & 1) << 2);
+}
+
+// The lane's byte offsets of its fragment reads within a tile.  The swizzles
+// depend on the row only through bits that the key-block (32 rows) and
+// 16-key steps leave alone, so one offset per K step ds and one per V d block
+// cover every read of a tile: key block kb adds kb*32 rows, V key step kk adds
+// kk*16 rows and the second transposing read 8 rows, all constants.  The
+// offsets are hidden from the optimizer (empty asm operand), so each read is
+// lane offset + (buffer base + constant), with the sum of constants folded
+// into the LDS instruction's immediate offset, instead of the buffer base
+// being recombined with the lane bits for every read of every ring slot.
+template <int D, int NW>
+__device__ inline void lds_lane_offsets(Bf16State<D, NW>& st) {
+    using C = Bf16Cfg<D, NW>;
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hb = lane >> 5;
+    const int g1 = (lane >> 4) & 1, s_row = (lane >> 2) & 3, u = lane & 3;
+#pragma unroll
+    for (int ds = 0; ds < C::NDS; ++ds) {
+        st.koff[ds] = l32 * (D * 2) + k_swz<D>(l32, ds * 2 + hb) * 16;
+        asm volatile("" : "+v"(st.koff[ds]));
+    }
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+        const int r0 = hb * 4 + s_row, c = db * 4 + g1 * 2 + (u >> 1);  // chunk of d = db*32 + 16*g1 + 4u
+        st.voff[db] = r0 * (D * 2) + v_swz<D>(r0, c) * 16 + (u & 1) * 8;
+        asm volatile("" : "+v"(st.voff[db]));
+    }
 }
 
 // Issue the HBM -> LDS copies of one K and one V tile (rows past kv_lim read as zero).
@@ -746,23 +778,19 @@ __device__ inline void bf16_compute_tile(const uint8_t* kl, const uint8_t* vl, B
                                          bool masked, const XMask& xm, const int* kidl) {
     using C = Bf16Cfg<D, NW>;
     constexpr int NDS = C::NDS, NDB = C::NDB;
-    const int lane = threadIdx.x & 63, l32 = lane & 31, hb = lane >> 5;
-    // K fragment of step i = kb*NDS + ds: row kb*32 + l32, chunk ds*2 + hb.
+    // K fragment of step i = kb*NDS + ds: row kb*32 + l32, chunk ds*2 + hb
+    // (l32 = lane % 32, hb = lane / 32), at the lane's offset for ds.
     auto kfrag = [&](int i) {
-        const int kb = i / NDS, ds = i % NDS, r = kb * 32 + l32;
-        return *(const uint4*)(kl + r * (D * 2) + k_swz<D>(r, ds * 2 + hb) * 16);
+        const int kb = i / NDS, ds = i % NDS;
+        return *(const uint4*)(kl + st.koff[ds] + kb * 32 * (D * 2));
     };
     // V^T fragment of step j = kk*NDB + db: keys kk*16 + {hb*4 + 0..3} then
     // kk*16 + 8 + {hb*4 + 0..3}, for d = db*32 + l32.
-    const int g1 = (lane >> 4) & 1, s_row = (lane >> 2) & 3, u = lane & 3;
     auto vfrag = [&](int j) {
         const int kk = j / NDB, db = j % NDB;
-        const int c = db * 4 + g1 * 2 + (u >> 1);  // 16-byte chunk of d = db*32 + 16*g1 + 4u
-        const int r0 = kk * 16 + hb * 4 + s_row, r1 = r0 + 8;
-        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(vl + r0 * (D * 2) + v_swz<D>(r0, c) * 16 + (u & 1) * 8));
-        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(vl + r1 * (D * 2) + v_swz<D>(r1, c) * 16 + (u & 1) * 8));
+        const uint8_t* a = vl + st.voff[db] + kk * 16 * (D * 2);  // rows kk*16 + hb*4 + 0..3
+        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 8 * (D * 2)));  // rows + 8
         uint4 out;
         out.x = __builtin_bit_cast(uint2, x0).x;
         out.y = __builtin_bit_cast(uint2, x0).y;
@@ -1069,6 +1097,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_fwd_bf16(const 
     st.xdoc = 0;
     if (XM) xmask_row(p, b, row, row_ok, st.xres, st.xdoc);
     wave_rows(st, row_ok, lo, hi);
+    lds_lane_offsets(st);
 
     const bool ne = row_ok && lo < hi;
     const Walk w0 = make_walk<C::TILE, C::NT>(p, b, qb, ne ? lo : 0x7fffffff, ne ? hi : 0,
@@ -1187,6 +1216,7 @@ __device__ inline void bal_item(const AttnLaunch& p, const Ring<D, NW>& ring, in
     st.xres = 0;
     st.xdoc = 0;
     wave_rows(st, row_ok, lo, hi);
+    lds_lane_offsets(st);
     const bool ne = row_ok && lo < hi;
     const Walk walk = make_walk<C::TILE, C::NT>(p, b, qb, ne ? lo : 0x7fffffff, ne ? hi : 0,
                                                 row_ok ? (ne ? lo : 0x7fffffff) : 0,

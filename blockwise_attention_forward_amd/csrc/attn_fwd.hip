@@ -946,7 +946,14 @@ __device__ __attribute__((always_inline)) inline bool bf16_step(const AttnLaunch
     const bool masked = cur.masked(walk.Lk);
     // This tile's copies are complete in every wave, and every wave is done
     // with the buffer the next copy goes to (the previous tile's).
-    wait_vmcnt(n_after * (XM && xm.kid ? LOADS + 1 : LOADS));  // K, V (and the key ids)
+    // At most NB - 2 (0 or 1) later tiles are in flight: a compile-time count
+    // either way, not a branch tree over the run-time product.
+    if (NB == 3 && n_after) {
+        if (XM && xm.kid) wait_vmcnt(LOADS + 1);  // K, V and the key ids
+        else wait_vmcnt(LOADS);
+    } else {
+        wait_vmcnt(0);
+    }
     __syncthreads();
     if (more) more = ahead.next(walk);
     if (more) {

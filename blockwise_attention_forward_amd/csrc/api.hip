@@ -36,6 +36,7 @@ int32_t hip_status(hipError_t e, const char* what) {
 }
 
 constexpr i64 kMaxLen = (i64)1 << 30;  // positions are kept in int32 inside the kernels
+constexpr i64 kMaxRowStride = (i64)1 << 24;
 
 int elem_size(int32_t dt) { return dt == BWA_BF16 ? 2 : 4; }
 
@@ -56,6 +57,10 @@ int32_t check_tensor(const bwa_tensor* t, const char* name) {
     if ((t->sB * es) % 16 || (t->sL * es) % 16 || (t->sH * es) % 16)
         return fail(BWA_ERR_BAD_STRIDE, "%s: strides must be multiples of 16 bytes", name);
     if (t->sB < 0 || t->sL < 0 || t->sH < 0) return fail(BWA_ERR_BAD_STRIDE, "%s: negative stride", name);
+    // A tile copy addresses up to 64 rows from one base with 32-bit byte
+    // offsets: row strides stay below 2^24 elements.
+    if (t->sL >= kMaxRowStride)
+        return fail(BWA_ERR_BAD_STRIDE, "%s: row stride of %lld elements (limit 2^24)", name, (long long)t->sL);
     // No two (b, l, h) rows may share an element: broadcast views (a zero
     // stride) and strides that interleave rows are rejected.  Sufficient
     // test: taken by increasing stride, each dimension of extent > 1 steps

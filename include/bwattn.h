@@ -27,7 +27,8 @@
  *    taken by increasing stride, each dimension of extent > 1 must step past
  *    everything the dimensions inside it span (so broadcast views with a zero
  *    stride, and L or H strides under D, return BWA_ERR_BAD_STRIDE; any
- *    permutation of B, L, H and padded row pitches are fine).  Per-row
+ *    permutation of B, L, H and padded row pitches are fine).  The L stride
+ *    must be below 2^24 elements (BWA_ERR_BAD_STRIDE otherwise).  Per-row
  *    statistics (lse, m) are dense fp32 [B, H, L].
  *  - Every pointer inside a tensor or mask, and every output pointer, is a
  *    device pointer unless the argument says "host".  The caller allocates

@@ -174,6 +174,14 @@ def test_mask_errors(mask, code):
     assert _attn(q, _t(), _t(), _t(), mask=_mask(**mask)) == code
 
 
+def test_row_stride_limit():
+    # row strides of 2^24 elements or more are refused before anything runs
+    # (the tile copies use 32-bit offsets over 64 rows)
+    assert _attn(_t(), _t(sL=1 << 24), _t(), _t()) == 3
+    assert "row stride" in bw.bwa_last_error()
+    assert _attn(_t(), _t(sL=(1 << 24) - 8, sB=(1 << 24) * 256), _t(), _t(), mask=_mask(causal=2)) == 5
+
+
 def test_non_overlapping_layouts_pass_the_stride_check():
     # head-major [B, H, L, D] views, a padded row pitch and a single row per
     # head with a zero stride are valid layouts: each call gets past the

@@ -631,9 +631,35 @@ __device__ inline void lds_lane_offsets(Bf16State<D, NW>& st) {
 }
 
 // Issue the HBM -> LDS copies of one K and one V tile (rows past kv_lim read as zero).
-template <int D, int NW, bool XM = false>
+// K and V buffer resources for a whole walk (online-only launches): one range
+// per tensor slice, from its first row to the end of row kv_lim - 1, with a
+// tile's rows addressed by the lane offset plus j0 rows, so no resource is
+// rebuilt per tile.  Rows past kv_lim fall outside the range and read as
+// zero, as with one range per tile.  Taken only when every row a tile can
+// address keeps its byte offset below 2^31.
+struct WalkRsrc {
+    __amdgpu_buffer_rsrc_t kr, vr;
+    int ksl2, vsl2;  // row strides in bytes
+    bool whole;
+};
+
+template <int D>
+__device__ inline WalkRsrc walk_rsrc(const AttnLaunch& p, const __bf16* kbase, const __bf16* vbase, int kv_lim) {
+    WalkRsrc w;
+    const i64 kb = kv_lim > 0 ? ((i64)(kv_lim - 1) * p.k_sL + D) * 2 : 0;
+    const i64 vb = kv_lim > 0 ? ((i64)(kv_lim - 1) * p.v_sL + D) * 2 : 0;
+    w.whole = (p.Lk + 64) * (i64)max(p.k_sL, p.v_sL) * 2 < ((i64)1 << 31);
+    w.kr = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, w.whole ? (int)kb : 0, kRsrcFlags);
+    w.vr = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, w.whole ? (int)vb : 0, kRsrcFlags);
+    w.ksl2 = (int)(p.k_sL * 2);
+    w.vsl2 = (int)(p.v_sL * 2);
+    return w;
+}
+
+template <int D, int NW, bool XM = false, bool WR = false>
 __device__ inline void bf16_issue_tile(const AttnLaunch& p, const __bf16* kbase, const __bf16* vbase, int j0,
-                                       int kv_lim, uint8_t* kl, uint8_t* vl, int* kidl, const XMask& xm) {
+                                       int kv_lim, uint8_t* kl, uint8_t* vl, int* kidl, const XMask& xm,
+                                       const WalkRsrc* wr = nullptr) {
     using C = Bf16Cfg<D, NW>;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     if (XM && xm.kid) {
@@ -643,6 +669,23 @@ __device__ inline void bf16_issue_tile(const AttnLaunch& p, const __bf16* kbase,
         const __amdgpu_buffer_rsrc_t ir = __builtin_amdgcn_make_buffer_rsrc((void*)(xm.kid + j0), 0, n * 4,
                                                                             kRsrcFlags);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ir, (lds_void*)kidl, 4, (unsigned)(lane * 4), 0, 0, 0);
+    }
+    if (WR && wr->whole) {
+        const int ko = j0 * wr->ksl2, vo = j0 * wr->vsl2;
+#pragma unroll
+        for (int it = 0; it < C::RUNS_PER_WAVE; ++it) {
+            const int run = wave * C::RUNS_PER_WAVE + it;
+            if (C::RUNS % NW == 0 || run < C::RUNS) {
+                const int slot = run * 64 + lane;
+                const int r = slot / C::NCH, pc = slot % C::NCH;
+                const int kc = k_swz<D>(r, pc), vc = v_swz<D>(r, pc);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr->kr, (lds_void*)(kl + run * 1024), 16,
+                                                         (unsigned)(r * wr->ksl2 + kc * 16 + ko), 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr->vr, (lds_void*)(vl + run * 1024), 16,
+                                                         (unsigned)(r * wr->vsl2 + vc * 16 + vo), 0, 0, 0);
+            }
+        }
+        return;
     }
     const int nvalid = uni(min(max(kv_lim - j0, 0), C::TILE));
     // The range ends with the last valid row's D elements: reads of later
@@ -938,7 +981,8 @@ __device__ __attribute__((always_inline)) inline bool bf16_step(const AttnLaunch
                                                                const W& walk, const Ring<D, NW>& ring,
                                                                Cursor<64>& cur, Cursor<64>& ahead, bool& more,
                                                                int& n_after, const __bf16* kbase,
-                                                               const __bf16* vbase, int kv_lim, const XMask& xm) {
+                                                               const __bf16* vbase, int kv_lim, const XMask& xm,
+                                                               const WalkRsrc& wr) {
     using C = Bf16Cfg<D, NW>;
     constexpr int NB = C::NBUF;
     constexpr int LOADS = 2 * C::RUNS_PER_WAVE;
@@ -958,7 +1002,8 @@ __device__ __attribute__((always_inline)) inline bool bf16_step(const AttnLaunch
     if (more) more = ahead.next(walk);
     if (more) {
         constexpr int J = (I + NB - 1) % NB;
-        bf16_issue_tile<D, NW, XM>(p, kbase, vbase, ahead.j0, kv_lim, ring.k[J], ring.v[J], ring.kid[J], xm);
+        bf16_issue_tile<D, NW, XM, SPEC>(p, kbase, vbase, ahead.j0, kv_lim, ring.k[J], ring.v[J], ring.kid[J], xm,
+                                         &wr);
         ++n_after;
     }
     // Tiles listed as partial, classified again for the wave's own rows: a
@@ -998,30 +1043,35 @@ __device__ inline void bf16_walk(const AttnLaunch& p, Bf16State<D, NW>& st, cons
     const int kv_lim = (int)p.mask.kv_valid;
     XMask xm{1, 0u, nullptr, 0};
     if (XM) xm = make_xmask(p, b);
+    WalkRsrc wr;
+    wr.whole = false;
+    if (SPEC) wr = walk_rsrc<D>(p, kbase, vbase, kv_lim);
     // Copies run NB - 1 tiles ahead of the compute.
     Cursor<C::TILE> cur, ahead;
     bool have = cur.next(walk);
     ahead = cur;
     bool more = have;
     int n_after = 0;  // tiles issued beyond the current one
-    if (have) bf16_issue_tile<D, NW, XM>(p, kbase, vbase, ahead.j0, kv_lim, ring.k[0], ring.v[0], ring.kid[0], xm);
+    if (have)
+        bf16_issue_tile<D, NW, XM, SPEC>(p, kbase, vbase, ahead.j0, kv_lim, ring.k[0], ring.v[0], ring.kid[0], xm, &wr);
     if (NB == 3) {
         if (more) more = ahead.next(walk);
         if (more) {
-            bf16_issue_tile<D, NW, XM>(p, kbase, vbase, ahead.j0, kv_lim, ring.k[1], ring.v[1], ring.kid[1], xm);
+            bf16_issue_tile<D, NW, XM, SPEC>(p, kbase, vbase, ahead.j0, kv_lim, ring.k[1], ring.v[1], ring.kid[1], xm,
+                                             &wr);
             ++n_after;
         }
     }
     while (have) {
         have = bf16_step<D, NW, BODY, XM, 0, SPEC>(p, st, walk, ring, cur, ahead, more, n_after, kbase, vbase, kv_lim,
-                                             xm);
+                                             xm, wr);
         if (!have) break;
         have = bf16_step<D, NW, BODY, XM, 1, SPEC>(p, st, walk, ring, cur, ahead, more, n_after, kbase, vbase, kv_lim,
-                                             xm);
+                                             xm, wr);
         if (NB == 3) {
             if (!have) break;
             have = bf16_step<D, NW, BODY, XM, NB - 1, SPEC>(p, st, walk, ring, cur, ahead, more, n_after, kbase, vbase,
-                                                      kv_lim, xm);
+                                                      kv_lim, xm, wr);
         }
     }
 }

@@ -559,3 +559,32 @@ def test_deterministic_repeat():
     mask = {"causal": True, "window": 200}
     outs = [bw.bwa_attn_fwd(q, k, v, mask) for _ in range(2)]
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mode", ["online", "fixed", "gated"])
+@pytest.mark.parametrize("balanced", [False, True])
+def test_keys_past_kv_valid_never_reach_the_result(D, mode, balanced):
+    # Keys at and past kv_valid hold NaN and Inf: their rows fall outside the
+    # K/V copy ranges and read as zero, and the mask hides them, so the call
+    # equals attention over the truncated keys (the oracle's "padded keys
+    # masked equals truncated keys").
+    B, H, Lq, Lk, kv_valid = 1, 2, 300, 700, 530
+    scale = 1 / math.sqrt(D)
+    q = _rand((B, Lq, H, D), 90, torch.bfloat16)
+    k = _rand((B, Lk, H, D), 91, torch.bfloat16)
+    v = _rand((B, Lk, H, D), 92, torch.bfloat16)
+    k[:, kv_valid:] = float("nan")
+    v[:, kv_valid:] = float("inf")
+    kt, vt = k[:, :kv_valid].contiguous(), v[:, :kv_valid].contiguous()
+    mask = {"kv_valid": kv_valid}
+    kmax, mmax, m, gate = bw.bwa_fixed_m_bound(q, [k], scale, 106.5, kv_valid=[kv_valid])
+    assert gate.all().item()
+    args = {"online": dict(mode=bw.BWA_MODE_ONLINE),
+            "fixed": dict(mode=bw.BWA_MODE_FIXED_M, m=m),
+            "gated": dict(mode=bw.BWA_MODE_GATED, m=m, gate=gate)}[mode]
+    call = bw.bwa_attn_fwd_balanced if balanced else bw.bwa_attn_fwd
+    o, l = call(q, k, v, mask, scale=scale, **args)
+    assert torch.isfinite(o).all() and torch.isfinite(l).all()
+    o_ref, l_ref = oracle_attention(q, kt, vt, {}, scale)
+    assert_close(o, l, o_ref, l_ref, torch.bfloat16, f"kv_valid {mode}")
